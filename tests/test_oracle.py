@@ -1,0 +1,290 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a library routine, brute force, a closed
+form, a stated invariant of the method, or a fixture worked by hand under
+tests/golden/ (each fixture cites the passage it follows).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nosa_oracle as O
+import nosa_inputs as NI
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- rounding
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(200000).astype(np.float32) * 100
+    # exact ties: low 16 bits = 0x8000, both parities of the kept part
+    ties = (np.arange(1000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1e-38, 3e38])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(O.to_bf16(x), ref)
+
+
+# ------------------------------------------------------------------ pooling
+def test_pooling_order_fixture():
+    g = _golden("pooling_small.json")["order_case"]
+    K = np.array(g["tokens"], dtype=np.float32)[:, None]
+    got = O.subblock_key_means(K, bf16=False)
+    assert got.shape == (1, 1)
+    assert got[0, 0] == np.float32(g["mean_f32"])
+    # the logits follow the same fp32 order
+    assert O.subblock_logit_means(K[:, 0])[0] == np.float32(g["mean_f32"])
+
+
+def test_block_constant_keys_pool_to_the_key():
+    rng = np.random.default_rng(1)
+    for bf16 in (False, True):
+        # 8 significant bits: every partial sum k*key (k <= 16) is exact in fp32
+        keys = O.to_bf16(rng.standard_normal((7, 32)).astype(np.float32))
+        K = np.repeat(keys, 64, axis=0)
+        kbar = O.subblock_key_means(K, bf16)
+        np.testing.assert_array_equal(kbar, np.repeat(keys, 4, axis=0))
+
+
+def test_pooling_agrees_with_exact_sum_except_rounding_boundaries():
+    rng = np.random.default_rng(2)
+    K = O.to_bf16(rng.standard_normal((64 * 256, 128)).astype(np.float32))
+    got = O.subblock_key_means(K, bf16=True)
+    exact = K.astype(np.float64).reshape(-1, 16, 128).sum(axis=1) / 16.0
+    alt = torch.from_numpy(exact).to(torch.bfloat16).to(torch.float32).numpy()
+    diff = got != alt
+    assert diff.mean() < 2e-3, diff.mean()
+    # where they differ the two are adjacent bf16 values (one ulp apart)
+    ulp = np.abs(got[diff].view(np.int32).astype(np.int64) - alt[diff].view(np.int32).astype(np.int64))
+    assert np.all(ulp == (1 << 16))
+
+
+def test_eviction_block_score_is_max_of_subblock_means():
+    g = _golden("pooling_small.json")["eviction_case"]
+    lam = np.repeat(np.array(g["subblock_values"], np.float32), 16)
+    E = O.block_eviction_scores(O.subblock_logit_means(lam))
+    assert E.shape == (1,) and E[0] == np.float32(g["E"])
+    # block-constant logits give that constant
+    vals = np.float32([0.25, -3.5, 7.0])
+    E2 = O.block_eviction_scores(O.subblock_logit_means(np.repeat(vals, 64)))
+    np.testing.assert_array_equal(E2, vals)
+
+
+# ------------------------------------------------------------ query scores
+def test_max_pool_of_scores_fixture():
+    g = _golden("pooling_small.json")["maxpool_case"]
+    keys = np.array(g["subblock_keys"], np.float32)
+    K = np.repeat(keys, 16, axis=0)              # 64 tokens, constant per sub-block
+    kbar = O.subblock_key_means(K, bf16=False)
+    s = O.query_block_scores(np.array([g["q"]], np.float32), kbar, 1)
+    assert s[0] == g["block_score"]
+
+
+def test_query_scores_block_constant_closed_form():
+    rng = np.random.default_rng(3)
+    keys = rng.integers(-4, 5, size=(9, 16)).astype(np.float32)
+    K = np.repeat(keys, 64, axis=0)
+    kbar = O.subblock_key_means(K, bf16=False)
+    q = rng.integers(-3, 4, size=(4, 16)).astype(np.float32)
+    s = O.query_block_scores(q, kbar, 9)
+    # integer data: the closed form is exact in any order
+    expect = [float(sum(int(q[g, d]) * int(keys[b, d]) for g in range(4) for d in range(16)))
+              for b in range(9)]
+    assert list(s) == expect
+
+
+def test_every_query_head_of_the_group_counts():
+    # two orthogonal query heads; block 3 aligned with head 1, block 6 with head 0,
+    # block 8 anti-aligned with both: the query-aware top-2 must be {3, 6} and
+    # block 8 must rank last (reading U3: one selection from the whole group).
+    rng = np.random.default_rng(4)
+    D = 64
+    q = np.zeros((2, D), np.float32)
+    q[0, :32] = rng.standard_normal(32)
+    q[1, 32:] = rng.standard_normal(32)
+    keys = 0.05 * rng.standard_normal((10, D)).astype(np.float32)
+    keys[3] = 3 * q[1] / np.linalg.norm(q[1])
+    keys[6] = 3 * q[0] / np.linalg.norm(q[0])
+    keys[8] = -3 * (q[0] + q[1]) / np.linalg.norm(q[0] + q[1])
+    K = np.repeat(keys, 64, axis=0)
+    s = O.query_block_scores(q, O.subblock_key_means(K, False), 10)
+    assert sorted(O.top_blocks(s, 2)) == [3, 6]
+    assert O.top_blocks(s, 10)[-1] == 8
+
+
+def test_selection_invariant_to_positive_query_scale():
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((64 * 40, 32)).astype(np.float32)
+    kbar = O.subblock_key_means(K, False)
+    q = rng.standard_normal((4, 32)).astype(np.float32)
+    a = O.top_blocks(O.query_block_scores(q, kbar, 40), 8)
+    b = O.top_blocks(O.query_block_scores(q * np.float32(4.0), kbar, 40), 8)
+    assert a == b
+
+
+# --------------------------------------------------------------- selection
+def test_selection_fixture():
+    for case in _golden("selection_small.json")["cases"]:
+        n = len(case["s_q"])
+        gq, ge, S = O.select_blocks(case["s_q"], case["E"], n, case["kq"], case["ke"])
+        assert gq == case["gamma_q"] and ge == case["gamma_e"] and S == case["S"]
+
+
+def _brute_topk(scores, k):
+    n = len(scores)
+    k = min(k, n)
+    best = None
+    for comb in itertools.combinations(range(n), k):
+        tot = sum(scores[j] for j in comb)          # integers: exact sums
+        key = (-tot, comb)                           # then lexicographically smallest ids
+        if best is None or key < best:
+            best = key
+    return list(best[1])
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_top_blocks_matches_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 13))
+    scores = [int(v) for v in rng.integers(-3, 4, size=n)]    # many ties
+    k = int(rng.integers(0, n + 2))
+    assert sorted(O.top_blocks(scores, k)) == _brute_topk(scores, k)
+
+
+# --------------------------------------------------------------- attention
+def _sdpa(q, k, v):
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[None, :, None, :],
+        torch.from_numpy(k.astype(np.float64))[None, None].expand(1, q.shape[0], -1, -1),
+        torch.from_numpy(v.astype(np.float64))[None, None].expand(1, q.shape[0], -1, -1))
+    return out[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("pos", [64 * 5, 64 * 5 + 17, 64 * 9 - 1])
+def test_dense_equivalence_when_topk_covers_all_blocks(pos):
+    rng = np.random.default_rng(pos)
+    T = pos + 1
+    D = 32
+    K = rng.standard_normal((T, D)).astype(np.float32)
+    V = rng.standard_normal((T, D)).astype(np.float32)
+    q = rng.standard_normal((3, D)).astype(np.float32)
+    c = pos // 64
+    lam = rng.standard_normal(T).astype(np.float32)
+    kbar = O.subblock_key_means(K, False)
+    E = O.block_eviction_scores(O.subblock_logit_means(lam))
+    s = O.query_block_scores(q, kbar, c)
+    _, _, S = O.select_blocks(s, E, c, kq=c, ke=0)
+    assert S == list(range(c))
+    got = O.sparse_attention(q, K, V, S, pos)
+    np.testing.assert_allclose(got, _sdpa(q, K[:T], V[:T]), rtol=1e-12, atol=1e-12)
+
+
+def test_window_only_attention():
+    rng = np.random.default_rng(7)
+    pos = 64 * 6 + 20
+    K = rng.standard_normal((pos + 1, 16)).astype(np.float32)
+    V = rng.standard_normal((pos + 1, 16)).astype(np.float32)
+    q = rng.standard_normal((2, 16)).astype(np.float32)
+    got = O.sparse_attention(q, K, V, [], pos)
+    np.testing.assert_allclose(got, _sdpa(q, K[64 * 6:], V[64 * 6:]), rtol=1e-12, atol=1e-12)
+
+
+def test_zero_query_gives_mean_of_attended_values():
+    rng = np.random.default_rng(8)
+    pos = 64 * 7 + 3
+    K = rng.standard_normal((pos + 1, 8)).astype(np.float32)
+    V = rng.standard_normal((pos + 1, 8)).astype(np.float32)
+    S = [1, 4]
+    got = O.sparse_attention(np.zeros((1, 8), np.float32), K, V, S, pos)
+    rows = list(range(64, 128)) + list(range(256, 320)) + list(range(448, pos + 1))
+    np.testing.assert_allclose(got[0], V[rows].astype(np.float64).mean(axis=0), rtol=1e-12, atol=1e-13)
+
+
+def test_one_hot_values_give_softmax_weights():
+    rng = np.random.default_rng(9)
+    pos = 64 * 2 + 5          # attended: block 0 + window of 6 tokens = 70 tokens
+    D = 16
+    K = rng.standard_normal((pos + 1, D)).astype(np.float32)
+    idx = list(range(0, 64)) + list(range(128, pos + 1))
+    V = np.zeros((pos + 1, len(idx)), np.float32)
+    for j, t in enumerate(idx):
+        V[t, j] = 1.0
+    q = rng.standard_normal((1, D)).astype(np.float32)
+    got = O.sparse_attention(q, K, V, [0], pos)[0]
+    logits = torch.from_numpy(K[idx].astype(np.float64)) @ torch.from_numpy(q[0].astype(np.float64)) / math.sqrt(D)
+    np.testing.assert_allclose(got, torch.softmax(logits, 0).numpy(), rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------- eviction & locality
+@pytest.mark.parametrize("kq,ke,L", [(4, 4, 64 * 20 + 13), (2, 6, 64 * 12 + 50), (8, 8, 64 * 30 + 1), (6, 3, 64 * 17)])
+def test_eviction_rule_and_locality_bound(kq, ke, L):
+    w = NI.scaled(NI.WORKLOADS["tiny"], prompt_len=L, n_steps=320, kq=kq, ke=ke, head_dim=16)
+    K, V, lam = NI.unit_kv(w, 0, 0)
+    q = NI.queries(w)[:, 0]                        # [n, Hq=G, D]
+    tr = O.decode_unit(K, V, lam, q, w.positions(), kq, ke, bf16=False, attend=False)
+    k = kq + ke
+    dropped = set()
+    for t in range(len(tr.sel)):
+        ge = set(tr.gamma_e[t])
+        assert not (ge & dropped), f"eviction rule broken at step {t}"
+        if t > 0:
+            dropped |= set(tr.gamma_e[t - 1]) - ge
+            c = int(w.positions()[t]) // 64
+            if c >= ke:
+                assert tr.locality[t] >= ke / k - 1e-12
+    # the run must cross several block boundaries
+    assert int(w.positions()[-1]) // 64 - int(w.positions()[0]) // 64 >= 4
+
+
+def test_locality_counts_previous_window_as_held():
+    assert O.locality([1, 2, 3], 7, [2, 3, 7, 9]) == 0.75
+    assert O.locality([], 0, []) == 1.0
+
+
+# ---------------------------------------------------------------- the pool
+def test_pool_fixture():
+    g = _golden("pool_lru.json")
+    pool = O.BlockPool(g["n_slots"])
+    for st in g["steps"]:
+        misses, ins, phys = pool.step(st["t"], st["S"], st["insert"])
+        assert [list(m) for m in misses] == st["misses"], st
+        assert ins == st["insert_slot"] and phys == st["phys"], st
+
+
+def test_pool_replay_invariants():
+    w = NI.scaled(NI.WORKLOADS["tiny"], prompt_len=64 * 24 + 9, n_steps=400, kq=5, ke=6, head_dim=16)
+    K, V, lam = NI.unit_kv(w, 0, 0)
+    q = NI.queries(w)[:, 0]
+    P = 14
+    tr = O.decode_unit(K, V, lam, q, w.positions(), 5, 6, bf16=False, pool_slots=P, attend=False)
+    resident = {}
+    total_misses = 0
+    for t, S in enumerate(tr.sel):
+        before = set(resident)
+        c = int(w.positions()[t]) // 64
+        if t > 0 and c > int(w.positions()[t - 1]) // 64:
+            assert tr.insert_slot[t] >= 0 or (c - 1) in before
+            if tr.insert_slot[t] >= 0:
+                slot = tr.insert_slot[t]
+                resident = {b: s for b, s in resident.items() if s != slot}
+                resident[c - 1] = slot
+        misses = tr.misses[t]
+        assert [b for b, _ in misses] == sorted(set(S) - set(resident))
+        for b, s in misses:
+            resident = {bb: ss for bb, ss in resident.items() if ss != s}
+            resident[b] = s
+        total_misses += len(misses)
+        assert all(b in resident for b in S)
+        assert [resident[b] for b in S] == tr.phys[t]
+        assert len(set(resident.values())) == len(resident) <= P
+    assert total_misses > 0
