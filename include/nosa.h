@@ -1,0 +1,246 @@
+/*
+ * nosa.h -- C ABI of libnosa, the decode-time hot path of NOSA (Native and
+ * Offloadable Sparse Attention, arXiv 2510.13602) on AMD CDNA4 (gfx950).
+ *
+ * The path, per decode step and per (batch b, KV head h):
+ *   1. nosa_pool_keys          compressed keys and block eviction scores
+ *   2. nosa_select_blocks      query-aware top-kq U query-agnostic top-ke
+ *   3. nosa_fetch_blocks       HBM block pool: set difference, slot choice,
+ *                              host -> HBM gather of the missing blocks
+ *   4. nosa_sparse_decode_attn exact attention over the selected blocks plus
+ *                              the current (window) block
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tokens are grouped in blocks of NOSA_BLOCK = 64 and sub-blocks of
+ *   NOSA_SUB = 16 (the NOSA-1B release post, "工程实现亮点": block size and
+ *   top-K are both 64; the 16-token sub-block is this library's choice).
+ * - Element type: NOSA_BF16 (bfloat16) or NOSA_F32; head_dim 64 or 128;
+ *   n_q_heads a multiple of n_kv_heads with at most 16 query heads per KV
+ *   head.
+ * - KV block format (one block = 2*64*head_dim elements): the 64 keys
+ *   token-major [64][head_dim], then the 64 values transposed
+ *   [head_dim][64].  The cache of one layer is [B][Hkv][max_blocks][block];
+ *   the HBM pool is [B][Hkv][pool_slots][block].  Host and HBM use the same
+ *   format, so a block moves as one contiguous span (32 KiB at D=128 bf16).
+ * - Decode position p attends tokens [0, p]; its window is block c = p/64
+ *   (tokens 64c..p); the candidates for selection are blocks 0..c-1.
+ * - Every buffer is allocated and owned by the caller.  "device" means HBM
+ *   of the current device; "pinned host" means host memory the GPU can read
+ *   directly (hipHostMalloc).  The library allocates nothing, frees nothing
+ *   and never synchronises: each call enqueues its kernels on `stream`
+ *   (a hipStream_t; NULL = the default stream) and returns.
+ * - Errors: every argument is validated on the host before any launch; a
+ *   failed call launches nothing.  Return codes below; nosa_last_error()
+ *   gives the text of the last failure on the calling thread.  Values that
+ *   live in device memory (positions, selected ids, slots) cannot be checked
+ *   on the host: the kernels skip out-of-range entries instead of reading or
+ *   writing outside the buffers, as documented per call.
+ * - Reentrant: concurrent calls are safe when their streams, outputs and
+ *   workspaces are distinct.
+ */
+#ifndef NOSA_H
+#define NOSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NOSA_BLOCK 64
+#define NOSA_SUB 16
+
+enum nosa_dtype { NOSA_BF16 = 0, NOSA_F32 = 1 };
+
+enum nosa_status {
+  NOSA_OK = 0,
+  NOSA_ERR_ARG = -1,          /* null pointer, bad size or range */
+  NOSA_ERR_UNSUPPORTED = -2,  /* dtype, head_dim or group size not built */
+  NOSA_ERR_HIP = -3,          /* a HIP launch or runtime call failed */
+  NOSA_ERR_WORKSPACE = -4     /* workspace smaller than nosa_workspace_size() */
+};
+
+enum nosa_op { NOSA_OP_SELECT = 1, NOSA_OP_ATTN = 2 };
+
+typedef struct nosa_dims {
+  int32_t batch;       /* B */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv; G = Hq / Hkv query heads share one KV head */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int32_t max_blocks;  /* NB: capacity of the cache in 64-token blocks per (b, h) */
+  int32_t dtype;       /* enum nosa_dtype */
+} nosa_dims;
+
+/*
+ * nosa_pool_keys -- compressed keys and the block eviction score.
+ *
+ * Defined by the gist.science summary of NOSA ("1. Algorithme : NOSA",
+ * block implementation: mean pooling inside sub-blocks, then max pooling per
+ * block, for the selection scores) and the montaan summary ("Key Design
+ * Components" item 2).  For every (b, h) and every block j in
+ * [blk_begin, blk_end), sub-blocks s = 4j..4j+3:
+ *   k_comp[b][h][s][:] = (sum of the 16 keys of s, fp32, token order) / 16,
+ *                        rounded to nearest-even to the cache dtype;
+ *   e_sub[b][h][s]     = (sum of the 16 logits of s, fp32, token order) / 16;
+ *   e_blk[b][h][j]     = max(e_sub[b][h][4j .. 4j+3]).
+ * Results are bit-exact (fixed summation order).
+ *
+ *   kv            device  blocks in the library's block format; block j of
+ *                         (b, h) starts at element
+ *                         (b*Hkv + h) * kv_unit_stride + j * kv_block_stride
+ *                         (the cache [B][Hkv][NB][block]: strides NB*block and
+ *                         block; a window buffer [B][Hkv][block] holding one
+ *                         block: strides block and 0).  Only keys are read.
+ *   evict_logits  device  fp32 [B][Hkv][NB*64]  per-token eviction logits
+ *                         (pre-exponential, as ED-DMA selects on them)
+ *   blk_begin, blk_end    0 <= blk_begin <= blk_end <= NB (host ints)
+ *   k_comp        device  [B][Hkv][NB*4][D], cache dtype      (written)
+ *   e_sub         device  fp32 [B][Hkv][NB*4]                 (written)
+ *   e_blk         device  fp32 [B][Hkv][NB]                   (written)
+ * Only the entries of blocks in the range are written.
+ */
+int nosa_pool_keys(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride,
+                   int64_t kv_block_stride, const float* evict_logits, int32_t blk_begin,
+                   int32_t blk_end, void* k_comp, float* e_sub, float* e_blk, void* stream);
+
+/*
+ * nosa_select_blocks -- the blocks each query row attends (Eq. 7).
+ *
+ * Defined by the montaan summary ("How it works": one Top-k over the query
+ * scores and one over the eviction-head scores; "Key Design Components"
+ * item 4, Eq. 7: up to k blocks, query-aware budget kq first, the
+ * query-agnostic budget ke for the rest) and the gist.science summary (dual
+ * selection Gamma_q / Gamma_e; ED-DMA: select on pre-exponential scores).
+ * For query row r of batch b at position p = pos[b][r], with c = p / 64:
+ *   qsum      = sum of the G query heads of KV head h (fp32);
+ *   sigma_s   = qsum . k_comp[b][h][s]   for sub-blocks s < 4c (fp32);
+ *   score_j   = max(sigma_4j .. sigma_4j+3)              (no scale, no exp);
+ *   Gamma_q   = the min(kq, c) blocks j < c with the best (score desc, j asc);
+ *   Gamma_e   = the min(ke, c) blocks j < c with the best (e_blk desc, j asc);
+ *   sel[b][r][h][0 .. n-1] = Gamma_q U Gamma_e ascending, the rest -1;
+ *   n_sel[b][r][h] = n (<= kq + ke).
+ * The window block c is not part of sel: the attention always adds it.
+ *
+ *   q        device  [B][n_query][Hq][D], cache dtype
+ *   n_query  query rows per batch entry (1 for decode)
+ *   pos      device  int32 [B][n_query]; rows with pos < 0 or
+ *                    pos >= NB*64 get n_sel = 0
+ *   k_comp, e_blk    as written by nosa_pool_keys for blocks 0..c-1
+ *   kq, ke   >= 0 budgets (in blocks)
+ *   sel      device  int32 [B][n_query][Hkv][kq+ke]            (written)
+ *   n_sel    device  int32 [B][n_query][Hkv]                    (written)
+ *   ws       device  workspace of at least
+ *                    nosa_workspace_size(dims, NOSA_OP_SELECT, n_query, kq, ke)
+ *                    bytes, zero-filled once before its first use; every
+ *                    call leaves it ready for the next one.
+ */
+int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query,
+                       const int32_t* pos, const void* k_comp, const float* e_blk,
+                       int32_t kq, int32_t ke, int32_t* sel, int32_t* n_sel, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * nosa_fetch_blocks -- keep the selected blocks in a fixed HBM block pool.
+ *
+ * Defined by the montaan summary ("System Optimization (NOSI)" item 2: KV in
+ * block-sized units on GPU and CPU, only blocks unused in the current step
+ * are swapped out; item 3: the host-to-device transfer reads host memory
+ * directly through unified virtual addressing) and the gist.science summary
+ * ("2. Système : NOSI": set differences drive block swapping; the wmrh.cn
+ * post: only the window and the Top-K blocks stay on the GPU).
+ * Per (b, h), with S = sel[b][h][0 .. n_sel-1] (one query row):
+ *   1. if insert_block[b] = j >= 0 and j is not resident, j (the block the
+ *      window just completed, held at insert_src) takes a slot first, with
+ *      last_use = step - 1;
+ *   2. the misses M = S minus the resident blocks, ascending, each take the
+ *      lowest free slot, else the slot of the resident block not in S with
+ *      the smallest (last_use, block id);
+ *   3. last_use = step for every block of S; phys[i] = slot of S[i];
+ *   4. the missing blocks are copied host -> pool by a gather kernel that
+ *      reads the pinned host cache directly (zero-copy), and the inserted
+ *      block is copied insert_src -> pool.
+ * Table updates (1-3) run in one wavefront per (b, h); the copies (4) run as
+ * a second kernel on the same stream (normally a side stream).
+ *
+ *   host_kv        pinned host [B][Hkv][NB][block]            (read)
+ *   pool           device [B][Hkv][pool_slots][block]         (written)
+ *   pool_slots     P, with kq + ke < P <= 1024
+ *   block_table    device int32 [B][Hkv][NB]: slot or -1     (read/written)
+ *   slot_block     device int32 [B][Hkv][P]: block or -1     (read/written)
+ *   slot_last_use  device int32 [B][Hkv][P]                   (read/written)
+ *                  (a fresh pool: block_table and slot_block all -1)
+ *   step           the decode step t (host int)
+ *   sel, n_sel     device, as written by nosa_select_blocks with n_query = 1;
+ *                  k_cap = kq + ke <= 64 is the row length of sel; entries
+ *                  outside [0, NB) are skipped
+ *   insert_block   device int32 [B] or NULL (no insertion)
+ *   insert_src     device [B][Hkv][block] or NULL (required with insert_block)
+ *   phys           device int32 [B][Hkv][k_cap]: slot of each sel entry, -1
+ *                  for skipped or padding entries                  (written)
+ *   miss_list      device int32 [B][Hkv][k_cap + 1][2]: (block, slot) of each
+ *                  miss in ascending block order; entry k_cap holds the
+ *                  inserted block (or -1, -1)                      (written)
+ *   n_miss         device int32 [B][Hkv]                             (written)
+ */
+int nosa_fetch_blocks(const nosa_dims* dims, const void* host_kv, void* pool,
+                      int32_t pool_slots, int32_t* block_table, int32_t* slot_block,
+                      int32_t* slot_last_use, int32_t step, const int32_t* sel,
+                      const int32_t* n_sel, int32_t k_cap, const int32_t* insert_block,
+                      const void* insert_src, int32_t* phys, int32_t* miss_list,
+                      int32_t* n_miss, void* stream);
+
+/*
+ * nosa_sparse_decode_attn -- exact attention over the selected blocks.
+ *
+ * Defined by the wmrh.cn NOSA-1B post ("工程实现亮点": two-stage attention,
+ * the compressed KV picks the Top-K blocks, then exact attention on them;
+ * "NOSA-1B 是什么": the current window and the Top-K blocks are kept).
+ * For query head g of KV head h (g in 0..G-1, query head index h*G + g):
+ *   T = tokens of the blocks phys[b][h][0 .. n_sel-1] plus the window
+ *       tokens 64c .. p (p = pos[b], c = p / 64);
+ *   out[b][h*G+g] = sum_{i in T} softmax_i(scale * q . K_i) V_i,
+ * accumulated in fp32 (split over the blocks, merged with the usual
+ * max/sum rescaling), stored once in the cache dtype (nearest-even).
+ *
+ *   q          device [B][Hq][D], cache dtype
+ *   blocks     device base of the blocks phys refers to:
+ *              [B][Hkv][blocks_per_head][block] (the full cache with phys =
+ *              sel, or the HBM pool with phys from nosa_fetch_blocks)
+ *   phys, n_sel  device int32 [B][Hkv][k_cap], [B][Hkv]; entries outside
+ *              [0, blocks_per_head) are skipped
+ *   window_kv  device; the window block of (b, h) starts at element
+ *              (b*Hkv + h) * window_head_stride + c * window_block_stride
+ *              (cache: strides NB*block and block; a separate window buffer
+ *              [B][Hkv][block]: strides block and 0)
+ *   pos        device int32 [B]; entries outside [0, NB*64) give zeros
+ *   scale      softmax scale (1/sqrt(D) for standard attention)
+ *   out        device [B][Hq][D], cache dtype                    (written)
+ *   ws         device workspace of at least
+ *              nosa_workspace_size(dims, NOSA_OP_ATTN, 1, k_cap, 0) bytes,
+ *              zero-filled once before its first use; every call leaves it
+ *              ready for the next one.
+ */
+int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* blocks,
+                            int32_t blocks_per_head, const int32_t* phys,
+                            const int32_t* n_sel, int32_t k_cap, const void* window_kv,
+                            int64_t window_head_stride, int64_t window_block_stride,
+                            const int32_t* pos, float scale, void* out, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by op (NOSA_OP_SELECT or NOSA_OP_ATTN); 0 on bad input. */
+size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, int32_t kq,
+                           int32_t ke);
+
+/* Static text of a status code. */
+const char* nosa_status_str(int32_t status);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* nosa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NOSA_H */

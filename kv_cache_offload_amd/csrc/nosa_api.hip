@@ -1,0 +1,241 @@
+// C ABI of libnosa: argument validation, launch geometry, status codes.
+//
+// Nothing here allocates, frees or synchronises.  Every argument that lives
+// on the host is checked before the first launch of a call; the kernels guard
+// the values that live in device memory.
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/nosa.h"
+#include "nosa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fn, const char* what) {
+  char buf[512];
+  snprintf(buf, sizeof buf, "%s: %s", fn, what);
+  g_last_error = buf;
+  return code;
+}
+
+int check_launch(const char* fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    char buf[512];
+    snprintf(buf, sizeof buf, "launch failed: %s", hipGetErrorString(e));
+    return fail(NOSA_ERR_HIP, fn, buf);
+  }
+  g_last_error.clear();
+  return NOSA_OK;
+}
+
+// Shape checks common to every call.
+int check_dims(const nosa_dims* d, const char* fn) {
+  if (!d) return fail(NOSA_ERR_ARG, fn, "dims is NULL");
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->max_blocks < 1)
+    return fail(NOSA_ERR_ARG, fn, "batch, head counts and max_blocks must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(NOSA_ERR_ARG, fn, "n_q_heads must be a multiple of n_kv_heads");
+  if (d->n_q_heads / d->n_kv_heads > 16)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "more than 16 query heads per KV head");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "head_dim must be 64 or 128");
+  if (d->dtype != NOSA_BF16 && d->dtype != NOSA_F32)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "dtype must be NOSA_BF16 or NOSA_F32");
+  if ((int64_t)d->max_blocks * NOSA_BLOCK > INT32_MAX)
+    return fail(NOSA_ERR_ARG, fn, "max_blocks * 64 overflows int32 positions");
+  return NOSA_OK;
+}
+
+constexpr int kMaxSelectBlocks = 4096;  // LDS of the selection stage: 10 bytes per block
+constexpr int kMaxPoolSlots = 1024;
+constexpr int kMaxFetchK = 64;          // one wavefront holds the selected set
+
+}  // namespace
+
+extern "C" {
+
+int nosa_pool_keys(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride,
+                   int64_t kv_block_stride, const float* evict_logits, int32_t blk_begin,
+                   int32_t blk_end, void* k_comp, float* e_sub, float* e_blk, void* stream) {
+  static const char* fn = "nosa_pool_keys";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (!kv || !evict_logits || !k_comp || !e_sub || !e_blk)
+    return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (blk_begin < 0 || blk_end < blk_begin || blk_end > dims->max_blocks)
+    return fail(NOSA_ERR_ARG, fn, "need 0 <= blk_begin <= blk_end <= max_blocks");
+  if (kv_unit_stride < 0 || kv_block_stride < 0)
+    return fail(NOSA_ERR_ARG, fn, "kv strides must be >= 0");
+  nosa::LaunchPool a{};
+  a.bf16 = dims->dtype == NOSA_BF16;
+  a.head_dim = dims->head_dim;
+  a.n_units = (int64_t)dims->batch * dims->n_kv_heads;
+  a.nb = dims->max_blocks;
+  a.blk_begin = blk_begin;
+  a.n_blk = blk_end - blk_begin;
+  a.kv = kv;
+  a.kv_unit_stride = kv_unit_stride;
+  a.kv_block_stride = kv_block_stride;
+  a.logits = evict_logits;
+  a.k_comp = k_comp;
+  a.e_sub = e_sub;
+  a.e_blk = e_blk;
+  a.stream = (hipStream_t)stream;
+  nosa::launch_pool_keys(a);
+  return check_launch(fn);
+}
+
+int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query, const int32_t* pos,
+                       const void* k_comp, const float* e_blk, int32_t kq, int32_t ke,
+                       int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "nosa_select_blocks";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (n_query < 1) return fail(NOSA_ERR_ARG, fn, "n_query must be >= 1");
+  if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
+  if ((int64_t)kq + ke > dims->max_blocks) return fail(NOSA_ERR_ARG, fn, "kq + ke > max_blocks");
+  if (!q || !pos || !k_comp || !e_blk || !n_sel || !ws || (kq + ke > 0 && !sel))
+    return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (dims->max_blocks > kMaxSelectBlocks)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "max_blocks above 4096 (256K tokens)");
+  if ((int64_t)dims->batch * n_query * dims->n_kv_heads > 65535)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_query * n_kv_heads above 65535");
+  const size_t need = nosa_workspace_size(dims, NOSA_OP_SELECT, n_query, kq, ke);
+  if (ws_bytes < need) return fail(NOSA_ERR_WORKSPACE, fn, "workspace too small");
+  nosa::LaunchSelect a{};
+  a.bf16 = dims->dtype == NOSA_BF16;
+  a.head_dim = dims->head_dim;
+  a.batch = dims->batch;
+  a.n_query = n_query;
+  a.n_q_heads = dims->n_q_heads;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.nb = dims->max_blocks;
+  a.kq = kq;
+  a.ke = ke;
+  a.q = q;
+  a.pos = pos;
+  a.k_comp = k_comp;
+  a.e_blk = e_blk;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.ws = ws;
+  a.stream = (hipStream_t)stream;
+  nosa::launch_select(a);
+  return check_launch(fn);
+}
+
+int nosa_fetch_blocks(const nosa_dims* dims, const void* host_kv, void* pool, int32_t pool_slots,
+                      int32_t* block_table, int32_t* slot_block, int32_t* slot_last_use,
+                      int32_t step, const int32_t* sel, const int32_t* n_sel, int32_t k_cap,
+                      const int32_t* insert_block, const void* insert_src, int32_t* phys,
+                      int32_t* miss_list, int32_t* n_miss, void* stream) {
+  static const char* fn = "nosa_fetch_blocks";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (k_cap < 0 || k_cap > kMaxFetchK)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "k_cap must be in [0, 64]");
+  if (pool_slots <= k_cap) return fail(NOSA_ERR_ARG, fn, "pool_slots must exceed k_cap = kq + ke");
+  if (pool_slots > kMaxPoolSlots) return fail(NOSA_ERR_UNSUPPORTED, fn, "pool_slots above 1024");
+  if (!host_kv || !pool || !block_table || !slot_block || !slot_last_use || !n_sel || !miss_list ||
+      !n_miss || (k_cap > 0 && (!sel || !phys)))
+    return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (insert_block && !insert_src) return fail(NOSA_ERR_ARG, fn, "insert_block needs insert_src");
+  if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_kv_heads above 65535");
+  nosa::LaunchFetch a{};
+  a.bf16 = dims->dtype == NOSA_BF16;
+  a.head_dim = dims->head_dim;
+  a.batch = dims->batch;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.nb = dims->max_blocks;
+  a.pool_slots = pool_slots;
+  a.k_cap = k_cap;
+  a.step = step;
+  a.host_kv = host_kv;
+  a.pool = pool;
+  a.block_table = block_table;
+  a.slot_block = slot_block;
+  a.slot_last_use = slot_last_use;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.insert_block = insert_block;
+  a.insert_src = insert_src;
+  a.phys = phys;
+  a.miss_list = miss_list;
+  a.n_miss = n_miss;
+  a.stream = (hipStream_t)stream;
+  nosa::launch_fetch(a);
+  return check_launch(fn);
+}
+
+int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* blocks,
+                            int32_t blocks_per_head, const int32_t* phys, const int32_t* n_sel,
+                            int32_t k_cap, const void* window_kv, int64_t window_head_stride,
+                            int64_t window_block_stride, const int32_t* pos, float scale, void* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "nosa_sparse_decode_attn";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (k_cap < 0 || k_cap > 4096) return fail(NOSA_ERR_ARG, fn, "k_cap must be in [0, 4096]");
+  if (blocks_per_head < 1 && k_cap > 0) return fail(NOSA_ERR_ARG, fn, "blocks_per_head must be >= 1");
+  if (!q || !window_kv || !pos || !out || !n_sel || !ws || (k_cap > 0 && (!blocks || !phys)))
+    return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (window_head_stride < 0 || window_block_stride < 0)
+    return fail(NOSA_ERR_ARG, fn, "window strides must be >= 0");
+  if (!(scale == scale)) return fail(NOSA_ERR_ARG, fn, "scale is NaN");
+  if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_kv_heads above 65535");
+  const size_t need = nosa_workspace_size(dims, NOSA_OP_ATTN, 1, k_cap, 0);
+  if (ws_bytes < need) return fail(NOSA_ERR_WORKSPACE, fn, "workspace too small");
+  nosa::LaunchAttn a{};
+  a.bf16 = dims->dtype == NOSA_BF16;
+  a.head_dim = dims->head_dim;
+  a.batch = dims->batch;
+  a.n_q_heads = dims->n_q_heads;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.nb = dims->max_blocks;
+  a.q = q;
+  a.blocks = blocks;
+  a.blocks_per_head = blocks_per_head;
+  a.phys = phys;
+  a.n_sel = n_sel;
+  a.k_cap = k_cap;
+  a.window_kv = window_kv;
+  a.window_head_stride = window_head_stride;
+  a.window_block_stride = window_block_stride;
+  a.pos = pos;
+  a.scale = scale;
+  a.out = out;
+  a.ws = ws;
+  a.stream = (hipStream_t)stream;
+  nosa::launch_attn(a);
+  return check_launch(fn);
+}
+
+size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, int32_t kq,
+                           int32_t ke) {
+  if (check_dims(dims, "nosa_workspace_size") != NOSA_OK) return 0;
+  if (n_query < 1 || kq < 0 || ke < 0) return 0;
+  if (op == NOSA_OP_SELECT)
+    return nosa::select_ws_bytes(dims->batch, n_query, dims->n_kv_heads, dims->max_blocks);
+  if (op == NOSA_OP_ATTN)
+    return nosa::attn_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                               kq + ke);
+  return 0;
+}
+
+const char* nosa_status_str(int32_t status) {
+  switch (status) {
+    case NOSA_OK: return "ok";
+    case NOSA_ERR_ARG: return "invalid argument";
+    case NOSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NOSA_ERR_HIP: return "HIP runtime error";
+    case NOSA_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* nosa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal helpers shared by the libnosa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nosa {
+
+constexpr int kBlock = 64;   // tokens per KV block
+constexpr int kSub = 16;     // tokens per sub-block of the compressed keys
+constexpr int kSubsPerBlock = kBlock / kSub;
+constexpr int kWave = 64;
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Element types of the cache.  Storage is raw bits; arithmetic is fp32.
+struct Bf16 {
+  using storage = uint16_t;
+  static constexpr int kBytes = 2;
+  static constexpr int kPer16B = 8;  // elements in one 16-byte load
+};
+struct F32 {
+  using storage = float;
+  static constexpr int kBytes = 4;
+  static constexpr int kPer16B = 4;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest, ties to even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Unpack one 16-byte chunk into fp32 values.
+__device__ __forceinline__ void unpack16(const uint4& v, float (&out)[8], Bf16) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const uint4& v, float (&out)[4], F32) {
+  out[0] = __uint_as_float(v.x);
+  out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z);
+  out[3] = __uint_as_float(v.w);
+}
+
+// Pack fp32 values into one 16-byte chunk of the cache type (bf16: nearest-even).
+__device__ __forceinline__ uint4 pack16(const float (&in)[8], Bf16) {
+  uint4 r;
+  r.x = f32_to_bf16_bits(in[0]) | (f32_to_bf16_bits(in[1]) << 16);
+  r.y = f32_to_bf16_bits(in[2]) | (f32_to_bf16_bits(in[3]) << 16);
+  r.z = f32_to_bf16_bits(in[4]) | (f32_to_bf16_bits(in[5]) << 16);
+  r.w = f32_to_bf16_bits(in[6]) | (f32_to_bf16_bits(in[7]) << 16);
+  return r;
+}
+__device__ __forceinline__ uint4 pack16(const float (&in)[4], F32) {
+  return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
+                    __float_as_uint(in[3]));
+}
+
+// Order-preserving map of a finite float onto uint32 (larger float -> larger
+// key); -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t orderable(float f) {
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace nosa

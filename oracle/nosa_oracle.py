@@ -236,6 +236,8 @@ class BlockPool:
 
         `insert` is a block that the window just completed (held in HBM); it is
         placed first, with last_use = t - 1, and is not a host fetch.
+        insert_slot is the slot it holds at the end of the step (-1 if there
+        was no insertion or a miss of the same step evicted it again).
         """
         needed = set(S)
         insert_slot = -1
@@ -248,6 +250,8 @@ class BlockPool:
             s = self._take_slot(needed)
             self.slot_block[s] = b
             misses.append((b, s))
+        if insert_slot >= 0 and self.slot_block[insert_slot] != insert:
+            insert_slot = -1                   # placed, then evicted again this step
         phys = []
         for b in sorted(needed):
             s = self.slot_of(b)

@@ -1,0 +1,145 @@
+"""The C ABI without a GPU: the library loads, exports what nosa.h declares,
+and rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_offload_amd import binding as nb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nb.LIB_PATH):
+        from kv_cache_offload_amd import build
+        build.build()
+    return nb.load()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "nosa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(nosa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for fn in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn"):
+        assert fn in names
+    assert sorted(nb.EXPORTS) == names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.nosa_status_str(0) == b"ok"
+    assert lib.nosa_status_str(-4) == b"workspace too small"
+    assert lib.nosa_status_str(12345) == b"unknown status"
+
+
+def _d(**kw):
+    base = dict(batch=2, n_q_heads=16, n_kv_heads=2, head_dim=128, max_blocks=64, dtype="bf16")
+    base.update(kw)
+    return nb.dims(**base)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def test_workspace_sizes(lib):
+    d = _d()
+    s = nb.workspace_size(d, nb.OP_SELECT, 1, 16, 48)
+    a = nb.workspace_size(d, nb.OP_ATTN, 1, 16, 48)
+    assert s >= 2 * 2 * 64 * 4 * 4 and a > 0
+    assert nb.workspace_size(d, 99, 1, 16, 48) == 0
+    assert nb.workspace_size(_d(head_dim=96), nb.OP_ATTN, 1, 16, 48) == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(head_dim=96), nb.ERR_UNSUPPORTED),
+    (dict(dtype=7), nb.ERR_UNSUPPORTED),
+    (dict(n_q_heads=15), nb.ERR_ARG),
+    (dict(n_q_heads=64, n_kv_heads=2), nb.ERR_UNSUPPORTED),
+    (dict(batch=0), nb.ERR_ARG),
+    (dict(max_blocks=0), nb.ERR_ARG),
+])
+def test_bad_dims_rejected(lib, bad, code):
+    d = _d(**bad)
+    with pytest.raises(nb.NosaError) as e:
+        nb.pool_keys(d, FAKE, 0, 0, FAKE, 0, 1, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == code
+
+
+def test_pool_keys_range_checked(lib):
+    for lo, hi in ((-1, 2), (3, 2), (0, 65)):
+        with pytest.raises(nb.NosaError) as e:
+            nb.pool_keys(_d(), FAKE, 0, 0, FAKE, lo, hi, FAKE, FAKE, FAKE, stream=0)
+        assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.pool_keys(_d(), None, 0, 0, FAKE, 0, 1, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_ARG and "NULL" in str(e.value)
+    with pytest.raises(nb.NosaError) as e:
+        nb.pool_keys(_d(), FAKE, -1, 0, FAKE, 0, 1, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_ARG
+
+
+def test_select_checks(lib):
+    d = _d()
+    need = nb.workspace_size(d, nb.OP_SELECT, 1, 4, 4)
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks(d, FAKE, 1, FAKE, FAKE, FAKE, 4, 4, FAKE, FAKE, FAKE, need - 1, stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks(d, FAKE, 1, FAKE, FAKE, FAKE, -1, 4, FAKE, FAKE, FAKE, need, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks(d, FAKE, 0, FAKE, FAKE, FAKE, 4, 4, FAKE, FAKE, FAKE, need, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks(_d(max_blocks=5000), FAKE, 1, FAKE, FAKE, FAKE, 4, 4, FAKE, FAKE, FAKE,
+                         1 << 40, stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+
+
+def test_fetch_checks(lib):
+    d = _d()
+    args = lambda P, k: (d, FAKE, FAKE, P, FAKE, FAKE, FAKE, 0, FAKE, FAKE, k, None, None, FAKE, FAKE, FAKE)
+    with pytest.raises(nb.NosaError) as e:
+        nb.fetch_blocks(*args(64, 64), stream=0)          # pool must exceed k
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.fetch_blocks(*args(80, 65), stream=0)          # one wavefront holds S
+    assert e.value.code == nb.ERR_UNSUPPORTED
+    with pytest.raises(nb.NosaError) as e:
+        nb.fetch_blocks(*args(2000, 8), stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+    a = list(args(80, 64))
+    a[11] = FAKE                                          # insert_block without insert_src
+    with pytest.raises(nb.NosaError) as e:
+        nb.fetch_blocks(*a, stream=0)
+    assert e.value.code == nb.ERR_ARG
+
+
+def test_attn_checks(lib):
+    d = _d()
+    need = nb.workspace_size(d, nb.OP_ATTN, 1, 64, 0)
+    base = [d, FAKE, FAKE, 64, FAKE, FAKE, 64, FAKE, 64 * 32768, 32768, FAKE, None, FAKE, FAKE]
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_decode_attn(*base, ws_bytes=need - 1, stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
+    bad = list(base)
+    bad[8] = -1
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_decode_attn(*bad, ws_bytes=need, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    bad = list(base)
+    bad[11] = float("nan")
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_decode_attn(*bad, ws_bytes=need, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    assert "scale" in lib.nosa_last_error().decode()

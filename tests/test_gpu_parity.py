@@ -1,0 +1,318 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: pooled keys and eviction scores bit-exact; selected block sets equal
+to the oracle's except where two scores at the kq-th place lie within 1e-5
+relative (then the GPU's choice must be a valid top-kq, and the oracle
+continues with it); pool tables, miss lists and slots exact; attention
+outputs within 2e-2 absolute (bf16) or 1e-4 (fp32).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import nosa_inputs as NI
+from kv_cache_offload_amd import binding as nb
+from kv_cache_offload_amd import runner as R
+from oracle import nosa_oracle as O
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nb.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _w(base, **kw):
+    return NI.scaled(NI.WORKLOADS[base], **kw)
+
+
+# ------------------------------------------------------------- pool keys
+@pytest.mark.parametrize("dtype,D,G", [("f32", 64, 2), ("bf16", 128, 8), ("bf16", 64, 4), ("f32", 128, 16)])
+def test_pool_keys_bit_exact(dtype, D, G):
+    _banner(f"pool_keys {dtype} D={D} G={G}")
+    w = _w("layer32k", batch=2, n_q_heads=2 * G, n_kv_heads=2, head_dim=D, prompt_len=64 * 37 + 5,
+           n_steps=1, dtype=dtype)
+    K, V, lam, q = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, q)
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, D, w.n_blocks, dtype, 4, 4)
+    layer.k_comp.fill_(float("nan"))
+    layer.e_sub.fill_(float("nan"))
+    layer.e_blk.fill_(float("nan"))
+    layer.pool_blocks(kv, logits, 0, 20)
+    layer.pool_blocks(kv, logits, 20, 37)
+    kc = layer.k_comp.float().cpu().numpy()
+    es = layer.e_sub.cpu().numpy()
+    eb = layer.e_blk.cpu().numpy()
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            kbar = O.subblock_key_means(K[b, h], bf16=(dtype == "bf16"))[: 37 * 4]
+            esub = O.subblock_logit_means(lam[b, h])[: 37 * 4]
+            E = O.block_eviction_scores(esub)
+            np.testing.assert_array_equal(kc[b, h, : 37 * 4].view(np.uint32), kbar.view(np.uint32))
+            np.testing.assert_array_equal(es[b, h, : 37 * 4].view(np.uint32), esub.view(np.uint32))
+            np.testing.assert_array_equal(eb[b, h, :37].view(np.uint32), E.view(np.uint32))
+            assert np.all(np.isnan(kc[b, h, 37 * 4:])) and np.all(np.isnan(eb[b, h, 37:]))
+
+
+def test_pool_keys_from_window_buffer():
+    _banner("pool_keys from a one-block window buffer")
+    w = _w("layer32k", batch=2, prompt_len=64 * 9, n_steps=1)
+    K, V, lam, q = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, q)
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, 4, 4)
+    ref = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, 4, 4)
+    ref.pool_blocks(kv, logits, 6, 7)
+    window = kv[:, :, 6].clone()
+    layer.pool_window(window, logits, 6)
+    assert torch.equal(layer.k_comp.view(torch.int16), ref.k_comp.view(torch.int16))
+    assert torch.equal(layer.e_blk, ref.e_blk)
+
+
+# --------------------------------------------------------------- selection
+SELECT_CASES = [
+    # name, workload overrides, kq, ke, positions
+    ("f32 D64 G2", dict(dtype="f32", head_dim=64, n_q_heads=2, n_kv_heads=1), 4, 4,
+     [5, 64 * 3 + 1, 64 * 37 + 17, 64 * 80 - 1]),
+    ("bf16 D128 G8", dict(), 16, 48, [0, 64 * 10 + 3, 64 * 70, 64 * 200 + 63]),
+    ("bf16 D64 G4 kq only", dict(head_dim=64, n_q_heads=8), 12, 0, [64 * 50 + 9, 64 * 129]),
+    ("bf16 D128 G16 ke only", dict(n_q_heads=32), 0, 20, [64 * 33 + 40]),
+    ("bf16 D128 wide k", dict(), 100, 150, [64 * 300 + 2]),
+]
+
+
+@pytest.mark.parametrize("name,over,kq,ke,positions", SELECT_CASES, ids=[c[0] for c in SELECT_CASES])
+def test_select_matches_oracle(name, over, kq, ke, positions):
+    _banner(f"select {name}")
+    T = max(positions) + 1
+    w = _w("layer32k", batch=3, prompt_len=T, n_steps=1, kq=kq, ke=ke, prefill=True, **over)
+    K, V, lam, _ = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, kq, ke)
+    layer.pool_blocks(kv, logits, 0, T // 64)
+    rng = np.random.default_rng(11)
+    ties = 0
+    for p in positions:
+        qn = rng.standard_normal((w.batch, w.n_q_heads, w.head_dim)).astype(np.float32)
+        if w.dtype == "bf16":
+            qn = NI.round_to_bf16(qn)
+        qd = torch.from_numpy(qn).cuda().to(R.torch_dtype(w.dtype))
+        pos = torch.full((w.batch,), p, dtype=torch.int32, device="cuda")
+        layer.select(qd, pos)
+        sel = layer.sel.cpu().numpy()
+        n = layer.n_sel.cpu().numpy()
+        c = p // 64
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                kbar = O.subblock_key_means(K[b, h], bf16=(w.dtype == "bf16"))
+                E = O.block_eviction_scores(O.subblock_logit_means(lam[b, h]))
+                s_q = O.query_block_scores(qn[b, h * w.group:(h + 1) * w.group], kbar, c)
+                _, _, S = O.select_blocks(s_q, E, c, kq, ke)
+                got = list(sel[b, h, : n[b, h]])
+                assert np.all(sel[b, h, n[b, h]:] == -1)
+                if got != S:
+                    assert H.selection_ok(got, s_q, E, c, kq, ke), (p, b, h, got, S)
+                    ties += 1
+    assert ties <= 2
+
+
+def test_select_invalid_positions_give_empty_sets():
+    _banner("select with out-of-range positions")
+    w = _w("layer32k", batch=2, prompt_len=64 * 8, n_steps=1, prefill=True)
+    K, V, lam, _ = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, 2, 2)
+    layer.pool_blocks(kv, logits, 0, 8)
+    q = torch.randn(w.batch, w.n_q_heads, w.head_dim, device="cuda").to(torch.bfloat16)
+    pos = torch.tensor([-5, 64 * 8 + 10], dtype=torch.int32, device="cuda")
+    layer.select(q, pos)
+    assert torch.all(layer.n_sel == 0) and torch.all(layer.sel == -1)
+    # the workspace is left ready: a valid call right after works
+    pos = torch.tensor([64 * 7 + 3, 64 * 7 + 3], dtype=torch.int32, device="cuda")
+    layer.select(q, pos)
+    assert torch.all((layer.n_sel >= 2) & (layer.n_sel <= 4))   # union of two 2-sets
+
+
+# --------------------------------------------------------------- attention
+ATTN_CASES = [
+    ("f32 D64 G2", dict(dtype="f32", head_dim=64, n_q_heads=2, n_kv_heads=1), 8),
+    ("bf16 D128 G8", dict(), 64),
+    ("bf16 D64 G4", dict(head_dim=64, n_q_heads=8), 12),
+    ("bf16 D128 G16", dict(n_q_heads=32), 20),
+    ("f32 D128 G1", dict(dtype="f32", n_q_heads=2), 9),
+]
+
+
+@pytest.mark.parametrize("name,over,k", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_with_oracle_selection(name, over, k):
+    _banner(f"attention {name}")
+    T = 64 * 90 + 1
+    w = _w("layer32k", batch=2, prompt_len=T, n_steps=1, prefill=True, **over)
+    K, V, lam, _ = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, k, 0)
+    rng = np.random.default_rng(5)
+    G = w.group
+    for p in (64 * 89 + 0, 64 * 89 + 33, 64 * 90, 64 * 88 + 63, 40):
+        c = p // 64
+        qn = rng.standard_normal((w.batch, w.n_q_heads, w.head_dim)).astype(np.float32)
+        if w.dtype == "bf16":
+            qn = NI.round_to_bf16(qn)
+        sel = np.full((w.batch, w.n_kv_heads, k), -1, np.int32)
+        nsel = np.zeros((w.batch, w.n_kv_heads), np.int32)
+        chosen = {}
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                m = int(rng.integers(0, min(k, c) + 1)) if (b + h) % 3 else min(k, c)
+                S = sorted(rng.choice(c, size=m, replace=False).tolist()) if m else []
+                sel[b, h, :m] = S
+                nsel[b, h] = m
+                chosen[b, h] = S
+        layer.sel.copy_(torch.from_numpy(sel))
+        layer.n_sel.copy_(torch.from_numpy(nsel))
+        qd = torch.from_numpy(qn).cuda().to(R.torch_dtype(w.dtype))
+        pos = torch.full((w.batch,), p, dtype=torch.int32, device="cuda")
+        layer.attend_resident(qd, kv, pos)
+        out = layer.out.float().cpu().numpy()
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                ref = O.round_output(O.sparse_attention(qn[b, h * G:(h + 1) * G], K[b, h], V[b, h],
+                                                        chosen[b, h], p), w.dtype == "bf16")
+                err = np.max(np.abs(out[b, h * G:(h + 1) * G] - ref))
+                assert err <= H.ATOL[w.dtype], (name, p, b, h, err)
+
+
+def test_attention_dense_equivalence():
+    _banner("attention: all blocks selected equals dense causal attention")
+    w = _w("layer32k", batch=1, n_q_heads=8, n_kv_heads=1, prompt_len=64 * 20 + 7, n_steps=1, prefill=True)
+    K, V, lam, _ = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    p = 64 * 20 + 6
+    layer = R.DecodeLayer(1, 8, 1, 128, w.n_blocks, "bf16", 20, 0)
+    layer.pool_blocks(kv, logits, 0, 20)
+    qn = NI.round_to_bf16(np.random.default_rng(2).standard_normal((1, 8, 128)).astype(np.float32))
+    qd = torch.from_numpy(qn).cuda().to(torch.bfloat16)
+    pos = torch.tensor([p], dtype=torch.int32, device="cuda")
+    layer.step_resident(qd, kv, pos)
+    assert layer.n_sel.item() == 20
+    out = layer.out.float().cpu()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qn[0]).double()[:, None, :],
+        torch.from_numpy(K[0, 0, : p + 1]).double()[None].expand(8, -1, -1),
+        torch.from_numpy(V[0, 0, : p + 1]).double()[None].expand(8, -1, -1))[:, 0, :]
+    assert float((out[0] - ref.float()).abs().max()) <= 2e-2
+
+
+def test_attention_split_counts_and_repeats_agree():
+    _banner("attention determinism across repeats")
+    w = _w("layer32k", batch=4, prompt_len=64 * 100 + 20, n_steps=3)
+    K, V, lam, q = NI.layer_inputs(w)
+    s1, n1, o1, _ = H.run_resident(w, K, V, lam, q)
+    s2, n2, o2, _ = H.run_resident(w, K, V, lam, q)
+    for a, b in zip(s1, s2):
+        assert np.array_equal(a, b)
+    for a, b in zip(o1, o2):
+        assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------- end-to-end decode
+def test_tiny_fp32_decode_matches_oracle():
+    _banner("tiny fp32 workload: 16 decode steps")
+    w = NI.WORKLOADS["tiny"]
+    K, V, lam, q = NI.layer_inputs(w)
+    sels, nsels, outs, _ = H.run_resident(w, K, V, lam, q)
+    st = H.compare_unit(w, K, V, lam, q, 0, 0, H.unit_selections(sels, nsels, 0, 0), gpu_out=outs)
+    assert st["max_err"] <= 1e-4
+
+
+def test_layer32k_decode_matches_oracle():
+    _banner("layer32k workload: B=8, 16/2 heads, D=128, 32K context, 64 steps")
+    w = NI.WORKLOADS["layer32k"]
+    K, V, lam, q = NI.layer_inputs(w)
+    sels, nsels, outs, _ = H.run_resident(w, K, V, lam, q)
+    ties = 0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            st = H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(sels, nsels, b, h), gpu_out=outs)
+            ties += st["ties"]
+    print(f"[layer32k] accepted ties: {ties}", flush=True)
+
+
+# ------------------------------------------------------------ offload path
+def _pool_consistent(layer, host, b, h):
+    bt = layer.block_table[b, h].cpu().numpy()
+    sb = layer.slot_block[b, h].cpu().numpy()
+    for s, blk in enumerate(sb):
+        if blk >= 0:
+            assert bt[blk] == s
+            assert torch.equal(layer.pool[b, h, s].cpu().view(torch.int16), host[b, h, blk].view(torch.int16)), (b, h, s, blk)
+    for blk, s in enumerate(bt):
+        if s >= 0:
+            assert sb[s] == blk
+
+
+@pytest.mark.parametrize("side", [True, False])
+def test_offload_small_pool_matches_oracle(side):
+    _banner(f"offload: B=3, L ragged, 100 steps, pool 14 slots, side stream={side}")
+    w = _w("offload", batch=3, prompt_len=64 * 40 + 30, n_steps=100, kq=4, ke=6, pool_slots=14)
+    K, V, lam, q = NI.layer_inputs(w)
+    rec, layer, host = H.run_offload(w, K, V, lam, q, side_stream=side)
+    total = 0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            st = H.check_offload_unit(w, K, V, lam, q, rec, b, h)
+            total += st["misses"]
+            _pool_consistent(layer, host, b, h)
+    assert total > w.batch * w.n_kv_heads * 10
+
+
+def test_offload_workload_sampled_units():
+    _banner("offload workload: B=64, 16K context, pool 80, 128 steps (sampled units)")
+    w = NI.WORKLOADS["offload"]
+    K, V, lam, q = NI.layer_inputs(w)
+    rec, layer, host = H.run_offload(w, K, V, lam, q, record_tables=False)
+    for b, h in ((0, 0), (17, 1), (40, 0), (63, 1)):
+        H.check_offload_unit(w, K, V, lam, q, rec, b, h)
+        _pool_consistent(layer, host, b, h)
+
+
+def test_prefill128k_chunk_selection():
+    _banner("prefill128k: pool 131072 tokens, select for 64 query rows")
+    w = NI.WORKLOADS["prefill128k"]
+    K, V, lam, q = NI.layer_inputs(w)                    # q: [64, 1, 16, 128]
+    kv, logits, qd, pos = H.device_inputs(w, K, V, lam, q)
+    layer = R.DecodeLayer(1, 16, 2, 128, w.n_blocks, "bf16", w.kq, w.ke)
+    layer.pool_blocks(kv, logits, 0, w.n_blocks)
+    n_q = w.n_steps
+    qrows = qd.permute(1, 0, 2, 3).contiguous()           # [B, n_query, Hq, D]
+    posr = pos.t().contiguous()                           # [B, n_query]
+    sel = torch.full((1, n_q, 2, w.kq + w.ke), -1, dtype=torch.int32, device="cuda")
+    n_sel = torch.zeros((1, n_q, 2), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, w.kq, w.ke), dtype=torch.uint8, device="cuda")
+    nb.select_blocks(layer.dims, qrows, n_q, posr, layer.k_comp, layer.e_blk, w.kq, w.ke, sel, n_sel, ws)
+    sel = sel.cpu().numpy()
+    n_sel = n_sel.cpu().numpy()
+    kc = layer.k_comp.float().cpu().numpy()
+    for h in range(2):
+        kbar = O.subblock_key_means(K[0, h], bf16=True)
+        assert np.array_equal(kc[0, h].view(np.uint32), kbar.view(np.uint32))
+        E = O.block_eviction_scores(O.subblock_logit_means(lam[0, h]))
+        for r in range(n_q):
+            p = int(w.positions()[r])
+            c = p // 64
+            s_q = O.query_block_scores(q[r, 0, h * 8:(h + 1) * 8], kbar, c)
+            _, _, S = O.select_blocks(s_q, E, c, w.kq, w.ke)
+            got = list(sel[0, r, h, : n_sel[0, r, h]])
+            assert got == S or H.selection_ok(got, s_q, E, c, w.kq, w.ke), (h, r)
