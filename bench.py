@@ -1,0 +1,343 @@
+"""Benchmark of the NOSA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-offload] [--no-cpu]
+
+Headline: the layer32k workload (one attention layer, batch 8, 16 query /
+2 KV heads, head_dim 128, bf16, 32K-token context, top-64 blocks of 64
+tokens: kq = 16 query-aware + ke = 48 query-agnostic, plus the window),
+synthetic seeded data.  A step is one decode token for the whole batch:
+nosa_select_blocks then nosa_sparse_decode_attn (no block completes during
+these 64 positions, so nosa_pool_keys has nothing to do; the offload leg
+exercises it).  Steps are captured in a HIP graph and replayed.
+
+Cold-cache protocol: the layer's cache plus compressed keys (264 MiB) would
+fit the 256 MB Infinity Cache, so four replicas at distinct addresses are
+rotated (step t uses replica t mod 4, 1 GiB in total).
+
+Prints ONE JSON line.  Extra objects: roofline of the dominant kernel
+(attention), per-kernel times, the offload leg (KV in pinned host memory,
+HBM pool of 80 blocks per KV head, the offload workload) and the oracle's
+CPU baseline on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+N_REPLICAS = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-offload", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch each step instead of graph replay")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(w, n_sel_rows, positions):
+    """Algorithmic HBM bytes of the steps whose per-unit n_S are given.
+
+    Per (b, KV head): q 2GD + compressed-key scan 4c*D*2 + block scores 4c +
+    selected K,V n_S*64*2D*2 + window (p-64c+1)*2D*2 + output 2GD (bytes,
+    bf16); the selected ids (4 bytes each) are counted with the attention.
+    """
+    G, D = w.group, w.head_dim
+    sel_b, attn_b = [], []
+    for n_s, p in zip(n_sel_rows, positions):
+        c = int(p) // 64
+        win = int(p) - 64 * c + 1
+        units = n_s.size
+        qb = G * D * 2
+        sel_b.append(units * (qb + 4 * c * D * 2 + 4 * c) + int(n_s.sum()) * 4)
+        attn_b.append(units * (qb + win * 2 * D * 2 + qb) + int(n_s.sum()) * (64 * 2 * D * 2 + 4))
+    return np.array(sel_b, np.float64), np.array(attn_b, np.float64)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import nosa_inputs as NI
+    from kv_cache_offload_amd import binding as nb
+    from kv_cache_offload_amd import runner as R
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    nb.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ inputs
+    w = NI.WORKLOADS["layer32k"]
+    t0 = time.perf_counter()
+    K, V, lam, q = NI.layer_inputs(w)
+    log(f"inputs {w.name}: {time.perf_counter() - t0:.1f}s")
+    kv0, logits, qd, pos = _device_inputs(w, K, V, lam, q, R)
+    kvs = [kv0] + [kv0.clone() for _ in range(N_REPLICAS - 1)]
+    layers = []
+    c0 = int(w.positions()[0]) // 64
+    for r in range(N_REPLICAS):
+        L = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
+        L.pool_blocks(kvs[r], logits, 0, c0)
+        layers.append(L)
+    n_pos = w.n_steps
+    positions = w.positions()
+    assert all(int(p) // 64 == c0 for p in positions), "no block completes in the headline workload"
+
+    def step(t, stream=None):
+        r = t % N_REPLICAS
+        i = t % n_pos
+        layers[r].step_resident(qd[i], kvs[r], pos[i], stream)
+
+    # untimed pass: warm-up and the per-step n_S for the byte count
+    n_sel_rows = []
+    for t in range(max(args.steps, args.warmup)):
+        step(t)
+        if t < args.steps:
+            n_sel_rows.append(layers[t % N_REPLICAS].n_sel.cpu().numpy().copy())
+    torch.cuda.synchronize()
+    pos_steps = [positions[t % n_pos] for t in range(args.steps)]
+    sel_bytes, attn_bytes = step_bytes(w, n_sel_rows, pos_steps)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for t in range(2):           # warm the capture stream
+                fn(t)
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for t in range(n):
+                    fn(t)
+        return g
+
+    def time_graph(g, reps=20):
+        """Median ms of one replay over `reps` replays (events on the replay stream)."""
+        times = []
+        with torch.cuda.stream(stream):
+            g.replay()
+            stream.synchronize()
+            for _ in range(reps):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                b.synchronize()
+                times.append(a.elapsed_time(b))
+        return float(np.median(times)), float(np.percentile(times, 10)), float(np.percentile(times, 90))
+
+    K_steps = args.steps
+    if args.eager:
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            for t in range(args.warmup):
+                step(t, stream)
+            a.record(stream)
+            for t in range(K_steps):
+                step(t, stream)
+            b.record(stream)
+        b.synchronize()
+        total_ms = a.elapsed_time(b)
+        p10 = p90 = total_ms
+    else:
+        g_step = capture(lambda t: step(t, stream), K_steps)
+        total_ms, p10, p90 = time_graph(g_step)
+    torch.cuda.synchronize()
+    ms_per_step = total_ms / K_steps
+
+    # per-kernel averages: graphs holding only one kernel, same arguments
+    def sel_only(t):
+        r = t % N_REPLICAS
+        layers[r].select(qd[t % n_pos], pos[t % n_pos], stream)
+
+    def attn_only(t):
+        r = t % N_REPLICAS
+        layers[r].attend_resident(qd[t % n_pos], kvs[r], pos[t % n_pos], stream)
+
+    g_sel = capture(sel_only, K_steps)
+    sel_ms = time_graph(g_sel)[0] / K_steps
+    g_attn = capture(attn_only, K_steps)
+    attn_ms = time_graph(g_attn)[0] / K_steps
+
+    tok_per_s = w.batch / (ms_per_step * 1e-3)
+    step_b = float((sel_bytes + attn_bytes).mean())
+    hbm_gbps = step_b / (ms_per_step * 1e-3) / 1e9
+    attn_gbps = float(attn_bytes.mean()) / (attn_ms * 1e-3) / 1e9
+    sel_gbps = float(sel_bytes.mean()) / (sel_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step * 1e3:.2f} us  select {sel_ms * 1e3:.2f} us  attention {attn_ms * 1e3:.2f} us")
+
+    result = {
+        "metric": "decode tokens/s at 32K ctx (bf16, top-64x64-tok blocks) + achieved HBM GB/s",
+        "value": round(tok_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step_p10_p90": [round(p10 / K_steps, 6), round(p90 / K_steps, 6)],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; keys N(0,1)+per-block N(0,0.5^2) offset, values N(0,1), AR(1) rho=0.9 queries)",
+        "config": {"workload": "layer32k", "batch": w.batch, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": w.prompt_len,
+                   "kq": w.kq, "ke": w.ke, "block": 64, "layers": 1,
+                   "cache_replicas": N_REPLICAS, "graph": not args.eager},
+        "hbm_gbps": round(hbm_gbps, 1),
+        "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "step_bytes": int(step_b),
+        "kernels": {"select_us": round(sel_ms * 1e3, 3), "select_gbps": round(sel_gbps, 1),
+                    "attn_us": round(attn_ms * 1e3, 3), "attn_gbps": round(attn_gbps, 1)},
+        "roofline": {"kernel": "nosa attn_kernel (split-K sparse decode attention)", "bound": "hbm",
+                     "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(attn_bytes.mean())},
+    }
+
+    if not args.no_offload:
+        result["offload"] = _offload_leg(torch, NI, R)
+    if not args.no_cpu:
+        result["cpu_baseline"] = _cpu_baseline(NI, w, K, V, lam, q)
+    print(json.dumps(result), flush=True)
+
+
+def _device_inputs(w, K, V, lam, q, R):
+    import torch
+    NB = w.n_blocks
+    kv = R.to_device_blocks(K, V, NB, w.dtype)
+    logits = R.pad_logits(torch.from_numpy(lam).cuda(), NB)
+    qd = torch.from_numpy(q).cuda().to(R.torch_dtype(w.dtype))
+    pos = torch.from_numpy(np.repeat(w.positions()[:, None], w.batch, axis=1).astype(np.int32)).cuda()
+    return kv, logits, qd, pos
+
+
+def _offload_leg(torch, NI, R):
+    """The offload workload: KV in pinned host memory, HBM pool of 80 blocks."""
+    w = NI.WORKLOADS["offload"]
+    t0 = time.perf_counter()
+    K, V, lam, q = NI.layer_inputs(w)
+    log(f"inputs {w.name}: {time.perf_counter() - t0:.1f}s")
+    kv_dev, logits, qd, pos = _device_inputs(w, K, V, lam, q, R)
+    del K, V
+    host = kv_dev.cpu().pin_memory()
+    positions = w.positions()
+    windows = {c: kv_dev[:, :, c].clone() for c in sorted({int(p) // 64 for p in positions})}
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq,
+                          w.ke, pool_slots=w.pool_slots)
+    c_prev = int(positions[0]) // 64
+    layer.pool_blocks(kv_dev, logits, 0, c_prev)
+    del kv_dev
+    torch.cuda.synchronize()
+    # host-link reference: one 1 GiB pinned -> HBM copy
+    ref_src = host.view(-1)[: (1 << 29)]
+    ref_dst = torch.empty_like(ref_src, device="cuda")
+    ref_dst.copy_(ref_src, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    ref_dst.copy_(ref_src, non_blocking=True)
+    b.record()
+    b.synchronize()
+    link_ref = ref_src.numel() * ref_src.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
+    del ref_dst
+
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    blk_bytes = 2 * 64 * w.head_dim * 2
+    step_ms, fetch_ms, misses = [], [], []
+    for t in range(w.n_steps):
+        c = int(positions[t]) // 64
+        ins_blk = ins_src = None
+        e0, e1, f0, f1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+        e0.record(main)
+        if c > c_prev:
+            layer.pool_window(windows[c_prev], logits, c_prev, main)
+            ins_blk = torch.full((w.batch,), c_prev, dtype=torch.int32, device="cuda")
+            ins_src = windows[c_prev]
+        layer.select(qd[t], pos[t], main)
+        side.wait_stream(main)
+        f0.record(side)
+        layer.fetch(host, t, ins_blk, ins_src, side)
+        f1.record(side)
+        main.wait_stream(side)
+        layer.attend_pool(qd[t], windows[c], pos[t], main)
+        e1.record(main)
+        e1.synchronize()
+        step_ms.append(e0.elapsed_time(e1))
+        fetch_ms.append(f0.elapsed_time(f1))
+        misses.append(int(layer.n_miss.sum().item()))
+        c_prev = c
+    warm = slice(1, None)                  # step 0 fills the cold pool
+    ms = float(np.mean(step_ms[warm]))
+    miss_bytes = np.array(misses, np.float64) * blk_bytes
+    link = float(miss_bytes[warm].sum() / (np.sum(fetch_ms[warm]) * 1e-3) / 1e9)
+    cold_link = float(miss_bytes[0] / (fetch_ms[0] * 1e-3) / 1e9)
+    units = w.batch * w.n_kv_heads
+    log(f"offload: step {ms:.3f} ms, misses/unit/step {np.mean(misses[1:]) / units:.2f}, "
+        f"link {link:.1f} GB/s (cold step {cold_link:.1f}), memcpy ref {link_ref:.1f} GB/s")
+    return {
+        "workload": "offload", "batch": w.batch, "context": w.prompt_len, "pool_slots": w.pool_slots,
+        "steps": w.n_steps, "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 4), "cold_step_ms": round(step_ms[0], 4),
+        "misses_per_unit_step": round(float(np.mean(misses[1:])) / units, 3),
+        "miss_fraction": round(float(np.mean(misses[1:])) / (units * (w.kq + w.ke)), 4),
+        "host_link_gbps": round(link, 2), "cold_step_host_link_gbps": round(cold_link, 2),
+        "memcpy_h2d_gbps": round(link_ref, 2),
+        "host_link_frac_of_memcpy": round(link / link_ref, 4),
+        "cold_frac_of_memcpy": round(cold_link / link_ref, 4),
+    }
+
+
+def _cpu_baseline(NI, w, K, V, lam, q):
+    """The oracle, as it stands, on a bounded sample of the headline workload."""
+    from oracle import nosa_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                      # pragma: no cover
+        threadpool_limits = None
+    batches = (0, 1)
+    G = w.group
+    limiter = threadpool_limits(limits=1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    for b in batches:
+        for h in range(w.n_kv_heads):
+            O.decode_unit(K[b, h], V[b, h], lam[b, h], q[:, b, h * G:(h + 1) * G], w.positions(),
+                          w.kq, w.ke, bf16=True)
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
+    tokens = len(batches) * w.n_steps
+    log(f"oracle: {tokens} tokens in {dt:.1f}s")
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer32k, batch entries {list(batches)} (both KV heads), all {w.n_steps} decode "
+                      f"steps incl. pooling the 32K prompt; numpy, BLAS limited to 1 thread",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -208,8 +208,8 @@ int nosa_fetch_blocks(const nosa_dims* dims, const void* host_kv, void* pool,
  *   blocks     device base of the blocks phys refers to:
  *              [B][Hkv][blocks_per_head][block] (the full cache with phys =
  *              sel, or the HBM pool with phys from nosa_fetch_blocks)
- *   phys, n_sel  device int32 [B][Hkv][k_cap], [B][Hkv]; entries outside
- *              [0, blocks_per_head) are skipped
+ *   phys, n_sel  device int32 [B][Hkv][k_cap], [B][Hkv] (k_cap <= 512);
+ *              entries outside [0, blocks_per_head) are skipped
  *   window_kv  device; the window block of (b, h) starts at element
  *              (b*Hkv + h) * window_head_stride + c * window_block_stride
  *              (cache: strides NB*block and block; a separate window buffer

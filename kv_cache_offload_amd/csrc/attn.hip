@@ -17,25 +17,25 @@
 // S tiles is permuted so that each lane's softmax weights are exactly the
 // P^T operand it needs for the V product, with no data exchange.
 //
-// Online softmax (running max / sum per head, exp2 with the scale folded in)
-// keeps the state in registers; the wavefronts of a workgroup merge through
-// LDS, workgroups through a fp32 workspace; the last workgroup of a (b, h)
-// (atomic ticket) merges the splits, normalises and stores the output.
+// Each wavefront keeps its block's max / sum per head (exp2 with the scale
+// folded in) and its unnormalised output in registers; the wavefronts of a
+// workgroup merge through LDS, workgroups through a fp32 workspace written
+// with coherent stores; the last workgroup of a (b, h) (atomic ticket)
+// merges the splits, normalises and stores the output.
 #include "nosa_common.h"
 #include "nosa_launch.h"
 
 namespace nosa {
 
-constexpr int kAttnWaves = 4;
-constexpr int kBlocksPerWave = 1;
-constexpr int kEntriesPerWG = kAttnWaves * kBlocksPerWave;
-
-static inline int attn_splits(int k_cap) { return (k_cap + 1 + kEntriesPerWG - 1) / kEntriesPerWG; }
+// One block per wavefront; 8 wavefronts per workgroup when the GQA group
+// fits 8 columns, 4 otherwise (the LDS merge buffer holds WAVES x G rows).
+static inline int attn_waves(int G) { return G <= 8 ? 8 : 4; }
+static inline int attn_splits(int k_cap, int G) { return (k_cap + 1 + attn_waves(G) - 1) / attn_waves(G); }
 
 size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap) {
   const size_t units = (size_t)batch * n_kv_heads;
   const size_t G = n_q_heads / n_kv_heads;
-  const size_t splits = attn_splits(k_cap);
+  const size_t splits = attn_splits(k_cap, (int)G);
   return align256(units * sizeof(int32_t)) + align256(units * splits * G * 2 * sizeof(float)) +
          align256(units * splits * G * head_dim * sizeof(float));
 }
@@ -182,7 +182,7 @@ __device__ __forceinline__ void block_pv(const Frags<T, D>& f, const float (&p)[
   }
 }
 
-template <class T, int D, int WAVES>
+template <class T, int D, int WAVES, int GMAX>
 __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ blocks,
     int blocks_per_head, const int32_t* __restrict__ phys, const int32_t* __restrict__ n_sel,
@@ -191,9 +191,11 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     int n_kv_heads, int nb, typename T::storage* __restrict__ out, int32_t* __restrict__ ticket,
     float* __restrict__ part_ml, float* __restrict__ part_o) {
   constexpr int ND = D / 16;
+  constexpr int NT = 64 * WAVES;
   const int G = n_q_heads / n_kv_heads;
   const int unit = blockIdx.y;  // b * Hkv + h
   const int b = unit / n_kv_heads;
+  const int h = unit % n_kv_heads;
   const int split = blockIdx.x;
   const int n_split = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -205,31 +207,30 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   const int c = valid_pos ? p / kBlock : 0;
   int ns = valid_pos ? n_sel[unit] : -1;
   ns = ns < 0 ? -1 : (ns > k_cap ? k_cap : ns);
-  const int n_ent = ns + 1;  // selected blocks, then the window (none if pos invalid)
+  const int n_ent = ns + 1;  // selected blocks, then the window (none if pos is invalid)
 
-  Frags<T, D> f;
-  load_q<T, D>(f, q + ((size_t)b * n_q_heads + (size_t)(unit % n_kv_heads) * G) * D, G, lane);
-
+  // ---- this wavefront's block: entry split*WAVES + wave
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int j = 0; j < kBlocksPerWave; ++j) {
-    const int e = split * kEntriesPerWG + wave + WAVES * j;
-    if (e >= n_ent) break;
-    const typename T::storage* blk;
-    int len;
-    if (e < ns) {
-      const int pb = phys[(size_t)unit * k_cap + e];
-      if (pb < 0 || pb >= blocks_per_head) continue;
+  const int e = split * WAVES + wave;
+  const typename T::storage* blk = nullptr;
+  int len = 0;
+  if (e < ns) {
+    const int pb = phys[(size_t)unit * k_cap + e];
+    if (pb >= 0 && pb < blocks_per_head) {
       blk = blocks + ((size_t)unit * blocks_per_head + pb) * blk_elems;
       len = kBlock;
-    } else {
-      blk = window_kv + (int64_t)unit * win_head_stride + (int64_t)c * win_block_stride;
-      len = p - c * kBlock + 1;
     }
+  } else if (e < n_ent) {
+    blk = window_kv + (int64_t)unit * win_head_stride + (int64_t)c * win_block_stride;
+    len = p - c * kBlock + 1;
+  }
+  if (blk != nullptr) {
+    Frags<T, D> f;
     load_block<T, D>(f, blk, lane);
+    load_q<T, D>(f, q + ((size_t)b * n_q_heads + (size_t)h * G) * D, G, lane);
     f32x4 acc[4];
     block_scores<T, D>(f, acc);
     float x[4][4];
@@ -244,43 +245,40 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
       }
     mb = fmaxf(mb, __shfl_xor(mb, 16));
     mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = exp2f(m_run - m_new);
     float pw[4][4], lb = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pw[t][i] = exp2f(x[t][i] - m_new);
+        pw[t][i] = exp2f(x[t][i] - mb);
         lb += pw[t][i];
       }
     lb += __shfl_xor(lb, 16);
     lb += __shfl_xor(lb, 32);
-    l_run = l_run * alpha + lb;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+    m_run = mb;
+    l_run = lb;
     block_pv<T, D>(f, pw, o);
   }
 
   // ---- merge the wavefronts of this workgroup through LDS
-  __shared__ float s_o[WAVES][16][D + 4];
-  __shared__ float s_m[WAVES][16], s_l[WAVES][16];
+  __shared__ float s_o[WAVES][GMAX][D + 4];
+  __shared__ float s_m[WAVES][GMAX], s_l[WAVES][GMAX];
+  if (col < G) {
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
+    for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[wave][col][16 * dt + 4 * grp + i] = o[dt][i];
-  if (grp == 0) {
-    s_m[wave][col] = m_run;
-    s_l[wave][col] = l_run;
+      for (int i = 0; i < 4; ++i) s_o[wave][col][16 * dt + 4 * grp + i] = o[dt][i];
+    if (grp == 0) {
+      s_m[wave][col] = m_run;
+      s_l[wave][col] = l_run;
+    }
   }
   __syncthreads();
 
-  const int h = unit % n_kv_heads;
   typename T::storage* out_u = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
   float* pml = part_ml + (size_t)unit * n_split * G * 2;
   float* po = part_o + (size_t)unit * n_split * G * D;
-  for (int idx = tid; idx < G * D; idx += 64 * WAVES) {
+  for (int idx = tid; idx < G * D; idx += NT) {
     const int g = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
@@ -299,10 +297,10 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
       else
         out_u[idx] = r;
     } else {
-      po[((size_t)split * G + g) * D + d] = num;
+      store_coherent(&po[((size_t)split * G + g) * D + d], num);
       if (d == 0) {
-        pml[((size_t)split * G + g) * 2 + 0] = M;
-        pml[((size_t)split * G + g) * 2 + 1] = den;
+        store_coherent(&pml[((size_t)split * G + g) * 2 + 0], M);
+        store_coherent(&pml[((size_t)split * G + g) * 2 + 1], den);
       }
     }
   }
@@ -310,51 +308,100 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
 
   // ---- the last workgroup of this (b, h) merges the splits
   __shared__ int s_last;
-  __threadfence();
+  wait_stores_done();
   __syncthreads();
   if (tid == 0) {
-    const int t = atomicAdd(&ticket[unit], 1);
+    const int t = ticket_take(&ticket[unit]);
     s_last = (t == n_split - 1);
-    if (s_last) ticket[unit] = 0;
+    if (s_last) ticket_reset(&ticket[unit]);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  for (int idx = tid; idx < G * D; idx += 64 * WAVES) {
-    const int g = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pml[((size_t)s * G + g) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float ms = pml[((size_t)s * G + g) * 2];
-      const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      num += wt * po[((size_t)s * G + g) * D + d];
-      den += wt * pml[((size_t)s * G + g) * 2 + 1];
+
+  // every partial this thread needs is loaded in one round trip: the split
+  // maxima and sums into LDS (reusing the merge buffer), the numerators into
+  // registers; then weights, then the weighted sums
+  constexpr int kMaxSplitRegs = 16;
+  float* fm = &s_o[0][0][0];
+  float* fl = fm + n_split * G;
+  __shared__ float s_den[GMAX];
+  for (int i = tid; i < n_split * G; i += NT) {
+    fm[i] = load_coherent(&pml[2 * i]);
+    fl[i] = load_coherent(&pml[2 * i + 1]);
+  }
+  constexpr int PER = (GMAX * D + NT - 1) / NT;  // outputs per thread
+  float v[PER][kMaxSplitRegs];
+  const bool in_regs = n_split <= kMaxSplitRegs;
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int idx = tid + r * NT;
+      const int g = idx / D, d = idx % D;
+#pragma unroll
+      for (int s = 0; s < kMaxSplitRegs; ++s)
+        v[r][s] = (idx < G * D && s < n_split) ? load_coherent(&po[((size_t)s * G + g) * D + d]) : 0.f;
     }
-    const float r = den > 0.f ? num / den : 0.f;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, fm[s * G + tid]);
+    float den = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+      const float ms = fm[s * G + tid];
+      const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      fm[s * G + tid] = wt;
+      den += wt * fl[s * G + tid];
+    }
+    s_den[tid] = den;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = tid + r * NT;
+    if (idx >= G * D) break;
+    const int g = idx / D, d = idx % D;
+    float num = 0.f;
+    if (in_regs) {
+#pragma unroll
+      for (int s = 0; s < kMaxSplitRegs; ++s)
+        if (s < n_split) num += fm[s * G + g] * v[r][s];
+    } else {
+      for (int s = 0; s < n_split; ++s) num += fm[s * G + g] * load_coherent(&po[((size_t)s * G + g) * D + d]);
+    }
+    const float den = s_den[g];
+    const float res = den > 0.f ? num / den : 0.f;
     if constexpr (sizeof(typename T::storage) == 2)
-      out_u[idx] = (uint16_t)f32_to_bf16_bits(r);
+      out_u[idx] = (uint16_t)f32_to_bf16_bits(res);
     else
-      out_u[idx] = r;
+      out_u[idx] = res;
   }
 }
 
-template <class T, int D>
-static void launch(const LaunchAttn& a) {
+template <class T, int D, int WAVES, int GMAX>
+static void launch_w(const LaunchAttn& a) {
   const int units = a.batch * a.n_kv_heads;
-  const int splits = attn_splits(a.k_cap);
   const int G = a.n_q_heads / a.n_kv_heads;
+  const int splits = attn_splits(a.k_cap, G);
   char* ws = (char*)a.ws;
   int32_t* ticket = (int32_t*)ws;
   float* part_ml = (float*)(ws + align256((size_t)units * sizeof(int32_t)));
   float* part_o = (float*)((char*)part_ml + align256((size_t)units * splits * G * 2 * sizeof(float)));
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_kernel<T, D, kAttnWaves>), dim3(splits, units), dim3(64 * kAttnWaves), 0,
+  hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX>), dim3(splits, units), dim3(64 * WAVES), 0,
                      a.stream, (const typename T::storage*)a.q, (const typename T::storage*)a.blocks,
                      a.blocks_per_head, a.phys, a.n_sel, a.k_cap,
                      (const typename T::storage*)a.window_kv, a.window_head_stride,
                      a.window_block_stride, a.pos, scale_log2, a.n_q_heads, a.n_kv_heads, a.nb,
                      (typename T::storage*)a.out, ticket, part_ml, part_o);
+}
+
+template <class T, int D>
+static void launch(const LaunchAttn& a) {
+  if (a.n_q_heads / a.n_kv_heads <= 8)
+    launch_w<T, D, 8, 8>(a);
+  else
+    launch_w<T, D, 4, 16>(a);
 }
 
 void launch_attn(const LaunchAttn& a) {

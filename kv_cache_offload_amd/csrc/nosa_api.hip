@@ -177,7 +177,7 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
                             void* ws, size_t ws_bytes, void* stream) {
   static const char* fn = "nosa_sparse_decode_attn";
   if (int rc = check_dims(dims, fn)) return rc;
-  if (k_cap < 0 || k_cap > 4096) return fail(NOSA_ERR_ARG, fn, "k_cap must be in [0, 4096]");
+  if (k_cap < 0 || k_cap > 512) return fail(NOSA_ERR_UNSUPPORTED, fn, "k_cap must be in [0, 512]");
   if (blocks_per_head < 1 && k_cap > 0) return fail(NOSA_ERR_ARG, fn, "blocks_per_head must be >= 1");
   if (!q || !window_kv || !pos || !out || !n_sel || !ws || (k_cap > 0 && (!blocks || !phys)))
     return fail(NOSA_ERR_ARG, fn, "NULL buffer");

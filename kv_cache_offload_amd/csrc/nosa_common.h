@@ -76,6 +76,26 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Hand-off of partial results between workgroups of one launch.  The L2
+// caches of the XCDs are not coherent with each other; loads and stores at
+// agent scope are (gfx950 issues them with sc1), so a workgroup publishes its
+// partials with coherent stores, waits until they have completed, and only
+// then bumps the ticket; the workgroup that draws the last ticket reads the
+// partials with coherent loads.  This needs no L2 write-back or invalidate.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_done() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ int ticket_take(int* t) {
+  return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ticket_reset(int* t) {
+  __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 

@@ -7,103 +7,131 @@
 // sub-block scores qsum . kbar (two-stage pooling, same summary).
 //
 // One launch per step.  Grid = (scan splits, query rows x KV heads):
-//  * every workgroup scans 128 compressed-key rows of one (row, KV head):
-//    groups of D*esize/16 lanes read one 16-byte chunk each of a row, so a
-//    wavefront load is 1 KiB of contiguous rows; partial dot products are
-//    reduced with cross-lane shuffles and the sub-block scores are written to
-//    the workspace;
-//  * the last workgroup to finish (atomic ticket) max-pools the scores to
-//    blocks, runs two radix selections at once (one per budget, one half of
-//    the workgroup each), merges the two sets in LDS and writes them in
-//    ascending order.  It also resets the ticket for the next call.
+//  * every workgroup scans 128 compressed-key rows (32 blocks) of one
+//    (row, KV head): groups of D*esize/16 lanes read one 16-byte chunk each
+//    of a row, so a wavefront load is 1 KiB of contiguous rows; the partial
+//    dot products are reduced with cross-lane shuffles, max-pooled to block
+//    scores in LDS and published with coherent stores;
+//  * the workgroup that draws the last ticket selects.  Each half of it
+//    (one per budget) bins its scores into 256 equal value bins between their
+//    min and max, finds the bin holding the k-th best, takes every block
+//    above it and ranks the few blocks inside it exactly by (score desc,
+//    id asc).
+//    The union is then written in ascending order with one prefix sum.
 #include "nosa_common.h"
 #include "nosa_launch.h"
 
 namespace nosa {
 
 constexpr int kSelThreads = 256;
+constexpr int kHalf = kSelThreads / 2;
 constexpr int kRowsPerWG = 128;  // compressed-key rows (sub-blocks) per scan workgroup
+constexpr int kBlocksPerWG = kRowsPerWG / kSubsPerBlock;
+constexpr int kBins = 256;
 
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb) {
   const size_t rows = (size_t)batch * n_query * n_kv_heads;
-  return align256(rows * sizeof(int32_t)) + align256(rows * (size_t)nb * kSubsPerBlock * sizeof(float));
+  return align256(rows * sizeof(int32_t)) + align256(rows * (size_t)nb * sizeof(float));
 }
 
 size_t select_lds_bytes(int nb) {
-  // two key arrays, two flag arrays, two 256-bin histograms, scratch
-  return align256((size_t)nb * 4) * 2 + align256((size_t)nb) * 2 + 2 * 256 * 4 + 64 * 4;
+  // two key arrays (4 B per block), two boundary lists (2 B), two flag arrays (1 B)
+  return align256((size_t)nb * 4) * 2 + align256((size_t)nb * 2) * 2 + align256((size_t)nb) * 2;
 }
 
-// Radix selection of the k largest keys among keys[0..n) (ties: lower index
-// first); sets flag[i] = 1 for each selected i.  Run by the NT threads
-// `tid` of one half-workgroup; both halves call it together so the barriers
-// match.  hist: 256 ints; small: 4 ints (both private to the half).
-__device__ void radix_topk(const uint32_t* keys, int n, int k, uint8_t* flag, int* hist,
-                           int* small, int tid, int NT) {
-  const bool active = (k > 0) && (n > 0);
-  if (k > n) k = n;
-  uint32_t prefix = 0, mask = 0;
-  int remaining = k;
-  const int lane = tid & 63;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
-    if (active) {
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t u = keys[i];
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
-      }
+// Inverse of orderable(): the float a key came from.
+__device__ __forceinline__ float key_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Select the k best of keys[0..n) (larger key first, then lower index) and set
+// flag[i] = 1 for them.  Run by the kHalf threads `tid` of one half of the
+// workgroup; both halves call it together so the barriers match.
+//   hist: kBins ints, small: 8 ints, blist: n ids  (all private to the half)
+// The bins split [min, max] of the scores evenly in value (fp64 arithmetic:
+// the bin of a score never decreases as the score grows), so every block in
+// a bin above the threshold bin is selected and only the threshold bin is
+// ranked exactly.
+__device__ void select_top(const uint32_t* keys, int n, int k, uint8_t* flag, int* hist, int* small,
+                           uint16_t* blist, int tid) {
+  const int lane = tid & 63, wv = tid >> 6;
+  const bool all = k >= n;
+  const bool none = k <= 0 || n <= 0;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = tid; i < n; i += kHalf) {
+    const uint32_t u = keys[i];
+    lo = min(lo, u);
+    hi = max(hi, u);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+  }
+  for (int i = tid; i < kBins; i += kHalf) hist[i] = 0;
+  if (lane == 0) {
+    small[2 * wv] = (int)lo;
+    small[2 * wv + 1] = (int)hi;
+  }
+  if (tid == 0) small[5] = 0;
+  __syncthreads();
+  lo = min((uint32_t)small[0], (uint32_t)small[2]);
+  hi = max((uint32_t)small[1], (uint32_t)small[3]);
+  const double vlo = key_value(lo), vhi = key_value(hi);
+  const double scale = vhi > vlo ? (double)kBins / (vhi - vlo) : 0.0;
+  auto bin_of = [&](uint32_t u) { return min(kBins - 1, (int)(((double)key_value(u) - vlo) * scale)); };
+  if (!none && !all)
+    for (int i = tid; i < n; i += kHalf) atomicAdd(&hist[bin_of(keys[i])], 1);
+  __syncthreads();
+  if (!none && !all && wv == 0) {
+    // lane owns bins 255-4*lane .. 252-4*lane (descending)
+    int cnt[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { cnt[j] = hist[kBins - 1 - 4 * lane - j]; local += cnt[j]; }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
     }
-    __syncthreads();
-    if (active && tid < 64) {
-      // lane owns digits 255-4*lane .. 252-4*lane (descending digit order)
-      int c[4], local = 0;
+    int run = incl - local;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; local += c[j]; }
-      int incl = local;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+    for (int j = 0; j < 4; ++j) {
+      if (run < k && run + cnt[j] >= k) {
+        small[4] = kBins - 1 - 4 * lane - j;  // the bin holding the k-th best
+        small[6] = k - run;                   // how many of that bin to take
       }
-      int run = incl - local;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (run < remaining && run + c[j] >= remaining) {
-          small[0] = 255 - 4 * lane - j;
-          small[1] = run;
-        }
-        run += c[j];
-      }
-    }
-    __syncthreads();
-    if (active) {
-      const int d = small[0];
-      remaining -= small[1];
-      prefix |= (uint32_t)d << shift;
-      mask |= 0xFFu << shift;
+      run += cnt[j];
     }
   }
-  // prefix = the k-th largest key; `remaining` of the keys equal to it are taken
-  if (active) {
-    const int n_eq = hist[prefix & 255u];
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t u = keys[i];
-      if (u > prefix || (u == prefix && n_eq == remaining)) flag[i] = 1;
-    }
-    if (n_eq > remaining && tid < 64) {
-      // ties at the threshold: the lowest indices win, scanned in order
-      int left = remaining;
-      for (int base = 0; base < n && left > 0; base += 64) {
-        const int i = base + lane;
-        const bool eq = (i < n) && (keys[i] == prefix);
-        const uint64_t m = __ballot(eq);
-        const int before = __popcll(m & ((1ull << lane) - 1ull));
-        if (eq && before < left) flag[i] = 1;
-        left -= __popcll(m);
+  __syncthreads();
+  const int bstar = small[4];
+  const int take = small[6];
+  if (!none) {
+    for (int i = tid; i < n; i += kHalf) {
+      if (all) {
+        flag[i] = 1;
+        continue;
       }
+      const int bi = bin_of(keys[i]);
+      if (bi > bstar)
+        flag[i] = 1;
+      else if (bi == bstar)
+        blist[atomicAdd(&small[5], 1)] = (uint16_t)i;
+    }
+  }
+  __syncthreads();
+  if (!none && !all) {
+    const int m = small[5];
+    for (int a = tid; a < m; a += kHalf) {
+      const uint32_t ia = blist[a], ua = keys[ia];
+      int rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < m; ++j) {
+        const uint32_t ib = blist[j], ub = keys[ib];
+        rank += (ub > ua) || (ub == ua && ib < ia);
+      }
+      if (rank < take) flag[ia] = 1;
     }
   }
   __syncthreads();
@@ -114,7 +142,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
     const typename T::storage* __restrict__ q, const int32_t* __restrict__ pos,
     const typename T::storage* __restrict__ k_comp, const float* __restrict__ e_blk, int n_query,
     int n_q_heads, int n_kv_heads, int nb, int kq, int ke, int32_t* __restrict__ sel,
-    int32_t* __restrict__ n_sel, int32_t* __restrict__ ticket, float* __restrict__ sig) {
+    int32_t* __restrict__ n_sel, int32_t* __restrict__ ticket, float* __restrict__ score) {
   constexpr int EPC = T::kPer16B;
   constexpr int LPR = D / EPC;               // lanes per compressed-key row
   constexpr int RPP = kSelThreads / LPR;     // rows per pass of the workgroup
@@ -126,17 +154,25 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   const int b = br / n_query;
   const int64_t unit = (int64_t)b * n_kv_heads + h;
   const int k_cap = kq + ke;
+  const int tid = threadIdx.x;
 
   const int p = pos[br];
   const int c = (p >= 0 && p < nb * kBlock) ? p / kBlock : 0;
   const int n_rows = c * kSubsPerBlock;
-  float* my_sig = sig + (size_t)row * nb * kSubsPerBlock;
+  float* my_score = score + (size_t)row * nb;
 
-  // ---- scan: sub-block scores of this workgroup's rows
-  const int tid = threadIdx.x;
-  const int ch = tid % LPR;
-  const int r0 = blockIdx.x * kRowsPerWG + tid / LPR;
-  if ((int)blockIdx.x * kRowsPerWG < n_rows) {
+  // ---- scan: block scores of this workgroup's 32 blocks
+  __shared__ float s_sig[kRowsPerWG];
+  const int row0 = blockIdx.x * kRowsPerWG;
+  if (row0 < n_rows) {
+    const int ch = tid % LPR;
+    const typename T::storage* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D + ch * EPC;
+    uint4 raw[PASSES];
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+      const int rr = row0 + i * RPP + tid / LPR;
+      raw[i] = (rr < n_rows) ? ld16(kc + (size_t)rr * D) : make_uint4(0, 0, 0, 0);
+    }
     float qs[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) qs[e] = 0.0f;
@@ -147,13 +183,6 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
 #pragma unroll
       for (int e = 0; e < EPC; ++e) qs[e] += v[e];
     }
-    const typename T::storage* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D + ch * EPC;
-    uint4 raw[PASSES];
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int rr = r0 + i * RPP;
-      raw[i] = (rr < n_rows) ? ld16(kc + (size_t)rr * D) : make_uint4(0, 0, 0, 0);
-    }
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
       float v[EPC];
@@ -163,71 +192,84 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
       for (int e = 0; e < EPC; ++e) s = fmaf(qs[e], v[e], s);
 #pragma unroll
       for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-      const int rr = r0 + i * RPP;
-      if (ch == 0 && rr < n_rows) my_sig[rr] = s;
+      if (ch == 0) s_sig[i * RPP + tid / LPR] = s;
+    }
+    __syncthreads();
+    if (tid < kBlocksPerWG) {
+      const int blk = blockIdx.x * kBlocksPerWG + tid;
+      if (blk < c) {
+        float m = s_sig[kSubsPerBlock * tid];
+#pragma unroll
+        for (int i = 1; i < kSubsPerBlock; ++i) m = fmaxf(m, s_sig[kSubsPerBlock * tid + i]);
+        store_coherent(&my_score[blk], m);
+      }
     }
   }
 
   // ---- ticket: the last workgroup of this row selects
   __shared__ int s_last;
-  __threadfence();
+  wait_stores_done();
   __syncthreads();
   if (tid == 0) {
-    const int t = atomicAdd(&ticket[row], 1);
+    const int t = ticket_take(&ticket[row]);
     s_last = (t == (int)gridDim.x - 1);
-    if (s_last) ticket[row] = 0;
+    if (s_last) ticket_reset(&ticket[row]);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   extern __shared__ __align__(16) unsigned char lds[];
-  const size_t keys_bytes = align256((size_t)nb * 4);
+  const size_t kb = align256((size_t)nb * 4);
   uint32_t* key_q = reinterpret_cast<uint32_t*>(lds);
-  uint32_t* key_e = reinterpret_cast<uint32_t*>(lds + keys_bytes);
-  uint8_t* flag_q = lds + 2 * keys_bytes;
+  uint32_t* key_e = reinterpret_cast<uint32_t*>(lds + kb);
+  const size_t lb = align256((size_t)nb * 2);
+  uint16_t* blist_q = reinterpret_cast<uint16_t*>(lds + 2 * kb);
+  uint16_t* blist_e = reinterpret_cast<uint16_t*>(lds + 2 * kb + lb);
+  uint8_t* flag_q = lds + 2 * kb + 2 * lb;
   uint8_t* flag_e = flag_q + align256((size_t)nb);
-  int* hist = reinterpret_cast<int*>(lds + 2 * keys_bytes + 2 * align256((size_t)nb));
-  int* small = hist + 2 * 256;
+  __shared__ int s_hist[2][kBins];
+  __shared__ int s_small[2][8];
 
   const float* eb = e_blk + (size_t)unit * nb;
-  for (int j = tid; j < c; j += kSelThreads) {
-    const float* s4 = my_sig + (size_t)j * kSubsPerBlock;
-    float m = s4[0];
-#pragma unroll
-    for (int i = 1; i < kSubsPerBlock; ++i) m = fmaxf(m, s4[i]);
-    key_q[j] = orderable(m);
-    key_e[j] = orderable(eb[j]);
-    flag_q[j] = 0;
-    flag_e[j] = 0;
+  for (int j0 = 0; j0 < c; j0 += 2 * kSelThreads) {
+    // two blocks per thread in flight
+    const int ja = j0 + tid, jb = j0 + kSelThreads + tid;
+    float sa = 0.f, sb = 0.f, ea = 0.f, e2 = 0.f;
+    if (ja < c) { sa = load_coherent(&my_score[ja]); ea = eb[ja]; }
+    if (jb < c) { sb = load_coherent(&my_score[jb]); e2 = eb[jb]; }
+    if (ja < c) { key_q[ja] = orderable(sa); key_e[ja] = orderable(ea); flag_q[ja] = 0; flag_e[ja] = 0; }
+    if (jb < c) { key_q[jb] = orderable(sb); key_e[jb] = orderable(e2); flag_q[jb] = 0; flag_e[jb] = 0; }
   }
   __syncthreads();
-  const int half = tid / (kSelThreads / 2);
-  const int htid = tid % (kSelThreads / 2);
-  radix_topk(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, hist + 256 * half,
-             small + 2 * half, htid, kSelThreads / 2);
+  const int half = tid / kHalf;
+  select_top(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, s_hist[half],
+             s_small[half], half ? blist_e : blist_q, tid % kHalf);
 
-  // ---- union, ascending
-  __shared__ int s_wcount[kSelThreads / 64];
-  const int lane = tid & 63, wave = tid >> 6;
-  int32_t* out = sel + (size_t)row * k_cap;
-  int written = 0;
-  for (int base = 0; base < c; base += kSelThreads) {
-    const int j = base + tid;
-    const bool f = (j < c) && (flag_q[j] | flag_e[j]);
-    const uint64_t m = __ballot(f);
-    if (lane == 0) s_wcount[wave] = __popcll(m);
-    __syncthreads();
-    int off = written;
-    for (int w = 0; w < wave; ++w) off += s_wcount[w];
-    if (f) out[off + __popcll(m & ((1ull << lane) - 1ull))] = j;
-    int tot = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) tot += s_wcount[w];
-    written += tot;
-    __syncthreads();
+  // ---- union in ascending order: each thread owns a contiguous id range
+  __shared__ int s_wsum[kSelThreads / 64];
+  const int per = (c + kSelThreads - 1) / kSelThreads;
+  const int lo = tid * per, hi = min(c, lo + per);
+  int cnt = 0;
+  for (int j = lo; j < hi; ++j) cnt += (flag_q[j] | flag_e[j]) ? 1 : 0;
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
-  for (int i = written + tid; i < k_cap; i += kSelThreads) out[i] = -1;
-  if (tid == 0) n_sel[row] = written;
+  if (lane == 63) s_wsum[wv] = incl;
+  __syncthreads();
+  int off = incl - cnt, total = 0;
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    if (w < wv) off += s_wsum[w];
+    total += s_wsum[w];
+  }
+  int32_t* out = sel + (size_t)row * k_cap;
+  for (int j = lo; j < hi; ++j)
+    if (flag_q[j] | flag_e[j]) out[off++] = j;
+  for (int i = total + tid; i < k_cap; i += kSelThreads) out[i] = -1;
+  if (tid == 0) n_sel[row] = total;
 }
 
 template <class T, int D>
@@ -236,11 +278,11 @@ static void launch(const LaunchSelect& a) {
   const int n_scan = (a.nb * kSubsPerBlock + kRowsPerWG - 1) / kRowsPerWG;
   char* ws = (char*)a.ws;
   int32_t* ticket = (int32_t*)ws;
-  float* sig = (float*)(ws + align256((size_t)rows * sizeof(int32_t)));
+  float* score = (float*)(ws + align256((size_t)rows * sizeof(int32_t)));
   hipLaunchKernelGGL((select_kernel<T, D>), dim3(n_scan, rows), dim3(kSelThreads),
                      select_lds_bytes(a.nb), a.stream, (const typename T::storage*)a.q, a.pos,
                      (const typename T::storage*)a.k_comp, a.e_blk, a.n_query, a.n_q_heads,
-                     a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel, ticket, sig);
+                     a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel, ticket, score);
 }
 
 void launch_select(const LaunchSelect& a) {
