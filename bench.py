@@ -32,6 +32,21 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 N_REPLICAS = 4
+# Byte counters of attn_kernel on this workload (rocprofv3 --pmc, KiB per dispatch),
+# valid for the kernel sources whose digest is recorded here.  FETCH_SIZE reads half
+# of a plain 256 MiB copy's bytes (factor 2.0); WRITE_SIZE reads all of them (1.0).
+ATTN_PMC = {"src_sha256": "1ee6762c8d55029e20cc93bb00aac9d0729674810bdc4d05223b65bfef8b9cf6", "fetch_kib": 16804.75, "write_kib": 685.0}
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
+
+
+def attn_source_digest():
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("attn.hip", "nosa_common.h"):
+        with open(os.path.join(here, "kv_cache_offload_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -42,7 +57,22 @@ def parse():
     ap.add_argument("--no-offload", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch each step instead of graph replay")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 256 MiB, three times: the reference that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
 def log(msg):
@@ -70,6 +100,9 @@ def step_bytes(w, n_sel_rows, positions):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -183,6 +216,9 @@ def main():
     g_attn = capture(attn_only, K_steps)
     attn_ms = time_graph(g_attn)[0] / K_steps
 
+    traffic = None
+    if ATTN_PMC["src_sha256"] == attn_source_digest():
+        traffic = int(ATTN_PMC["fetch_kib"] * 1024 * FETCH_FACTOR + ATTN_PMC["write_kib"] * 1024 * WRITE_FACTOR)
     tok_per_s = w.batch / (ms_per_step * 1e-3)
     step_b = float((sel_bytes + attn_bytes).mean())
     hbm_gbps = step_b / (ms_per_step * 1e-3) / 1e9
@@ -215,7 +251,7 @@ def main():
                     "attn_us": round(attn_ms * 1e3, 3), "attn_gbps": round(attn_gbps, 1)},
         "roofline": {"kernel": "nosa attn_kernel (split-K sparse decode attention)", "bound": "hbm",
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": int(attn_bytes.mean())},
     }
 
@@ -320,7 +356,7 @@ def _cpu_baseline(NI, w, K, V, lam, q):
         from threadpoolctl import threadpool_limits
     except ImportError:                      # pragma: no cover
         threadpool_limits = None
-    batches = (0, 1)
+    batches = tuple(range(w.batch))
     G = w.group
     limiter = threadpool_limits(limits=1) if threadpool_limits else None
     t0 = time.perf_counter()
@@ -334,8 +370,8 @@ def _cpu_baseline(NI, w, K, V, lam, q):
     tokens = len(batches) * w.n_steps
     log(f"oracle: {tokens} tokens in {dt:.1f}s")
     return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer32k, batch entries {list(batches)} (both KV heads), all {w.n_steps} decode "
-                      f"steps incl. pooling the 32K prompt; numpy, BLAS limited to 1 thread",
+            "sample": f"the whole layer32k workload: {len(batches)} batch entries x {w.n_kv_heads} KV heads, "
+                      f"all {w.n_steps} decode steps, incl. pooling the 32K prompt; numpy, BLAS limited to 1 thread",
             "seconds": round(dt, 2)}
 
 
