@@ -55,7 +55,7 @@ def test_workspace_sizes(lib):
     d = _d()
     s = nb.workspace_size(d, nb.OP_SELECT, 1, 16, 48)
     a = nb.workspace_size(d, nb.OP_ATTN, 1, 16, 48)
-    assert s >= 2 * 2 * 64 * 4 * 4 and a > 0
+    assert s >= 2 * 2 * 64 * 4 and a > 0          # one fp32 score per block and row
     assert nb.workspace_size(d, 99, 1, 16, 48) == 0
     assert nb.workspace_size(_d(head_dim=96), nb.OP_ATTN, 1, 16, 48) == 0
 
