@@ -18,11 +18,19 @@
  * - Element type: NOSA_BF16 (bfloat16) or NOSA_F32; head_dim 64 or 128;
  *   n_q_heads a multiple of n_kv_heads with at most 16 query heads per KV
  *   head.
- * - KV block format (one block = 2*64*head_dim elements): the 64 keys
- *   token-major [64][head_dim], then the 64 values transposed
- *   [head_dim][64].  The cache of one layer is [B][Hkv][max_blocks][block];
- *   the HBM pool is [B][Hkv][pool_slots][block].  Host and HBM use the same
- *   format, so a block moves as one contiguous span (32 KiB at D=128 bf16).
+ * - KV block format (one block = 2*64*head_dim elements): the 64 keys,
+ *   then the 64 values, each half stored as 1 KiB MFMA fragments of 64 lanes
+ *   x 16 bytes, so that the attention reads every fragment with one
+ *   contiguous wavefront load.  With tile_token(t, r) = 32(t/2) + 8(r/4) +
+ *   4(t%2) + r%4 and lane = 16g + r (g < 4, r < 16):
+ *     bf16: key fragment t*(D/32)+s holds, in lane 16g+r, K[tile_token(t,r)]
+ *           [32s+8g .. 32s+8g+7]  (t < 4, s < D/32); value fragment
+ *           h*(D/16)+u holds V[32h+8g .. 32h+8g+7][16u+r]  (h < 2, u < D/16);
+ *     fp32: key fragment t*(D/16)+s holds K[16t+r][16s+4g .. 16s+4g+3];
+ *           value fragment t*(D/16)+u holds V[16t+4g .. 16t+4g+3][16u+r].
+ *   The cache of one layer is [B][Hkv][max_blocks][block]; the HBM pool is
+ *   [B][Hkv][pool_slots][block].  Host and HBM use the same format, so a
+ *   block moves as one contiguous span (32 KiB at D=128 bf16).
  * - Decode position p attends tokens [0, p]; its window is block c = p/64
  *   (tokens 64c..p); the candidates for selection are blocks 0..c-1.
  * - Every buffer is allocated and owned by the caller.  "device" means HBM

@@ -10,12 +10,12 @@
 //   S^T (64 tokens x 16 heads) = K (64 x D) . Q^T (D x 16)   4 tiles
 //   O^T (D x 16 heads)        += V^T (D x 64) . P^T (64 x 16)
 // bf16 uses v_mfma_f32_16x16x32_bf16, fp32 uses v_mfma_f32_16x16x4_f32.
-// Every lane reads 16-byte chunks straight from HBM into MFMA operand
-// registers: K rows are token-major and the V half of a block is stored
-// transposed ([D][64]), so both operands are contiguous 16-byte runs and a
-// block's 32 KiB (D=128 bf16) is read exactly once.  The token order of the
-// S tiles is permuted so that each lane's softmax weights are exactly the
-// P^T operand it needs for the V product, with no data exchange.
+// Blocks are stored in MFMA fragment order (nosa_common.h): every operand
+// fragment is one contiguous 1 KiB wavefront load straight from HBM into
+// registers, and a block's 32 KiB (D=128 bf16) is read exactly once.  The
+// token order of the S tiles is permuted so that each lane's softmax weights
+// are exactly the P^T operand it needs for the V product, with no data
+// exchange.
 //
 // Each wavefront keeps its block's max / sum per head (exp2 with the scale
 // folded in) and its unnormalised output in registers; the wavefronts of a
@@ -27,8 +27,10 @@
 
 namespace nosa {
 
-// One block per wavefront; 8 wavefronts per workgroup when the GQA group
-// fits 8 columns, 4 otherwise (the LDS merge buffer holds WAVES x G rows).
+// One block per wavefront and 8 wavefronts per workgroup (4 when the GQA
+// group needs all 16 MFMA columns, to keep the LDS merge buffer within
+// 64 KiB).  Fewer, fuller workgroups beat more, smaller ones here: every
+// split adds a partial to write, a ticket and a share of the final merge.
 static inline int attn_waves(int G) { return G <= 8 ? 8 : 4; }
 static inline int attn_splits(int k_cap, int G) { return (k_cap + 1 + attn_waves(G) - 1) / attn_waves(G); }
 
@@ -96,36 +98,23 @@ __device__ __forceinline__ void load_q(Frags<T, D>& f, const typename T::storage
   }
 }
 
+// One block's operands: 32 fully contiguous 1 KiB wavefront loads (see the
+// block format in nosa_common.h).
 template <class T, int D>
 __device__ __forceinline__ void load_block(Frags<T, D>& f, const typename T::storage* blk, int lane) {
-  const int col = lane & 15, grp = lane >> 4;
-  const typename T::storage* kp = blk;
-  const typename T::storage* vp = blk + (size_t)kBlock * D;  // V^T [D][64]
-  if constexpr (sizeof(typename T::storage) == 2) {
+  constexpr int EPC = T::kPer16B;
+  constexpr int NK = Frags<T, D>::NK, ND = Frags<T, D>::ND;
+  const typename T::storage* kp = blk + lane * EPC;
+  const typename T::storage* vp = blk + (size_t)kBlock * D + lane * EPC;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tok = tile_token<T>(t, col);
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int s = 0; s < Frags<T, D>::NK; ++s) f.k[t][s] = ld16(kp + (size_t)tok * D + 32 * s + 8 * grp);
-    }
+    for (int s = 0; s < NK; ++s) f.k[t][s] = ld16(kp + (size_t)(t * NK + s) * 64 * EPC);
+  constexpr int NVT = sizeof(f.v) / sizeof(f.v[0]);  // 2 token halves (bf16) or 4 tiles (fp32)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+  for (int h = 0; h < NVT; ++h)
 #pragma unroll
-      for (int dt = 0; dt < Frags<T, D>::ND; ++dt)
-        f.v[h2][dt] = ld16(vp + (size_t)(16 * dt + col) * kBlock + 32 * h2 + 8 * grp);
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tok = tile_token<T>(t, col);
-#pragma unroll
-      for (int s = 0; s < Frags<T, D>::NK; ++s) f.k[t][s] = ld16(kp + (size_t)tok * D + 16 * s + 4 * grp);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int dt = 0; dt < Frags<T, D>::ND; ++dt)
-        f.v[t][dt] = ld16(vp + (size_t)(16 * dt + col) * kBlock + 16 * t + 4 * grp);
-  }
+    for (int u = 0; u < ND; ++u) f.v[h][u] = ld16(vp + (size_t)(h * ND + u) * 64 * EPC);
 }
 
 // S^T tiles of one block: acc[t][i] = q_col . K[tile_token(t, 4*grp + i)]
@@ -193,11 +182,14 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   constexpr int ND = D / 16;
   constexpr int NT = 64 * WAVES;
   const int G = n_q_heads / n_kv_heads;
-  const int unit = blockIdx.y;  // b * Hkv + h
+  // grid (units, splits): workgroups are dispatched x-fastest, so every
+  // unit's first split starts before any unit's second and the light last
+  // splits (often just the window) go last
+  const int n_split = gridDim.y;
+  const int split = blockIdx.y;
+  const int unit = blockIdx.x;  // b * Hkv + h
   const int b = unit / n_kv_heads;
   const int h = unit % n_kv_heads;
-  const int split = blockIdx.x;
-  const int n_split = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const size_t blk_elems = (size_t)2 * kBlock * D;
@@ -321,7 +313,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   // every partial this thread needs is loaded in one round trip: the split
   // maxima and sums into LDS (reusing the merge buffer), the numerators into
   // registers; then weights, then the weighted sums
-  constexpr int kMaxSplitRegs = 16;
+  constexpr int kMaxSplitRegs = 20;
   float* fm = &s_o[0][0][0];
   float* fl = fm + n_split * G;
   __shared__ float s_den[GMAX];
@@ -388,7 +380,7 @@ static void launch_w(const LaunchAttn& a) {
   float* part_ml = (float*)(ws + align256((size_t)units * sizeof(int32_t)));
   float* part_o = (float*)((char*)part_ml + align256((size_t)units * splits * G * 2 * sizeof(float)));
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX>), dim3(splits, units), dim3(64 * WAVES), 0,
+  hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX>), dim3(units, splits), dim3(64 * WAVES), 0,
                      a.stream, (const typename T::storage*)a.q, (const typename T::storage*)a.blocks,
                      a.blocks_per_head, a.phys, a.n_sel, a.k_cap,
                      (const typename T::storage*)a.window_kv, a.window_head_stride,

@@ -96,7 +96,66 @@ __device__ __forceinline__ void ticket_reset(int* t) {
   __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// KV block format: MFMA fragment order.
+//
+// A block holds 64 tokens.  Its first 64*D elements are the keys, its last
+// 64*D the values, each stored as a sequence of 1 KiB fragments: fragment f
+// holds, for lane l = 0..63, the 16 bytes lane l feeds to one MFMA of the
+// decode attention.  A wavefront therefore loads every fragment with one
+// fully contiguous 16-byte-per-lane instruction.
+//
+// bf16 (v_mfma_f32_16x16x32_bf16, 8 elements per lane):
+//   key fragment (t, s), t < 4 tiles, s < D/32:   lane l = 16g + r holds
+//     K[tile_token(t, r)][32s + 8g .. +7]
+//   value fragment (h, u), h < 2, u < D/16:         lane l = 16g + r holds
+//     V[32h + 8g .. +7][16u + r]            (8 tokens of one dimension)
+//   tile_token(t, r) = 32(t/2) + 8(r/4) + 4(t%2) + r%4
+// fp32 (v_mfma_f32_16x16x4_f32, 4 elements per lane per 4 MFMAs):
+//   key fragment (t, s), s < D/16:   lane 16g + r holds K[16t + r][16s + 4g .. +3]
+//   value fragment (t, u), u < D/16: lane 16g + r holds V[16t + 4g .. +3][16u + r]
+// Fragments are numbered t-major (key: t*(D/32 or D/16) + s; value: h or t major).
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int key_frags_per_tile(int D, bool bf16) { return bf16 ? D / 32 : D / 16; }
+
+// Element offset, inside a block, of the 16-byte chunk holding key dims
+// [ch*EPC, ch*EPC + EPC) of token `tok` (EPC = 8 for bf16, 4 for fp32).
+template <bool BF16>
+__device__ __forceinline__ int key_chunk_offset(int tok, int ch, int D) {
+  if constexpr (BF16) {
+    const int t = 2 * (tok >> 5) + ((tok >> 2) & 1);
+    const int r = 4 * ((tok >> 3) & 3) + (tok & 3);
+    const int s = ch >> 2, g = ch & 3;
+    return ((t * (D / 32) + s) * 64 + 16 * g + r) * 8;
+  } else {
+    const int t = tok >> 4, r = tok & 15;
+    const int s = ch >> 2, g = ch & 3;
+    return ((t * (D / 16) + s) * 64 + 16 * g + r) * 4;
+  }
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Cross-lane moves through DPP (a VALU modifier; no LDS round trip).
+// 0xB1 = swap with lane^1, 0x4E = lane^2, 0x141 = mirror inside 8 lanes,
+// 0x140 = mirror inside 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16): every lane of a
+// group ends with the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_f32<0xB1>(v);
+  if constexpr (N >= 4) v += dpp_f32<0x4E>(v);
+  if constexpr (N >= 8) v += dpp_f32<0x141>(v);
+  if constexpr (N >= 16) v += dpp_f32<0x140>(v);
+  return v;
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 }  // namespace nosa

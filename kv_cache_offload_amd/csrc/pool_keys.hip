@@ -6,9 +6,9 @@
 // is the max over the 4 sub-block means of a 64-token block.
 //
 // One thread owns one 16-byte column chunk of one sub-block and adds its 16
-// rows serially in token order, so the fp32 sums are bit-exact and each
-// group of D*esize/16 consecutive lanes reads one contiguous key row (256 B
-// for D=128 bf16): a wavefront load covers 4 rows, 1 KiB, fully coalesced.
+// tokens serially in token order, so the fp32 sums are bit-exact.  Keys sit
+// in the block's MFMA fragment order (nosa_common.h); a wavefront load still
+// touches only whole 16-byte chunks of one block's 16 KiB of keys.
 #include "nosa_common.h"
 #include "nosa_launch.h"
 
@@ -33,11 +33,11 @@ __global__ void __launch_bounds__(256) pool_keys_kernel(
   const int64_t unit = r / n_blk;
 
   const typename T::storage* keys = kv + unit * kv_unit_stride + (int64_t)jb * kv_block_stride;
-  const typename T::storage* src = keys + (size_t)(kSub * sb) * D + ch * EPC;
+  constexpr bool BF16 = sizeof(typename T::storage) == 2;
 
   uint4 raw[kSub];
 #pragma unroll
-  for (int i = 0; i < kSub; ++i) raw[i] = ld16(src + (size_t)i * D);
+  for (int i = 0; i < kSub; ++i) raw[i] = ld16(keys + key_chunk_offset<BF16>(kSub * sb + i, ch, D));
   float acc[EPC], v[EPC];
   unpack16(raw[0], acc, T{});
 #pragma unroll

@@ -33,11 +33,45 @@ def torch_dtype(dtype: str):
     return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
 
 
+def _fragment_sources(D: int, bf16: bool):
+    """(token, dim) read by every element of a block's key half and value half.
+
+    The library stores a block in MFMA fragment order: 1 KiB fragments of
+    64 lanes x 16 bytes.  bf16: key fragment (t, s) lane 16g+r holds
+    K[tile_token(t, r)][32s+8g .. +7]; value fragment (h, u) lane 16g+r holds
+    V[32h+8g .. +7][16u+r]; tile_token(t, r) = 32(t//2) + 8(r//4) + 4(t%2) + r%4.
+    fp32: key fragment (t, s) lane 16g+r holds K[16t+r][16s+4g .. +3]; value
+    fragment (t, u) lane 16g+r holds V[16t+4g .. +3][16u+r].
+    """
+    n = BLOCK * D
+    p = np.arange(n)
+    if bf16:
+        nk = D // 32
+        j, lane = p % 8, (p // 8) % 64
+        g, r = lane // 16, lane % 16
+        t, s = p // (nk * 512), (p // 512) % nk
+        k_tok = 32 * (t // 2) + 8 * (r // 4) + 4 * (t % 2) + r % 4
+        k_dim = 32 * s + 8 * g + j
+        nd = D // 16
+        h, u = p // (nd * 512), (p // 512) % nd
+        v_tok = 32 * h + 8 * g + j
+        v_dim = 16 * u + r
+    else:
+        nk = nd = D // 16
+        j, lane = p % 4, (p // 4) % 64
+        g, r = lane // 16, lane % 16
+        t, s = p // (nk * 256), (p // 256) % nk
+        k_tok, k_dim = 16 * t + r, 16 * s + 4 * g + j
+        v_tok, v_dim = 16 * t + 4 * g + j, 16 * (p // 256 % nd) + r
+    return k_tok * D + k_dim, v_tok * D + v_dim
+
+
 def pack_kv_blocks(K: torch.Tensor, V: torch.Tensor, n_blocks: int) -> torch.Tensor:
     """Lay K, V [B, Hkv, T, D] out in the library's block format.
 
-    Returns [B, Hkv, n_blocks, 2*64*D]: per block the 64 keys token-major,
-    then the 64 values transposed ([D][64]).  Tokens past T are zero.
+    Returns [B, Hkv, n_blocks, 2*64*D]: per block the keys, then the values,
+    each in MFMA fragment order (see _fragment_sources).  Tokens past T are
+    zero.
     """
     B, H, T, D = K.shape
     pad = n_blocks * BLOCK - T
@@ -46,8 +80,11 @@ def pack_kv_blocks(K: torch.Tensor, V: torch.Tensor, n_blocks: int) -> torch.Ten
     if pad:
         K = torch.nn.functional.pad(K, (0, 0, 0, pad))
         V = torch.nn.functional.pad(V, (0, 0, 0, pad))
-    kb = K.reshape(B, H, n_blocks, BLOCK * D)
-    vb = V.reshape(B, H, n_blocks, BLOCK, D).transpose(-1, -2).reshape(B, H, n_blocks, BLOCK * D)
+    ks, vs = _fragment_sources(D, K.dtype == torch.bfloat16)
+    ks = torch.from_numpy(ks).to(K.device)
+    vs = torch.from_numpy(vs).to(K.device)
+    kb = K.reshape(B, H, n_blocks, BLOCK * D).index_select(-1, ks)
+    vb = V.reshape(B, H, n_blocks, BLOCK * D).index_select(-1, vs)
     return torch.cat([kb, vb], dim=-1).contiguous()
 
 

@@ -90,6 +90,8 @@ SELECT_CASES = [
     ("bf16 D64 G4 kq only", dict(head_dim=64, n_q_heads=8), 12, 0, [64 * 50 + 9, 64 * 129]),
     ("bf16 D128 G16 ke only", dict(n_q_heads=32), 0, 20, [64 * 33 + 40]),
     ("bf16 D128 wide k", dict(), 100, 150, [64 * 300 + 2]),
+    ("bf16 D128 split scan", dict(), 16, 48, [64 * 1100 + 5, 64 * 700 + 1]),
+    ("f32 D128 split scan", dict(dtype="f32", n_q_heads=4), 5, 7, [64 * 1030 + 63]),
 ]
 
 
