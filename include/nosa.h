@@ -70,7 +70,7 @@ enum nosa_status {
   NOSA_ERR_WORKSPACE = -4     /* workspace smaller than nosa_workspace_size() */
 };
 
-enum nosa_op { NOSA_OP_SELECT = 1, NOSA_OP_ATTN = 2 };
+enum nosa_op { NOSA_OP_SELECT = 1, NOSA_OP_ATTN = 2, NOSA_OP_STEP = 3 };
 
 typedef struct nosa_dims {
   int32_t batch;       /* B */
@@ -237,7 +237,41 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
                             const int32_t* pos, float scale, void* out, void* ws,
                             size_t ws_bytes, void* stream);
 
-/* Workspace bytes needed by op (NOSA_OP_SELECT or NOSA_OP_ATTN); 0 on bad input. */
+/*
+ * nosa_decode_step -- one decode step of a resident cache in one launch:
+ * nosa_select_blocks (n_query = 1) followed by nosa_sparse_decode_attn over
+ * the cache, with the same results.
+ *
+ * Follows from the same passages.  The query-agnostic set Gamma_e depends
+ * only on the block eviction scores, which do not change once a block is
+ * complete (gist.science summary, "1. Algorithme : NOSA": the eviction head
+ * scores KV pairs independently of the query), so the attention over Gamma_e
+ * and the window runs while the compressed-key scan for Gamma_q is still in
+ * flight; only the blocks of Gamma_q outside Gamma_e wait for the scan.
+ *
+ *   q, pos, k_comp, e_blk, kq, ke   as for nosa_select_blocks (n_query = 1;
+ *                    pos is [B]); kq + ke <= 256; at most 8 query heads per
+ *                    KV head
+ *   kv       device [B][Hkv][NB][block]: the cache, read in place (the
+ *            window is block pos/64 of the cache)
+ *   scale    softmax scale
+ *   sel, n_sel  device [B][Hkv][kq+ke], [B][Hkv]: the selected blocks
+ *            (ascending, -1 padded), as nosa_select_blocks writes them
+ *   out      device [B][Hq][D], cache dtype                      (written)
+ *   ws       device workspace of nosa_workspace_size(dims, NOSA_OP_STEP,
+ *            1, kq, ke) bytes, zero-filled once before its first use.  It
+ *            keeps Gamma_e per (b, h) between calls, keyed by the window
+ *            block: the eviction scores of blocks before the window must
+ *            not change between calls with the same window block (they
+ *            never do in decoding; zero-fill the workspace again after
+ *            changing them).  Calls sharing a workspace must not overlap.
+ */
+int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
+                     const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,
+                     int32_t* sel, int32_t* n_sel, void* out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Workspace bytes needed by op (NOSA_OP_SELECT, NOSA_OP_ATTN or NOSA_OP_STEP); 0 on bad input. */
 size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, int32_t kq,
                            int32_t ke);
 

@@ -19,11 +19,11 @@ BLOCK = 64
 SUB = 16
 BF16, F32 = 0, 1
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4
-OP_SELECT, OP_ATTN = 1, 2
+OP_SELECT, OP_ATTN, OP_STEP = 1, 2, 3
 
 EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
-           "nosa_sparse_decode_attn", "nosa_workspace_size", "nosa_status_str",
-           "nosa_last_error")
+           "nosa_sparse_decode_attn", "nosa_decode_step", "nosa_workspace_size",
+           "nosa_status_str", "nosa_last_error")
 
 
 class NosaError(RuntimeError):
@@ -55,13 +55,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_select_blocks.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
     lib.nosa_fetch_blocks.argtypes = [D, P, P, I32, P, P, P, I32, P, P, I32, P, P, P, P, P, P]
     lib.nosa_sparse_decode_attn.argtypes = [D, P, P, I32, P, P, I32, P, I64, I64, P, F, P, P, SZ, P]
+    lib.nosa_decode_step.argtypes = [D, P, P, P, P, I32, I32, P, F, P, P, P, P, SZ, P]
     lib.nosa_workspace_size.argtypes = [D, I32, I32, I32, I32]
     lib.nosa_workspace_size.restype = SZ
     lib.nosa_status_str.argtypes = [I32]
     lib.nosa_status_str.restype = ctypes.c_char_p
     lib.nosa_last_error.argtypes = []
     lib.nosa_last_error.restype = ctypes.c_char_p
-    for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn"):
+    for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
+                 "nosa_decode_step"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -143,3 +145,15 @@ def sparse_decode_attn(d: Dims, q, blocks, blocks_per_head: int, phys, n_sel, k_
                                         float(scale), _ptr(out), _ptr(ws), ws_bytes,
                                         _stream(stream))
     _check("nosa_sparse_decode_attn", rc)
+
+
+def decode_step(d: Dims, q, pos, k_comp, e_blk, kq: int, ke: int, kv, scale: Optional[float], sel,
+                n_sel, out, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if scale is None:
+        scale = 1.0 / math.sqrt(d.head_dim)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = load().nosa_decode_step(ctypes.byref(d), _ptr(q), _ptr(pos), _ptr(k_comp), _ptr(e_blk), kq, ke,
+                                 _ptr(kv), float(scale), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(ws),
+                                 ws_bytes, _stream(stream))
+    _check("nosa_decode_step", rc)

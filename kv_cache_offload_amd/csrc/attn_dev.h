@@ -1,0 +1,359 @@
+// Device building blocks of the NOSA decode attention: one wavefront
+// attends one 64-token block with MFMA; a workgroup merges its wavefronts in
+// LDS; the last workgroup of a (b, h) merges the splits.  Used by the
+// stand-alone attention kernel and by the fused decode-step kernel.
+#pragma once
+
+#include "nosa_common.h"
+
+namespace nosa {
+
+// Token of row r of S tile t, chosen so that lane group g (lanes 16g..16g+15)
+// ends up holding consecutive tokens for the P^T operand.
+template <class T>
+__device__ __forceinline__ int tile_token(int t, int r);
+template <>
+__device__ __forceinline__ int tile_token<Bf16>(int t, int r) {
+  return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
+}
+template <>
+__device__ __forceinline__ int tile_token<F32>(int t, int r) {
+  return 16 * t + r;
+}
+
+template <class T, int D>
+struct Frags;
+
+// bf16: K operand 4 tiles x D/32 k-steps, V operand 2 halves x D/16 d-tiles
+template <int D>
+struct Frags<Bf16, D> {
+  static constexpr int NK = D / 32;
+  static constexpr int ND = D / 16;
+  bf16x8 q[NK];
+  uint4 k[4][NK];
+  uint4 v[2][ND];
+};
+// fp32: K operand 4 tiles x D/16 chunks of 4, V operand 4 tiles x D/16 d-tiles
+template <int D>
+struct Frags<F32, D> {
+  static constexpr int NK = D / 16;
+  static constexpr int ND = D / 16;
+  float4 q[NK];
+  uint4 k[4][NK];
+  uint4 v[4][ND];
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+template <class T, int D>
+__device__ __forceinline__ void load_q(Frags<T, D>& f, const typename T::storage* qg, int G, int lane) {
+  const int col = lane & 15, grp = lane >> 4;
+  if constexpr (sizeof(typename T::storage) == 2) {
+#pragma unroll
+    for (int s = 0; s < Frags<T, D>::NK; ++s) {
+      const uint4 u = (col < G) ? ld16(qg + (size_t)col * D + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0);
+      f.q[s] = as_bf16x8(u);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < Frags<T, D>::NK; ++s) {
+      const uint4 u = (col < G) ? ld16(qg + (size_t)col * D + 16 * s + 4 * grp) : make_uint4(0, 0, 0, 0);
+      f.q[s] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                           __uint_as_float(u.w));
+    }
+  }
+}
+
+// One block's operands: 32 fully contiguous 1 KiB wavefront loads (see the
+// block format in nosa_common.h).
+template <class T, int D>
+__device__ __forceinline__ void load_block(Frags<T, D>& f, const typename T::storage* blk, int lane) {
+  constexpr int EPC = T::kPer16B;
+  constexpr int NK = Frags<T, D>::NK, ND = Frags<T, D>::ND;
+  const typename T::storage* kp = blk + lane * EPC;
+  const typename T::storage* vp = blk + (size_t)kBlock * D + lane * EPC;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int s = 0; s < NK; ++s) f.k[t][s] = ld16(kp + (size_t)(t * NK + s) * 64 * EPC);
+  constexpr int NVT = sizeof(f.v) / sizeof(f.v[0]);  // 2 token halves (bf16) or 4 tiles (fp32)
+#pragma unroll
+  for (int h = 0; h < NVT; ++h)
+#pragma unroll
+    for (int u = 0; u < ND; ++u) f.v[h][u] = ld16(vp + (size_t)(h * ND + u) * 64 * EPC);
+}
+
+// S^T tiles of one block: acc[t][i] = q_col . K[tile_token(t, 4*grp + i)]
+template <class T, int D>
+__device__ __forceinline__ void block_scores(const Frags<T, D>& f, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (sizeof(typename T::storage) == 2) {
+#pragma unroll
+      for (int s = 0; s < Frags<T, D>::NK; ++s)
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.k[t][s]), f.q[s], a, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int s = 0; s < Frags<T, D>::NK; ++s) {
+        const float4 q = f.q[s];
+        a = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.k[t][s].x), q.x, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.k[t][s].y), q.y, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.k[t][s].z), q.z, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.k[t][s].w), q.w, a, 0, 0, 0);
+      }
+    }
+    acc[t] = a;
+  }
+}
+
+// O^T += V^T . P^T for one block
+template <class T, int D>
+__device__ __forceinline__ void block_pv(const Frags<T, D>& f, const float (&p)[4][4], f32x4 (&o)[D / 16]) {
+  if constexpr (sizeof(typename T::storage) == 2) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = (__bf16)p[2 * h2][i];
+        pb[4 + i] = (__bf16)p[2 * h2 + 1][i];
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[h2][dt]), pb, o[dt], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const uint4 v = f.v[t][dt];
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.x), p[t][0], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.y), p[t][1], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.z), p[t][2], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w), p[t][3], o[dt], 0, 0, 0);
+      }
+  }
+}
+
+
+// One wavefront: the unnormalised attention partial of one block, whose
+// first `len` tokens are valid.  m, l are per head (lane column), o holds
+// O^T[d = 16*dt + 4*(lane/16) + i][head = lane%16].
+template <class T, int D>
+__device__ __forceinline__ void attend_block(const typename T::storage* q_group, int G,
+                                             const typename T::storage* blk, int len,
+                                             float scale_log2, int lane, float& m_out,
+                                             float& l_out, f32x4 (&o)[D / 16]) {
+  const int grp = lane >> 4;
+  Frags<T, D> f;
+  load_block<T, D>(f, blk, lane);
+  load_q<T, D>(f, q_group, G, lane);
+  f32x4 acc[4];
+  block_scores<T, D>(f, acc);
+  float x[4][4];
+  float mb = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tile_token<T>(t, 4 * grp + i);
+      x[t][i] = (tok < len) ? acc[t][i] * scale_log2 : -INFINITY;
+      mb = fmaxf(mb, x[t][i]);
+    }
+  mb = fmaxf(mb, __shfl_xor(mb, 16));
+  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  float pw[4][4], lb = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[t][i] = exp2f(x[t][i] - mb);
+      lb += pw[t][i];
+    }
+  lb += __shfl_xor(lb, 16);
+  lb += __shfl_xor(lb, 32);
+  m_out = mb;
+  l_out = lb;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  block_pv<T, D>(f, pw, o);
+}
+
+template <int D, int WAVES, int GMAX>
+struct AttnLds {
+  float o[WAVES][GMAX][D + 4];
+  float m[WAVES][GMAX];
+  float l[WAVES][GMAX];
+  float den[GMAX];
+};
+
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+
+// Workgroup: merge the WAVES wavefront partials (m_run = -inf for an idle
+// wavefront) through LDS.  With a single split the normalised result goes
+// to out_g (the G query heads of the KV head); otherwise this split's
+// partial (unnormalised sums, max, sum) goes to po / pml with coherent
+// stores.
+template <class T, int D, int WAVES, int GMAX>
+__device__ void merge_waves(AttnLds<D, WAVES, GMAX>& L, float m_run, float l_run,
+                            const f32x4 (&o)[D / 16], int G, int tid, int split, int n_split,
+                            typename T::storage* out_g, float* po, float* pml) {
+  const int lane = tid & 63, wave = tid >> 6, col = lane & 15, grp = lane >> 4;
+  constexpr int NT = 64 * WAVES;
+  if (col < G) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.o[wave][col][16 * dt + 4 * grp + i] = o[dt][i];
+    if (grp == 0) {
+      L.m[wave][col] = m_run;
+      L.l[wave][col] = l_run;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int g = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, L.m[w][g]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float wt = (L.m[w][g] == -INFINITY) ? 0.f : exp2f(L.m[w][g] - M);
+      num += wt * L.o[w][g][d];
+      den += wt * L.l[w][g];
+    }
+    if (n_split == 1) {
+      store_out(&out_g[idx], den > 0.f ? num / den : 0.f);
+    } else {
+      store_coherent(&po[((size_t)split * G + g) * D + d], num);
+      if (d == 0) {
+        store_coherent(&pml[((size_t)split * G + g) * 2 + 0], M);
+        store_coherent(&pml[((size_t)split * G + g) * 2 + 1], den);
+      }
+    }
+  }
+}
+
+// Workgroup: merge the wavefront partials through LDS and keep the result
+// on chip: own[r] (numerators of outputs tid + r*NT) in registers, maxima and
+// sums in own_m / own_l (LDS).  For the workgroup that merges all splits.
+template <class T, int D, int WAVES, int GMAX>
+__device__ void merge_waves_keep(AttnLds<D, WAVES, GMAX>& L, float m_run, float l_run,
+                                 const f32x4 (&o)[D / 16], int G, int tid,
+                                 float (&own)[(GMAX * D + 64 * WAVES - 1) / (64 * WAVES)],
+                                 float* own_m, float* own_l) {
+  const int lane = tid & 63, wave = tid >> 6, col = lane & 15, grp = lane >> 4;
+  constexpr int NT = 64 * WAVES;
+  constexpr int PER = (GMAX * D + NT - 1) / NT;
+  if (col < G) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.o[wave][col][16 * dt + 4 * grp + i] = o[dt][i];
+    if (grp == 0) {
+      L.m[wave][col] = m_run;
+      L.l[wave][col] = l_run;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = tid + r * NT;
+    own[r] = 0.f;
+    if (idx >= G * D) continue;
+    const int g = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, L.m[w][g]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float wt = (L.m[w][g] == -INFINITY) ? 0.f : exp2f(L.m[w][g] - M);
+      num += wt * L.o[w][g][d];
+      den += wt * L.l[w][g];
+    }
+    own[r] = num;
+    if (d == 0) {
+      own_m[g] = M;
+      own_l[g] = den;
+    }
+  }
+  __syncthreads();
+}
+
+// The last workgroup of a (b, h): merge the n_split partials in one round
+// trip (split maxima and sums into LDS, numerators into registers), then
+// normalise and store.  Reuses L's merge buffer.  With own_part >= 0 the
+// partial of that split is this workgroup's own, taken from own / own_m /
+// own_l instead of memory.
+template <class T, int D, int WAVES, int GMAX>
+__device__ void merge_splits(AttnLds<D, WAVES, GMAX>& L, int G, int tid, int n_split,
+                             const float* po, const float* pml, typename T::storage* out_g,
+                             int own_part = -1, const float* own = nullptr,
+                             const float* own_m = nullptr, const float* own_l = nullptr) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int kMaxSplitRegs = 20;
+  float* fm = &L.o[0][0][0];
+  float* fl = fm + n_split * G;
+  for (int i = tid; i < n_split * G; i += NT) {
+    if (i / G == own_part) {
+      fm[i] = own_m[i % G];
+      fl[i] = own_l[i % G];
+    } else {
+      fm[i] = load_coherent(&pml[2 * i]);
+      fl[i] = load_coherent(&pml[2 * i + 1]);
+    }
+  }
+  constexpr int PER = (GMAX * D + NT - 1) / NT;  // outputs per thread
+  float v[PER][kMaxSplitRegs];
+  const bool in_regs = n_split <= kMaxSplitRegs;
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int idx = tid + r * NT;
+      const int g = idx / D, d = idx % D;
+#pragma unroll
+      for (int s = 0; s < kMaxSplitRegs; ++s)
+        v[r][s] = (idx < G * D && s < n_split)
+                      ? (s == own_part ? own[r] : load_coherent(&po[((size_t)s * G + g) * D + d]))
+                      : 0.f;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, fm[s * G + tid]);
+    float den = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+      const float ms = fm[s * G + tid];
+      const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      fm[s * G + tid] = wt;
+      den += wt * fl[s * G + tid];
+    }
+    L.den[tid] = den;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = tid + r * NT;
+    if (idx >= G * D) break;
+    const int g = idx / D, d = idx % D;
+    float num = 0.f;
+    if (in_regs) {
+#pragma unroll
+      for (int s = 0; s < kMaxSplitRegs; ++s)
+        if (s < n_split) num += fm[s * G + g] * v[r][s];
+    } else {
+      for (int s = 0; s < n_split; ++s)
+        num += fm[s * G + g] * (s == own_part ? own[r] : load_coherent(&po[((size_t)s * G + g) * D + d]));
+    }
+    const float den = L.den[g];
+    store_out(&out_g[idx], den > 0.f ? num / den : 0.f);
+  }
+}
+
+}  // namespace nosa

@@ -54,6 +54,7 @@ int check_dims(const nosa_dims* d, const char* fn) {
 constexpr int kMaxSelectBlocks = 4096;  // LDS of the selection stage: 10 bytes per block
 constexpr int kMaxPoolSlots = 1024;
 constexpr int kMaxFetchK = 64;          // one wavefront holds the selected set
+constexpr int kMaxStepK = 256;          // the fused step keeps its lists in LDS
 
 }  // namespace
 
@@ -96,7 +97,7 @@ int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query, co
   if (int rc = check_dims(dims, fn)) return rc;
   if (n_query < 1) return fail(NOSA_ERR_ARG, fn, "n_query must be >= 1");
   if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
-  if ((int64_t)kq + ke > dims->max_blocks) return fail(NOSA_ERR_ARG, fn, "kq + ke > max_blocks");
+  if ((int64_t)kq + ke > 65535) return fail(NOSA_ERR_ARG, fn, "kq + ke above 65535");
   if (!q || !pos || !k_comp || !e_blk || !n_sel || !ws || (kq + ke > 0 && !sel))
     return fail(NOSA_ERR_ARG, fn, "NULL buffer");
   if (dims->max_blocks > kMaxSelectBlocks)
@@ -213,6 +214,48 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
   return check_launch(fn);
 }
 
+int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
+                     const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,
+                     int32_t* sel, int32_t* n_sel, void* out, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "nosa_decode_step";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
+  if (kq + ke > kMaxStepK) return fail(NOSA_ERR_UNSUPPORTED, fn, "kq + ke above 256");
+  if (dims->n_q_heads / dims->n_kv_heads > 8)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "more than 8 query heads per KV head");
+  if (dims->max_blocks > kMaxSelectBlocks)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "max_blocks above 4096 (256K tokens)");
+  if (!q || !pos || !k_comp || !e_blk || !kv || !n_sel || !out || !ws || (kq + ke > 0 && !sel))
+    return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (!(scale == scale)) return fail(NOSA_ERR_ARG, fn, "scale is NaN");
+  if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_kv_heads above 65535");
+  const size_t need = nosa_workspace_size(dims, NOSA_OP_STEP, 1, kq, ke);
+  if (ws_bytes < need) return fail(NOSA_ERR_WORKSPACE, fn, "workspace too small");
+  nosa::LaunchStep a{};
+  a.bf16 = dims->dtype == NOSA_BF16;
+  a.head_dim = dims->head_dim;
+  a.batch = dims->batch;
+  a.n_q_heads = dims->n_q_heads;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.nb = dims->max_blocks;
+  a.kq = kq;
+  a.ke = ke;
+  a.q = q;
+  a.pos = pos;
+  a.k_comp = k_comp;
+  a.e_blk = e_blk;
+  a.kv = kv;
+  a.scale = scale;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.out = out;
+  a.ws = ws;
+  a.stream = (hipStream_t)stream;
+  nosa::launch_step(a);
+  return check_launch(fn);
+}
+
 size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, int32_t kq,
                            int32_t ke) {
   if (check_dims(dims, "nosa_workspace_size") != NOSA_OK) return 0;
@@ -222,6 +265,9 @@ size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, i
   if (op == NOSA_OP_ATTN)
     return nosa::attn_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
                                kq + ke);
+  if (op == NOSA_OP_STEP)
+    return nosa::step_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                               dims->max_blocks, kq, ke);
   return 0;
 }
 

@@ -76,9 +76,28 @@ struct LaunchAttn {
   hipStream_t stream;
 };
 
+struct LaunchStep {
+  bool bf16;
+  int head_dim;
+  int batch, n_q_heads, n_kv_heads, nb;
+  int kq, ke;
+  const void* q;
+  const int32_t* pos;
+  const void* k_comp;
+  const float* e_blk;
+  const void* kv;
+  float scale;
+  int32_t* sel;
+  int32_t* n_sel;
+  void* out;
+  void* ws;
+  hipStream_t stream;
+};
+
 // Workspace geometry (bytes), shared by the size query and the launchers.
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb);
 size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap);
+size_t step_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq, int ke);
 // Dynamic LDS the selection kernel needs for nb candidate blocks.
 size_t select_lds_bytes(int nb);
 
@@ -86,5 +105,6 @@ void launch_pool_keys(const LaunchPool& a);
 void launch_select(const LaunchSelect& a);
 void launch_fetch(const LaunchFetch& a);
 void launch_attn(const LaunchAttn& a);
+void launch_step(const LaunchStep& a);
 
 }  // namespace nosa

@@ -23,14 +23,12 @@
 //    written in ascending order with one prefix sum.
 #include "nosa_common.h"
 #include "nosa_launch.h"
+#include "select_dev.h"
 
 namespace nosa {
 
 constexpr int kSelThreads = 1024;
 constexpr int kHalf = kSelThreads / 2;
-constexpr int kHalfWaves = kHalf / 64;
-constexpr int kBins = 256;
-constexpr int kScanUnroll = 8;   // 16-byte loads per thread per round (two rounds in flight)
 
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb) {
   const size_t rows = (size_t)batch * n_query * n_kv_heads;
@@ -53,120 +51,12 @@ static int select_splits(int rows, int nb) {
   return s;
 }
 
-// Inverse of orderable(): the float a key came from.
-__device__ __forceinline__ float key_value(uint32_t u) {
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
-
-// Select the k best of keys[0..n) (larger key first, then lower index) and set
-// flag[i] = 1 for them.  Run by the kHalf threads `tid` of one half of the
-// workgroup; both halves call it together so the barriers match.
-//   hist: kBins ints, small: 32 ints, blist: n ids  (all private to the half)
-// The bins split [min, max] of the scores evenly in value (fp64 arithmetic:
-// the bin of a score never decreases as the score grows), so every block in
-// a bin above the threshold bin is selected and only the threshold bin is
-// ranked exactly.
-__device__ void select_top(const uint32_t* keys, int n, int k, uint8_t* flag, int* hist, int* small,
-                           uint16_t* blist, int tid) {
-  const int lane = tid & 63, wv = tid >> 6;
-  const bool all = k >= n;
-  const bool none = k <= 0 || n <= 0;
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = tid; i < n; i += kHalf) {
-    const uint32_t u = keys[i];
-    lo = min(lo, u);
-    hi = max(hi, u);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
-  }
-  for (int i = tid; i < kBins; i += kHalf) hist[i] = 0;
-  if (lane == 0) {
-    small[2 * wv] = (int)lo;
-    small[2 * wv + 1] = (int)hi;
-  }
-  if (tid == 0) small[17] = 0;
-  __syncthreads();
-  lo = (uint32_t)small[0];
-  hi = (uint32_t)small[1];
-#pragma unroll
-  for (int w = 1; w < kHalfWaves; ++w) {
-    lo = min(lo, (uint32_t)small[2 * w]);
-    hi = max(hi, (uint32_t)small[2 * w + 1]);
-  }
-  const double vlo = key_value(lo), vhi = key_value(hi);
-  const double scale = vhi > vlo ? (double)kBins / (vhi - vlo) : 0.0;
-  auto bin_of = [&](uint32_t u) { return min(kBins - 1, (int)(((double)key_value(u) - vlo) * scale)); };
-  if (!none && !all)
-    for (int i = tid; i < n; i += kHalf) atomicAdd(&hist[bin_of(keys[i])], 1);
-  __syncthreads();
-  if (!none && !all && wv == 0) {
-    // lane owns bins 255-4*lane .. 252-4*lane (descending)
-    int cnt[4], local = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { cnt[j] = hist[kBins - 1 - 4 * lane - j]; local += cnt[j]; }
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    int run = incl - local;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (run < k && run + cnt[j] >= k) {
-        small[16] = kBins - 1 - 4 * lane - j;  // the bin holding the k-th best
-        small[18] = k - run;                   // how many of that bin to take
-      }
-      run += cnt[j];
-    }
-  }
-  __syncthreads();
-  const int bstar = small[16];
-  const int take = small[18];
-  if (!none) {
-    for (int i = tid; i < n; i += kHalf) {
-      if (all) {
-        flag[i] = 1;
-        continue;
-      }
-      const int bi = bin_of(keys[i]);
-      if (bi > bstar)
-        flag[i] = 1;
-      else if (bi == bstar)
-        blist[atomicAdd(&small[17], 1)] = (uint16_t)i;
-    }
-  }
-  __syncthreads();
-  if (!none && !all) {
-    const int m = small[17];
-    for (int a = tid; a < m; a += kHalf) {
-      const uint32_t ia = blist[a], ua = keys[ia];
-      int rank = 0;
-#pragma unroll 8
-      for (int j = 0; j < m; ++j) {
-        const uint32_t ib = blist[j], ub = keys[ib];
-        rank += (ub > ua) || (ub == ua && ib < ia);
-      }
-      if (rank < take) flag[ia] = 1;
-    }
-  }
-  __syncthreads();
-}
-
 template <class T, int D>
 __global__ void __launch_bounds__(kSelThreads) select_kernel(
     const typename T::storage* __restrict__ q, const int32_t* __restrict__ pos,
     const typename T::storage* __restrict__ k_comp, const float* __restrict__ e_blk, int n_query,
     int n_q_heads, int n_kv_heads, int nb, int kq, int ke, int32_t* __restrict__ sel,
     int32_t* __restrict__ n_sel, int32_t* __restrict__ ticket, float* __restrict__ score) {
-  constexpr int EPC = T::kPer16B;
-  constexpr int LPR = D / EPC;            // lanes per compressed-key row
-  constexpr int RPW = kWave / LPR;        // rows per wavefront load (2, 4 or 8)
-  constexpr int WAVES = kSelThreads / kWave;
-  constexpr int ROWS_PER_ROUND = WAVES * kScanUnroll * RPW;
   const int G = n_q_heads / n_kv_heads;
   const int row = blockIdx.y;             // (b * n_query + r) * Hkv + h
   const int h = row % n_kv_heads;
@@ -174,7 +64,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   const int b = br / n_query;
   const int64_t unit = (int64_t)b * n_kv_heads + h;
   const int k_cap = kq + ke;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int n_split = gridDim.x;
 
   const int p = pos[br];
@@ -193,12 +83,12 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   uint8_t* flag_e = flag_q + align256((size_t)nb);
   __shared__ int s_hist[2][kBins];
   __shared__ int s_small[2][32];
+  __shared__ int s_wsum[kSelThreads / 64];
   float* my_score = score + (size_t)row * nb;
 
   // block eviction scores and cleared flags first, so their loads overlap the scan
   const float* eb = e_blk + (size_t)unit * nb;
-  const bool selector = n_split == 1 || blockIdx.x == 0;
-  if (selector) {
+  if (n_split == 1 || blockIdx.x == 0) {
     for (int j = tid; j < c; j += kSelThreads) {
       key_e[j] = orderable(eb[j]);
       flag_q[j] = 0;
@@ -208,87 +98,14 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
 
   // ---- scan: block scores of blocks [blk_lo, blk_hi)
   if (blk_lo < blk_hi) {
-    const int ch = lane % LPR;
-    const int row_lo = kSubsPerBlock * blk_lo, row_hi = kSubsPerBlock * blk_hi;
-    // the query sum first: all G loads in flight at once, ahead of the key stream
-    float qs[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) qs[e] = 0.0f;
-    {
-      const typename T::storage* qh = q + ((size_t)br * n_q_heads + (size_t)h * G) * D + ch * EPC;
-      uint4 qr[16];
-#pragma unroll
-      for (int g = 0; g < 16; ++g) qr[g] = g < G ? ld16(qh + (size_t)g * D) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        float v[EPC];
-        unpack16(qr[g], v, T{});
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) qs[e] += v[e];
-      }
-    }
-    const typename T::storage* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D + ch * EPC;
-    auto load_round = [&](uint4 (&raw)[kScanUnroll], int r0) {
-#pragma unroll
-      for (int u = 0; u < kScanUnroll; ++u) {
-        const int rr = r0 + (wave * kScanUnroll + u) * RPW + lane / LPR;
-        raw[u] = (rr < row_hi) ? ld16(kc + (size_t)rr * D) : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto score_round = [&](const uint4 (&raw)[kScanUnroll], int r0) {
-      float pend = 0.0f;  // first half of a block when a row spans 32 lanes
-#pragma unroll
-      for (int u = 0; u < kScanUnroll; ++u) {
-        const int first = r0 + (wave * kScanUnroll + u) * RPW;  // first row of this load
-        float v[EPC];
-        unpack16(raw[u], v, T{});
-        float s = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) s = fmaf(qs[e], v[e], s);
-        s = group_sum<(LPR < 16 ? LPR : 16)>(s);
-        // row sums sit in lanes 0, 16, 32, 48 (or every 8 lanes); the block
-        // maximum is taken on those wavefront-uniform values
-        if constexpr (LPR == 16) {
-          const float m = fmaxf(fmaxf(lane_value(s, 0), lane_value(s, 16)),
-                                fmaxf(lane_value(s, 32), lane_value(s, 48)));
-          if (lane == 0 && first < row_hi) {
-            if (n_split == 1) key_q[first / kSubsPerBlock] = orderable(m);
-            else store_coherent(&my_score[first / kSubsPerBlock], m);
-          }
-        } else if constexpr (LPR == 8) {
-          const float m0 = fmaxf(fmaxf(lane_value(s, 0), lane_value(s, 8)),
-                                 fmaxf(lane_value(s, 16), lane_value(s, 24)));
-          const float m1 = fmaxf(fmaxf(lane_value(s, 32), lane_value(s, 40)),
-                                 fmaxf(lane_value(s, 48), lane_value(s, 56)));
-          if (lane < 2 && first + 4 * lane < row_hi) {
-            const float m = lane ? m1 : m0;
-            const int blk = first / kSubsPerBlock + lane;
-            if (n_split == 1) key_q[blk] = orderable(m);
-            else store_coherent(&my_score[blk], m);
-          }
-        } else {  // LPR == 32: two rows per load, a block over two loads
-          const float r0s = lane_value(s, 0) + lane_value(s, 16);
-          const float r1s = lane_value(s, 32) + lane_value(s, 48);
-          const float m = fmaxf(r0s, r1s);
-          if ((u & 1) == 0) {
-            pend = m;
-          } else if (lane == 0 && first < row_hi) {
-            const float mb = fmaxf(m, pend);
-            if (n_split == 1) key_q[first / kSubsPerBlock] = orderable(mb);
-            else store_coherent(&my_score[first / kSubsPerBlock], mb);
-          }
-        }
-      }
-    };
-    // two rounds of loads in flight: round i+1 streams in while round i is scored
-    uint4 ra[kScanUnroll], rb[kScanUnroll];
-    load_round(ra, row_lo);
-    for (int r0 = row_lo; r0 < row_hi; r0 += 2 * ROWS_PER_ROUND) {
-      load_round(rb, r0 + ROWS_PER_ROUND);
-      score_round(ra, r0);
-      load_round(ra, r0 + 2 * ROWS_PER_ROUND);
-      score_round(rb, r0 + ROWS_PER_ROUND);
-    }
+    const typename T::storage* qh = q + ((size_t)br * n_q_heads + (size_t)h * G) * D;
+    const typename T::storage* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D;
+    if (n_split == 1)
+      scan_block_scores<T, D, kSelThreads>(qh, G, kc, kSubsPerBlock * blk_lo, kSubsPerBlock * blk_hi, tid,
+                                          [&](int blk, float s) { key_q[blk] = orderable(s); });
+    else
+      scan_block_scores<T, D, kSelThreads>(qh, G, kc, kSubsPerBlock * blk_lo, kSubsPerBlock * blk_hi, tid,
+                                          [&](int blk, float s) { store_coherent(&my_score[blk], s); });
   }
 
   if (n_split > 1) {
@@ -314,32 +131,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   }
   __syncthreads();
   const int half = tid / kHalf;
-  select_top(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, s_hist[half],
-             s_small[half], half ? blist_e : blist_q, tid % kHalf);
+  select_top<kHalf>(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, s_hist[half],
+                    s_small[half], half ? blist_e : blist_q, tid % kHalf);
 
-  // ---- union in ascending order: each thread owns a contiguous id range
-  __shared__ int s_wsum[WAVES];
-  const int per = (c + kSelThreads - 1) / kSelThreads;
-  const int lo = tid * per, hi = min(c, lo + per);
-  int cnt = 0;
-  for (int j = lo; j < hi; ++j) cnt += (flag_q[j] | flag_e[j]) ? 1 : 0;
-  int incl = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
-  int off = incl - cnt, total = 0;
-  for (int w = 0; w < WAVES; ++w) {
-    if (w < wave) off += s_wsum[w];
-    total += s_wsum[w];
-  }
-  int32_t* out = sel + (size_t)row * k_cap;
-  for (int j = lo; j < hi; ++j)
-    if (flag_q[j] | flag_e[j]) out[off++] = j;
-  for (int i = total + tid; i < k_cap; i += kSelThreads) out[i] = -1;
+  // ---- union in ascending order
+  const int total = write_union<kSelThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
   if (tid == 0) n_sel[row] = total;
 }
 

@@ -1,0 +1,239 @@
+// Device building blocks of the NOSA block selection: the compressed-key
+// scan (block scores), the exact top-k of a half workgroup, and the
+// ascending union.  Used by the stand-alone selection kernel and by the
+// fused decode-step kernel.
+#pragma once
+
+#include "nosa_common.h"
+
+namespace nosa {
+
+constexpr int kBins = 256;
+constexpr int kScanUnroll = 8;   // 16-byte loads per thread per round (two rounds in flight)
+
+// Inverse of orderable(): the float a key came from.
+__device__ __forceinline__ float key_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Select the k best of keys[0..n) (larger key first, then lower index) and set
+// flag[i] = 1 for them.  Run by the kHalf threads `tid` of one half of the
+// workgroup (kHalf <= 1024); both halves call it together so the barriers
+// match.  hist: kBins ints, small: 32 ints, blist: n ids (private to the half)
+// The bins split [min, max] of the scores evenly in value (fp64 arithmetic:
+// the bin of a score never decreases as the score grows), so every block in
+// a bin above the threshold bin is selected and only the threshold bin is
+// ranked exactly.
+template <int kHalf>
+__device__ void select_top(const uint32_t* keys, int n, int k, uint8_t* flag, int* hist, int* small,
+                           uint16_t* blist, int tid) {
+  constexpr int kHalfWaves = kHalf / 64;
+  const int lane = tid & 63, wv = tid >> 6;
+  const bool all = k >= n;
+  const bool none = k <= 0 || n <= 0;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = tid; i < n; i += kHalf) {
+    const uint32_t u = keys[i];
+    lo = min(lo, u);
+    hi = max(hi, u);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+  }
+  for (int i = tid; i < kBins; i += kHalf) hist[i] = 0;
+  if (lane == 0) {
+    small[2 * wv] = (int)lo;
+    small[2 * wv + 1] = (int)hi;
+  }
+  if (tid == 0) small[17] = 0;
+  __syncthreads();
+  lo = (uint32_t)small[0];
+  hi = (uint32_t)small[1];
+#pragma unroll
+  for (int w = 1; w < kHalfWaves; ++w) {
+    lo = min(lo, (uint32_t)small[2 * w]);
+    hi = max(hi, (uint32_t)small[2 * w + 1]);
+  }
+  const double vlo = key_value(lo), vhi = key_value(hi);
+  const double scale = vhi > vlo ? (double)kBins / (vhi - vlo) : 0.0;
+  auto bin_of = [&](uint32_t u) { return min(kBins - 1, (int)(((double)key_value(u) - vlo) * scale)); };
+  if (!none && !all)
+    for (int i = tid; i < n; i += kHalf) atomicAdd(&hist[bin_of(keys[i])], 1);
+  __syncthreads();
+  if (!none && !all && wv == 0) {
+    // lane owns bins 255-4*lane .. 252-4*lane (descending)
+    int cnt[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { cnt[j] = hist[kBins - 1 - 4 * lane - j]; local += cnt[j]; }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run < k && run + cnt[j] >= k) {
+        small[16] = kBins - 1 - 4 * lane - j;  // the bin holding the k-th best
+        small[18] = k - run;                   // how many of that bin to take
+      }
+      run += cnt[j];
+    }
+  }
+  __syncthreads();
+  const int bstar = small[16];
+  const int take = small[18];
+  if (!none) {
+    for (int i = tid; i < n; i += kHalf) {
+      if (all) {
+        flag[i] = 1;
+        continue;
+      }
+      const int bi = bin_of(keys[i]);
+      if (bi > bstar)
+        flag[i] = 1;
+      else if (bi == bstar)
+        blist[atomicAdd(&small[17], 1)] = (uint16_t)i;
+    }
+  }
+  __syncthreads();
+  if (!none && !all) {
+    const int m = small[17];
+    for (int a = tid; a < m; a += kHalf) {
+      const uint32_t ia = blist[a], ua = keys[ia];
+      int rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < m; ++j) {
+        const uint32_t ib = blist[j], ub = keys[ib];
+        rank += (ub > ua) || (ub == ua && ib < ia);
+      }
+      if (rank < take) flag[ia] = 1;
+    }
+  }
+  __syncthreads();
+}
+
+
+// Scan compressed-key rows [row_lo, row_hi) (whole blocks) of one KV head
+// with NT threads; put(blk, score) receives every block score (called by
+// one lane per block).  qh: the G query heads of the KV head.
+template <class T, int D, int NT, class Put>
+__device__ __forceinline__ void scan_block_scores(const typename T::storage* qh, int G,
+                                                  const typename T::storage* kc_unit, int row_lo,
+                                                  int row_hi, int tid, Put put) {
+  constexpr int EPC = T::kPer16B;
+  constexpr int LPR = D / EPC;            // lanes per compressed-key row
+  constexpr int RPW = kWave / LPR;        // rows per wavefront load (2, 4 or 8)
+  constexpr int WAVES = NT / kWave;
+  constexpr int ROWS_PER_ROUND = WAVES * kScanUnroll * RPW;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ch = lane % LPR;
+  // the query sum first: all G loads in flight at once, ahead of the key stream
+  float qs[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) qs[e] = 0.0f;
+  {
+    uint4 qr[16];
+#pragma unroll
+    for (int g = 0; g < 16; ++g) qr[g] = g < G ? ld16(qh + (size_t)g * D + ch * EPC) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      float v[EPC];
+      unpack16(qr[g], v, T{});
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) qs[e] += v[e];
+    }
+  }
+  const typename T::storage* kc = kc_unit + ch * EPC;
+  auto load_round = [&](uint4 (&raw)[kScanUnroll], int r0) {
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      const int rr = r0 + (wave * kScanUnroll + u) * RPW + lane / LPR;
+      raw[u] = (rr < row_hi) ? ld16(kc + (size_t)rr * D) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto score_round = [&](const uint4 (&raw)[kScanUnroll], int r0) {
+    float pend = 0.0f;  // first half of a block when a row spans 32 lanes
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      const int first = r0 + (wave * kScanUnroll + u) * RPW;  // first row of this load
+      float v[EPC];
+      unpack16(raw[u], v, T{});
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) s = fmaf(qs[e], v[e], s);
+      s = group_sum<(LPR < 16 ? LPR : 16)>(s);
+      // row sums sit in lanes 0, 16, 32, 48 (or every 8 lanes); the block
+      // maximum is taken on those wavefront-uniform values
+      if constexpr (LPR == 16) {
+        const float m = fmaxf(fmaxf(lane_value(s, 0), lane_value(s, 16)),
+                              fmaxf(lane_value(s, 32), lane_value(s, 48)));
+        if (lane == 0 && first < row_hi) put(first / kSubsPerBlock, m);
+      } else if constexpr (LPR == 8) {
+        const float m0 = fmaxf(fmaxf(lane_value(s, 0), lane_value(s, 8)),
+                               fmaxf(lane_value(s, 16), lane_value(s, 24)));
+        const float m1 = fmaxf(fmaxf(lane_value(s, 32), lane_value(s, 40)),
+                               fmaxf(lane_value(s, 48), lane_value(s, 56)));
+        if (lane < 2 && first + 4 * lane < row_hi) put(first / kSubsPerBlock + lane, lane ? m1 : m0);
+      } else {  // LPR == 32: two rows per load, a block over two loads
+        const float r0s = lane_value(s, 0) + lane_value(s, 16);
+        const float r1s = lane_value(s, 32) + lane_value(s, 48);
+        const float m = fmaxf(r0s, r1s);
+        if ((u & 1) == 0)
+          pend = m;
+        else if (lane == 0 && first < row_hi)
+          put(first / kSubsPerBlock, fmaxf(m, pend));
+      }
+    }
+  };
+  // two rounds of loads in flight: round i+1 streams in while round i is scored
+  uint4 ra[kScanUnroll], rb[kScanUnroll];
+  load_round(ra, row_lo);
+  for (int r0 = row_lo; r0 < row_hi; r0 += 2 * ROWS_PER_ROUND) {
+    load_round(rb, r0 + ROWS_PER_ROUND);
+    score_round(ra, r0);
+    load_round(ra, r0 + 2 * ROWS_PER_ROUND);
+    score_round(rb, r0 + ROWS_PER_ROUND);
+  }
+}
+
+// Write the ids j in [0, c) with pick(j) in ascending order to out[0 ..
+// total), pad to k_cap with -1; returns total (in every thread).  wsum:
+// NT/64 ints of LDS.
+template <int NT, class Pick>
+__device__ int write_ids(Pick pick, int c, int32_t* out, int k_cap, int* wsum, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int per = (c + NT - 1) / NT;
+  const int lo = tid * per, hi = min(c, lo + per);
+  int cnt = 0;
+  for (int j = lo; j < hi; ++j) cnt += pick(j) ? 1 : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int off = incl - cnt, total = 0;
+  for (int w = 0; w < NT / 64; ++w) {
+    if (w < wave) off += wsum[w];
+    total += wsum[w];
+  }
+  for (int j = lo; j < hi; ++j)
+    if (pick(j)) out[off++] = j;
+  for (int i = total + tid; i < k_cap; i += NT) out[i] = -1;
+  return total;
+}
+
+// The union of two flag arrays, ascending (see write_ids).
+template <int NT>
+__device__ int write_union(const uint8_t* flag_q, const uint8_t* flag_e, int c, int32_t* out,
+                           int k_cap, int* wsum, int tid) {
+  return write_ids<NT>([&](int j) { return (flag_q[j] | flag_e[j]) != 0; }, c, out, k_cap, wsum, tid);
+}
+
+}  // namespace nosa

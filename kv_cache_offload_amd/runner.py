@@ -118,6 +118,7 @@ class DecodeLayer:
         self.out = torch.zeros(B, n_q_heads, D, dtype=self.tdt, **z)
         self.ws_sel = torch.zeros(nb.workspace_size(self.dims, nb.OP_SELECT, 1, kq, ke), dtype=torch.uint8, **z)
         self.ws_attn = torch.zeros(nb.workspace_size(self.dims, nb.OP_ATTN, 1, kq, ke), dtype=torch.uint8, **z)
+        self.ws_step = None
         self.pool_slots = pool_slots
         if pool_slots:
             P = pool_slots
@@ -167,6 +168,14 @@ class DecodeLayer:
     def step_resident(self, q, kv, pos, stream=None) -> None:
         self.select(q, pos, stream)
         self.attend_resident(q, kv, pos, stream)
+
+    def step_fused(self, q, kv, pos, stream=None) -> None:
+        """Selection and attention of one step in one launch (resident cache)."""
+        if self.ws_step is None:
+            self.ws_step = torch.zeros(nb.workspace_size(self.dims, nb.OP_STEP, 1, self.kq, self.ke),
+                                       dtype=torch.uint8, device=self.dev)
+        nb.decode_step(self.dims, q, pos, self.k_comp, self.e_blk, self.kq, self.ke, kv, self.scale,
+                       self.sel, self.n_sel, self.out, self.ws_step, stream=stream)
 
     def step_offload(self, q, host_kv, window, pos, step: int, insert_block=None, insert_src=None,
                      side: Optional[torch.cuda.Stream] = None) -> None:

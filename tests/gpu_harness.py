@@ -48,8 +48,9 @@ def device_inputs(w: NI.Workload, K, V, lam, q, device="cuda"):
     return kv, logits, qd, pos
 
 
-def run_resident(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None):
-    """GPU decode in resident mode; returns per-step sel lists and outputs."""
+def run_resident(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None, fused: bool = False):
+    """GPU decode in resident mode (separate calls, or the one-launch step);
+    returns per-step sel lists and outputs."""
     n = w.n_steps if steps is None else steps
     kv, logits, qd, pos = device_inputs(w, K, V, lam, q)
     layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
@@ -62,7 +63,10 @@ def run_resident(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None):
         if c > c_prev:
             layer.pool_blocks(kv, logits, c_prev, c)
             c_prev = c
-        layer.step_resident(qd[t], kv, pos[t])
+        if fused:
+            layer.step_fused(qd[t], kv, pos[t])
+        else:
+            layer.step_resident(qd[t], kv, pos[t])
         sels.append(layer.sel.clone())
         nsels.append(layer.n_sel.clone())
         outs.append(layer.out.float().clone())

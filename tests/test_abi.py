@@ -26,7 +26,8 @@ def _declared():
 
 def test_header_declares_the_four_calls():
     names = _declared()
-    for fn in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn"):
+    for fn in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
+               "nosa_decode_step"):
         assert fn in names
     assert sorted(nb.EXPORTS) == names
 
@@ -143,3 +144,21 @@ def test_attn_checks(lib):
         nb.sparse_decode_attn(*bad, ws_bytes=need, stream=0)
     assert e.value.code == nb.ERR_ARG
     assert "scale" in lib.nosa_last_error().decode()
+
+
+def test_step_checks(lib):
+    d = _d()
+    need = nb.workspace_size(d, nb.OP_STEP, 1, 16, 48)
+    assert need > 0
+    args = [d, FAKE, FAKE, FAKE, FAKE, 16, 48, FAKE, None, FAKE, FAKE, FAKE, FAKE]
+    with pytest.raises(nb.NosaError) as e:
+        nb.decode_step(*args, ws_bytes=need - 1, stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
+    bad = list(args)
+    bad[5], bad[6] = 200, 100
+    with pytest.raises(nb.NosaError) as e:
+        nb.decode_step(*bad, ws_bytes=1 << 30, stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+    with pytest.raises(nb.NosaError) as e:
+        nb.decode_step(_d(n_q_heads=32), *args[1:], ws_bytes=1 << 30, stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED

@@ -318,3 +318,35 @@ def test_prefill128k_chunk_selection():
             _, _, S = O.select_blocks(s_q, E, c, w.kq, w.ke)
             got = list(sel[0, r, h, : n_sel[0, r, h]])
             assert got == S or H.selection_ok(got, s_q, E, c, w.kq, w.ke), (h, r)
+
+
+# ---------------------------------------------------- one-launch decode step
+@pytest.mark.parametrize("wname,over", [
+    ("tiny", {}),
+    ("layer32k", dict(batch=3, prompt_len=64 * 40 + 50, n_steps=100)),     # crosses block ends
+    ("layer32k", dict(batch=2, prompt_len=64 * 200 + 7, n_steps=70, kq=5, ke=0)),
+    ("layer32k", dict(batch=2, prompt_len=64 * 30 + 60, n_steps=10, kq=0, ke=9, head_dim=64, n_q_heads=4)),
+], ids=["tiny", "boundaries", "kq-only", "ke-only-D64"])
+def test_fused_step_matches_oracle(wname, over):
+    _banner(f"fused step {wname} {over}")
+    w = NI.scaled(NI.WORKLOADS[wname], **over) if over else NI.WORKLOADS[wname]
+    K, V, lam, q = NI.layer_inputs(w)
+    s1, n1, o1, _ = H.run_resident(w, K, V, lam, q, fused=True)
+    s2, n2, o2, _ = H.run_resident(w, K, V, lam, q, fused=False)
+    for a, b in zip(n1, n2):
+        assert np.array_equal(a, b)
+    for a, b in zip(s1, s2):
+        assert np.array_equal(a, b)            # same scan arithmetic: identical sets
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
+
+
+def test_fused_step_layer32k_full():
+    _banner("fused step on the full layer32k workload")
+    w = NI.WORKLOADS["layer32k"]
+    K, V, lam, q = NI.layer_inputs(w)
+    s1, n1, o1, _ = H.run_resident(w, K, V, lam, q, fused=True)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
