@@ -259,12 +259,18 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
  *            (ascending, -1 padded), as nosa_select_blocks writes them
  *   out      device [B][Hq][D], cache dtype                      (written)
  *   ws       device workspace of nosa_workspace_size(dims, NOSA_OP_STEP,
- *            1, kq, ke) bytes, zero-filled once before its first use.  It
- *            keeps Gamma_e per (b, h) between calls, keyed by the window
- *            block: the eviction scores of blocks before the window must
- *            not change between calls with the same window block (they
- *            never do in decoding; zero-fill the workspace again after
- *            changing them).  Calls sharing a workspace must not overlap.
+ *            1, kq, ke) bytes, zero-filled once before its first use (and
+ *            again before it is used with other dims, kq or ke).  It keeps
+ *            a launch counter per (b, h) and Gamma_e per (b, h) between
+ *            calls, keyed by the window block: the eviction scores of blocks
+ *            before the window must not change between calls with the same
+ *            window block (they never do in decoding; zero-fill the
+ *            workspace again after changing them).  Calls sharing a
+ *            workspace must not overlap.  The int32 at byte offset
+ *            256 * ceil(4 * B * Hkv / 256) counts hand-off waits between the
+ *            kernel's workgroups that hit their bound (about 0.3 s); it
+ *            stays 0 unless the device failed to run them concurrently, in
+ *            which case the outputs of that call are wrong.
  */
 int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
                      const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,

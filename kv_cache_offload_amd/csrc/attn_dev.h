@@ -64,30 +64,38 @@ __device__ __forceinline__ void load_q(Frags<T, D>& f, const typename T::storage
   }
 }
 
-// One block's operands: 32 fully contiguous 1 KiB wavefront loads (see the
-// block format in nosa_common.h).
-template <class T, int D>
-__device__ __forceinline__ void load_block(Frags<T, D>& f, const typename T::storage* blk, int lane) {
+// Operands of NTL consecutive 16-token tiles t0 .. t0+NTL-1 of one block
+// (NTL = 4: the whole block; NTL = 2: one 32-token half, t0 = 0 or 2): fully
+// contiguous 1 KiB wavefront loads (see the block format in nosa_common.h).
+template <class T, int D, int NTL>
+__device__ __forceinline__ void load_tiles(Frags<T, D>& f, const typename T::storage* blk, int t0, int lane) {
   constexpr int EPC = T::kPer16B;
   constexpr int NK = Frags<T, D>::NK, ND = Frags<T, D>::ND;
   const typename T::storage* kp = blk + lane * EPC;
   const typename T::storage* vp = blk + (size_t)kBlock * D + lane * EPC;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < NTL; ++t)
 #pragma unroll
-    for (int s = 0; s < NK; ++s) f.k[t][s] = ld16(kp + (size_t)(t * NK + s) * 64 * EPC);
-  constexpr int NVT = sizeof(f.v) / sizeof(f.v[0]);  // 2 token halves (bf16) or 4 tiles (fp32)
+    for (int s = 0; s < NK; ++s) f.k[t][s] = ld16(kp + (size_t)((t0 + t) * NK + s) * 64 * EPC);
+  if constexpr (sizeof(typename T::storage) == 2) {
+    // V fragments come in 32-token halves
 #pragma unroll
-  for (int h = 0; h < NVT; ++h)
+    for (int h = 0; h < NTL / 2; ++h)
 #pragma unroll
-    for (int u = 0; u < ND; ++u) f.v[h][u] = ld16(vp + (size_t)(h * ND + u) * 64 * EPC);
+      for (int u = 0; u < ND; ++u) f.v[h][u] = ld16(vp + (size_t)((t0 / 2 + h) * ND + u) * 64 * EPC);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+      for (int u = 0; u < ND; ++u) f.v[t][u] = ld16(vp + (size_t)((t0 + t) * ND + u) * 64 * EPC);
+  }
 }
 
-// S^T tiles of one block: acc[t][i] = q_col . K[tile_token(t, 4*grp + i)]
-template <class T, int D>
+// S^T tiles: acc[t][i] = q_col . K[tile_token(t0 + t, 4*grp + i)]
+template <class T, int D, int NTL>
 __device__ __forceinline__ void block_scores(const Frags<T, D>& f, f32x4 (&acc)[4]) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NTL; ++t) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     if constexpr (sizeof(typename T::storage) == 2) {
 #pragma unroll
@@ -107,12 +115,12 @@ __device__ __forceinline__ void block_scores(const Frags<T, D>& f, f32x4 (&acc)[
   }
 }
 
-// O^T += V^T . P^T for one block
-template <class T, int D>
+// O^T += V^T . P^T over the loaded tiles
+template <class T, int D, int NTL>
 __device__ __forceinline__ void block_pv(const Frags<T, D>& f, const float (&p)[4][4], f32x4 (&o)[D / 16]) {
   if constexpr (sizeof(typename T::storage) == 2) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < NTL / 2; ++h2) {
       bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -125,7 +133,7 @@ __device__ __forceinline__ void block_pv(const Frags<T, D>& f, const float (&p)[
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NTL; ++t)
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const uint4 v = f.v[t][dt];
@@ -137,28 +145,27 @@ __device__ __forceinline__ void block_pv(const Frags<T, D>& f, const float (&p)[
   }
 }
 
-
-// One wavefront: the unnormalised attention partial of one block, whose
-// first `len` tokens are valid.  m, l are per head (lane column), o holds
-// O^T[d = 16*dt + 4*(lane/16) + i][head = lane%16].
-template <class T, int D>
-__device__ __forceinline__ void attend_block(const typename T::storage* q_group, int G,
-                                             const typename T::storage* blk, int len,
+// One wavefront: the unnormalised attention partial of tiles t0 .. t0+NTL-1
+// of one block, whose first `len` tokens are valid.  m, l are per head (lane
+// column), o holds O^T[d = 16*dt + 4*(lane/16) + i][head = lane%16].
+template <class T, int D, int NTL>
+__device__ __forceinline__ void attend_tiles(const typename T::storage* q_group, int G,
+                                             const typename T::storage* blk, int t0, int len,
                                              float scale_log2, int lane, float& m_out,
                                              float& l_out, f32x4 (&o)[D / 16]) {
   const int grp = lane >> 4;
   Frags<T, D> f;
-  load_block<T, D>(f, blk, lane);
+  load_tiles<T, D, NTL>(f, blk, t0, lane);
   load_q<T, D>(f, q_group, G, lane);
   f32x4 acc[4];
-  block_scores<T, D>(f, acc);
+  block_scores<T, D, NTL>(f, acc);
   float x[4][4];
   float mb = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < NTL; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = tile_token<T>(t, 4 * grp + i);
+      const int tok = tile_token<T>(t0 + t, 4 * grp + i);
       x[t][i] = (tok < len) ? acc[t][i] * scale_log2 : -INFINITY;
       mb = fmaxf(mb, x[t][i]);
     }
@@ -166,7 +173,7 @@ __device__ __forceinline__ void attend_block(const typename T::storage* q_group,
   mb = fmaxf(mb, __shfl_xor(mb, 32));
   float pw[4][4], lb = 0.f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < NTL; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pw[t][i] = exp2f(x[t][i] - mb);
@@ -178,7 +185,16 @@ __device__ __forceinline__ void attend_block(const typename T::storage* q_group,
   l_out = lb;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  block_pv<T, D>(f, pw, o);
+  block_pv<T, D, NTL>(f, pw, o);
+}
+
+// A whole block (tiles 0..3).
+template <class T, int D>
+__device__ __forceinline__ void attend_block(const typename T::storage* q_group, int G,
+                                             const typename T::storage* blk, int len,
+                                             float scale_log2, int lane, float& m_out,
+                                             float& l_out, f32x4 (&o)[D / 16]) {
+  attend_tiles<T, D, 4>(q_group, G, blk, 0, len, scale_log2, lane, m_out, l_out, o);
 }
 
 template <int D, int WAVES, int GMAX>
@@ -238,9 +254,26 @@ __device__ void merge_waves(AttnLds<D, WAVES, GMAX>& L, float m_run, float l_run
   }
 }
 
+// Fold one more unnormalised partial (m_b, l_b, o_b) of the same heads into
+// a wavefront's running one (online softmax rescaling).
+template <int ND>
+__device__ __forceinline__ void combine_partial(float& m_run, float& l_run, f32x4 (&o_run)[ND], float m_b,
+                                                float l_b, const f32x4 (&o_b)[ND]) {
+  const float M = fmaxf(m_run, m_b);
+  if (M == -INFINITY) return;
+  const float a = exp2f(m_run - M), b = exp2f(m_b - M);
+  l_run = a * l_run + b * l_b;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o_run[dt][i] = a * o_run[dt][i] + b * o_b[dt][i];
+  m_run = M;
+}
+
 // Workgroup: merge the wavefront partials through LDS and keep the result
-// on chip: own[r] (numerators of outputs tid + r*NT) in registers, maxima and
-// sums in own_m / own_l (LDS).  For the workgroup that merges all splits.
+// on chip: own[r] (numerator of output tid + r*NT, head-major) in registers,
+// the heads' maxima and sums in own_m / own_l (LDS).  Every thread reads all
+// the wavefront values it needs in one batch.
 template <class T, int D, int WAVES, int GMAX>
 __device__ void merge_waves_keep(AttnLds<D, WAVES, GMAX>& L, float m_run, float l_run,
                                  const f32x4 (&o)[D / 16], int G, int tid,
@@ -260,29 +293,172 @@ __device__ void merge_waves_keep(AttnLds<D, WAVES, GMAX>& L, float m_run, float 
     }
   }
   __syncthreads();
+  float mw[PER][WAVES], lw[PER][WAVES], ow[PER][WAVES];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = min(tid + r * NT, G * D - 1);
+    const int g = idx / D, d = idx % D;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      mw[r][w] = L.m[w][g];
+      lw[r][w] = L.l[w][g];
+      ow[r][w] = L.o[w][g][d];
+    }
+  }
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
     const int idx = tid + r * NT;
-    own[r] = 0.f;
-    if (idx >= G * D) continue;
-    const int g = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, L.m[w][g]);
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[r][w]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-      const float wt = (L.m[w][g] == -INFINITY) ? 0.f : exp2f(L.m[w][g] - M);
-      num += wt * L.o[w][g][d];
-      den += wt * L.l[w][g];
+      const float wt = (mw[r][w] == -INFINITY) ? 0.f : exp2f(mw[r][w] - M);
+      num += wt * ow[r][w];
+      den += wt * lw[r][w];
     }
-    own[r] = num;
-    if (d == 0) {
-      own_m[g] = M;
-      own_l[g] = den;
+    own[r] = idx < G * D ? num : 0.f;
+    if (idx < G * D && idx % D == 0) {
+      own_m[idx / D] = M;
+      own_l[idx / D] = den;
     }
   }
   __syncthreads();
+}
+
+// Words of one flagged partial record: GMAX*D numerators (head-major),
+// GMAX maxima, GMAX sums.
+template <int D, int GMAX>
+constexpr int part_record_words() { return GMAX * D + 2 * GMAX; }
+
+// Publish a workgroup's merged partial (from merge_waves_keep) as flagged
+// words; no wait: the merging workgroup polls the words themselves.
+template <int D, int WAVES, int GMAX>
+__device__ void publish_part_ll(int G, int tid, const float (&own)[(GMAX * D + 64 * WAVES - 1) / (64 * WAVES)],
+                                const float* own_m, const float* own_l, uint64_t* rec, uint32_t flag) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int PER = (GMAX * D + NT - 1) / NT;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = tid + r * NT;
+    if (idx < G * D) ll_store(&rec[idx], own[r], flag);
+  }
+  if (tid < G) {
+    ll_store(&rec[GMAX * D + tid], own_m[tid], flag);
+    ll_store(&rec[GMAX * D + GMAX + tid], own_l[tid], flag);
+  }
+}
+
+// The merging workgroup of a (b, h): combine its own partial (own, own_m,
+// own_l from merge_waves_keep, part own_part) with the other n_part - 1,
+// polled as flagged records (record s at recs + s * part_record_words), then
+// normalise and store.  All numerator words are requested at once (up to
+// kRegParts parts in registers; beyond that each word is polled in turn),
+// the maxima and sums go through LDS with one barrier.
+template <class T, int D, int WAVES, int GMAX>
+__device__ void merge_parts_ll(AttnLds<D, WAVES, GMAX>& L, int G, int tid, int n_part, int own_part,
+                               const float (&own)[(GMAX * D + 64 * WAVES - 1) / (64 * WAVES)],
+                               const float* own_m, const float* own_l, const uint64_t* recs,
+                               uint32_t flag, int spin_limit, int* err, typename T::storage* out_g) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int PER = (GMAX * D + NT - 1) / NT;
+  constexpr int REC = part_record_words<D, GMAX>();
+  constexpr int kRegParts = 16;
+  float* fm = &L.o[0][0][0];   // [n_part][G] maxima, then [n_part][G] sums
+  float* fl = fm + n_part * G;
+  const bool in_regs = n_part <= kRegParts;
+  uint64_t w[PER][kRegParts];
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int idx = tid + r * NT;
+#pragma unroll
+      for (int sp = 0; sp < kRegParts; ++sp) {
+        const bool need = idx < G * D && sp < n_part && sp != own_part;
+        w[r][sp] = need ? ll_load(&recs[(size_t)sp * REC + idx])
+                        : ll_word(sp == own_part ? own[r] : 0.f, flag);
+      }
+    }
+  }
+  // maxima and sums: one word per thread
+  for (int i = tid; i < 2 * n_part * G; i += NT) {
+    const int which = i / (n_part * G), j = i % (n_part * G);   // 0: max, 1: sum
+    const int sp = j / G, g = j % G;
+    float v;
+    if (sp == own_part) {
+      v = which ? own_l[g] : own_m[g];
+    } else {
+      const uint64_t* pw = &recs[(size_t)sp * REC + GMAX * D + which * GMAX + g];
+      v = ll_float(ll_wait(pw, ll_load(pw), flag, spin_limit, err));
+    }
+    fm[i] = v;
+  }
+  if (in_regs) {
+    int it = 0;
+    bool ok = false;
+    while (true) {
+      ok = true;
+#pragma unroll
+      for (int r = 0; r < PER; ++r)
+#pragma unroll
+        for (int sp = 0; sp < kRegParts; ++sp) ok = ok && ll_ok(w[r][sp], flag);
+      if (ok || it >= spin_limit) break;
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int idx = tid + r * NT;
+#pragma unroll
+        for (int sp = 0; sp < kRegParts; ++sp)
+          if (!ll_ok(w[r][sp], flag)) w[r][sp] = ll_load(&recs[(size_t)sp * REC + idx]);
+      }
+      ++it;
+    }
+    if (!ok) atomicAdd(err, 1);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = tid + r * NT;
+    if (idx >= G * D) break;
+    const int g = idx / D;
+    float num = 0.f, den = 0.f;
+    if (in_regs) {
+      // every part at a fixed register: all reads issued together
+      float mv[kRegParts], lv[kRegParts];
+#pragma unroll
+      for (int sp = 0; sp < kRegParts; ++sp) {
+        mv[sp] = sp < n_part ? fm[sp * G + g] : -INFINITY;
+        lv[sp] = sp < n_part ? fl[sp * G + g] : 0.f;
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int sp = 0; sp < kRegParts; ++sp) M = fmaxf(M, mv[sp]);
+#pragma unroll
+      for (int sp = 0; sp < kRegParts; ++sp) {
+        const float wt = (mv[sp] == -INFINITY) ? 0.f : exp2f(mv[sp] - M);
+        den += wt * lv[sp];
+        num += wt * ll_float(w[r][sp]);
+      }
+    } else {
+      float M = -INFINITY;
+      for (int sp = 0; sp < n_part; ++sp) M = fmaxf(M, fm[sp * G + g]);
+      for (int sp = 0; sp < n_part; ++sp) {
+        const float ms = fm[sp * G + g];
+        const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+        den += wt * fl[sp * G + g];
+        float v;
+        if (sp == own_part) {
+          v = own[r];
+        } else {
+          const uint64_t* pw = &recs[(size_t)sp * REC + idx];
+          v = ll_float(ll_wait(pw, ll_load(pw), flag, spin_limit, err));
+        }
+        num += wt * v;
+      }
+    }
+    store_out(&out_g[idx], den > 0.f ? num / den : 0.f);
+  }
 }
 
 // The last workgroup of a (b, h): merge the n_split partials in one round

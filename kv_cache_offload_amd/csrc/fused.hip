@@ -5,22 +5,33 @@
 // scores, which are fixed once a block is complete (gist.science summary,
 // "1. Algorithme : NOSA": the eviction head scores KV pairs independently of
 // the query; ED-DMA selects on pre-exponential scores).  So the attention over
-// Gamma_e and the window -- three quarters of the step's bytes at kq/k = 1/4
-// -- does not have to wait for the query-aware scan.  This kernel runs three
-// kinds of workgroups at once:
-//   R1  compressed-key scan + top-kq (+ top-ke) of one KV head, as in
-//       nosa_select_blocks; publishes X = Gamma_q \ Gamma_e and the union;
-//   R2  attention over Gamma_e + the window, started immediately (Gamma_e is
-//       cached per KV head in the workspace and recomputed when the window
-//       moves to a new block);
-//   R3  attention over X, started as soon as R1 publishes it.
-// The last attention workgroup of a (b, h) merges all partials.
+// Gamma_e -- three quarters of the step's bytes at kq/k = 1/4 -- does not
+// wait for the query-aware scan.  Each (b, KV head) unit gets W workgroups:
+//   E workers (j < nE)  scan one slice of the unit's compressed keys and
+//                       publish the block scores, then attend their share of
+//                       Gamma_e (cached per unit in the workspace, keyed by
+//                       the window block, recomputed when the window moves);
+//   Q workers (j >= nE) attend the window while the scores arrive, then each
+//                       takes top-kq itself (the first one also writes the
+//                       union out) and attends its share of X = Gamma_q \
+//                       Gamma_e.
+// Work is dealt in 32-token halves of blocks, one per wavefront at a time.
+// The unit's last workgroup merges all partials, keeping its own on chip.
+// Spreading the scan over every E worker lets it finish while the chip's
+// bandwidth is still free, which shortens the scan -> select -> X chain.
 //
-// Roles follow the order in which workgroups start (a dynamic id from an
-// atomic counter): every R1 workgroup has started before any workgroup that
-// waits for one, and R1 waits for nothing, so the R3 spin-waits always end.
-// The waits are bounded as well; the last workgroup to finish resets the
-// counters and flags for the next launch.
+// Every hand-off between workgroups goes through flagged 8-byte words
+// (payload + launch flag; see nosa_common.h): producers store and move on,
+// consumers poll the words.  The flag is a per-unit launch counter that the
+// merging workgroup advances when it is done -- by then every workgroup of
+// the unit has read it, since the merge depends on all of them -- so the
+// workspace never needs resetting between launches.
+//
+// Workgroup j of unit u has index j * U + u, and every wait is on a
+// workgroup of lower index (Q workers wait on E workers, the merger on all
+// others), which the dispatcher has started earlier, so each wait ends; the
+// waits are bounded as well (a timeout is counted in the workspace and leaves
+// a wrong result, never a hang).
 #include "nosa_common.h"
 #include "nosa_launch.h"
 #include "attn_dev.h"
@@ -31,33 +42,38 @@ namespace nosa {
 constexpr int kStepThreads = 512;
 constexpr int kStepWaves = kStepThreads / 64;
 constexpr int kStepMaxK = 256;        // kq + ke
-constexpr int kSpinLimit = 1 << 22;   // bounded waits (about 0.2 s)
+constexpr int kStepGMax = 8;          // query heads per KV head
+constexpr int kSpinLimit = 1 << 18;   // bounded waits: polls of about 1 us, so about 0.3 s
+constexpr int kScoreRegs = 8;         // score words polled per thread at once (nb <= 4096)
+constexpr int kStepWgsTarget = 256;   // workgroups per launch to aim for: one per CU
 
 struct StepGeometry {
-  int units, S, n2, n3;
-  size_t off_ctl, off_sel_ticket, off_attn_ticket, off_xflag, off_xlist, off_ge, off_score, off_ml, off_o, total;
+  int units, W, nQ, nE;
+  size_t off_epoch, off_err, off_ge, off_score, off_part, total;
 };
 
 static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq,
                                   int ke) {
+  (void)n_q_heads;
+  (void)ke;
   StepGeometry g{};
   g.units = batch * n_kv_heads;
-  const int G = n_q_heads / n_kv_heads;
-  g.S = (nb + 127) / 128;
-  g.S = g.S < 1 ? 1 : (g.S > 16 ? 16 : g.S);
-  g.n2 = (ke + 1 + kStepWaves - 1) / kStepWaves;
-  g.n3 = (kq + kStepWaves - 1) / kStepWaves;
-  const size_t U = g.units, P = g.n2 + g.n3;
+  int W = (kStepWgsTarget + g.units - 1) / g.units;
+  W = W < 2 ? 2 : (W > 16 ? 16 : W);
+  g.W = W;
+  // Q workers: one half block of X per wavefront, at least one E worker left
+  int nQ = kq > 0 ? (2 * kq + kStepWaves - 1) / kStepWaves : 0;
+  nQ = nQ > W - 1 ? W - 1 : nQ;
+  g.nQ = nQ;
+  g.nE = W - nQ;
+  const size_t U = g.units;
+  const size_t rec = (size_t)kStepGMax * head_dim + 2 * kStepGMax;
   size_t o = 0;
-  g.off_ctl = o; o += 256;
-  g.off_sel_ticket = o; o += align256(U * 4);
-  g.off_attn_ticket = o; o += align256(U * 4);
-  g.off_xflag = o; o += align256(U * 4);
-  g.off_xlist = o; o += align256(U * (kq + 1) * 4);
-  g.off_ge = o; o += align256(U * (ke + 2) * 4);
-  g.off_score = o; o += align256(U * (size_t)nb * 4);
-  g.off_ml = o; o += align256(U * P * G * 2 * 4);
-  g.off_o = o; o += align256(U * P * G * (size_t)head_dim * 4);
+  g.off_epoch = o; o += align256(U * 4);
+  g.off_err = o; o += 256;
+  g.off_ge = o; o += align256(U * (kStepMaxK + 1) * 8);
+  g.off_score = o; o += align256(U * (size_t)nb * 8);
+  g.off_part = o; o += align256(U * (size_t)W * rec * 8);
   g.total = o;
   return g;
 }
@@ -68,16 +84,29 @@ size_t step_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int
 
 template <int D>
 static size_t step_lds_bytes(int nb) {
-  const size_t a = sizeof(AttnLds<D, kStepWaves, 8>);
+  const size_t a = sizeof(AttnLds<D, kStepWaves, kStepGMax>);
   const size_t s = select_lds_bytes(nb);
   return a > s ? a : s;
 }
 
-__device__ __forceinline__ void store_coherent_i(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int load_coherent_i(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Attend half blocks first, first + stride, ... < n_half of the list
+// (entry e: half e & 1 of block blk_of(e >> 1), len_of(e >> 1) valid tokens),
+// folding them into the wavefront's running partial.
+template <class T, int D, class BlkOf, class LenOf>
+__device__ __forceinline__ void attend_halves(const typename T::storage* q_group, int G,
+                                              const typename T::storage* unit_kv, int nb, int first, int stride,
+                                              int n_half, BlkOf blk_of, LenOf len_of, float scale_log2, int lane,
+                                              float& m_run, float& l_run, f32x4 (&o)[D / 16]) {
+  const size_t blk_elems = (size_t)2 * kBlock * D;
+  for (int e = first; e < n_half; e += stride) {
+    const int blk = blk_of(e >> 1);
+    if (blk < 0 || blk >= nb) continue;
+    float mb, lb;
+    f32x4 ob[D / 16];
+    attend_tiles<T, D, 2>(q_group, G, unit_kv + (size_t)blk * blk_elems, 2 * (e & 1), len_of(e >> 1),
+                          scale_log2, lane, mb, lb, ob);
+    combine_partial<D / 16>(m_run, l_run, o, mb, lb, ob);
+  }
 }
 
 template <class T, int D>
@@ -86,239 +115,216 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     const typename T::storage* __restrict__ k_comp, const float* __restrict__ e_blk,
     const typename T::storage* __restrict__ kv, int n_q_heads, int n_kv_heads, int nb, int kq,
     int ke, float scale_log2, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
-    typename T::storage* __restrict__ out, unsigned char* __restrict__ ws, int S, int n2, int n3,
-    size_t off_sel_ticket, size_t off_attn_ticket, size_t off_xflag, size_t off_xlist,
-    size_t off_ge, size_t off_score, size_t off_ml, size_t off_o) {
+    typename T::storage* __restrict__ out, unsigned char* __restrict__ ws, int W, int nQ,
+    size_t off_err, size_t off_ge, size_t off_score, size_t off_part) {
   constexpr int ND = D / 16;
+  constexpr int PER = (kStepGMax * D + kStepThreads - 1) / kStepThreads;
+  constexpr int REC = part_record_words<D, kStepGMax>();
+  constexpr int GER = (kStepMaxK + 1 + kStepThreads - 1) / kStepThreads;   // cache words per thread
   const int G = n_q_heads / n_kv_heads;
-  const int U = gridDim.x / (S + n2 + n3);
-  const int total_wgs = gridDim.x;
+  const int U = gridDim.x / W;
+  const int nE = W - nQ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k_cap = kq + ke;
-  const size_t blk_elems = (size_t)2 * kBlock * D;
 
-  int* ctl = reinterpret_cast<int*>(ws);                 // [0] start order, [1] finished, [2] wait timeouts
-  int* sel_ticket = reinterpret_cast<int*>(ws + off_sel_ticket);
-  int* attn_ticket = reinterpret_cast<int*>(ws + off_attn_ticket);
-  int* xflag = reinterpret_cast<int*>(ws + off_xflag);
-  int* xlist_all = reinterpret_cast<int*>(ws + off_xlist);
-  int* ge_all = reinterpret_cast<int*>(ws + off_ge);
-  float* score_all = reinterpret_cast<float*>(ws + off_score);
-  float* ml_all = reinterpret_cast<float*>(ws + off_ml);
-  float* o_all = reinterpret_cast<float*>(ws + off_o);
+  const int unit = blockIdx.x % U, j = blockIdx.x / U;
+  const bool is_q = j >= nE;
+  const int b = unit / n_kv_heads, h = unit % n_kv_heads;
+  int* epoch = reinterpret_cast<int*>(ws);
+  int* err = reinterpret_cast<int*>(ws + off_err);
+  uint64_t* score_ll = reinterpret_cast<uint64_t*>(ws + off_score) + (size_t)unit * nb;
+  // Gamma_e cache: word 0 = count, words 1.. = ids, each tagged with the
+  // window block + 1 it was computed for
+  uint64_t* ge = reinterpret_cast<uint64_t*>(ws + off_ge) + (size_t)unit * (kStepMaxK + 1);
+  const typename T::storage* q_group = q + ((size_t)b * n_q_heads + (size_t)h * G) * D;
+  const typename T::storage* unit_kv = kv + (size_t)unit * nb * ((size_t)2 * kBlock * D);
+  const float* eb = e_blk + (size_t)unit * nb;
 
   extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ int s_hist[2][kBins];
-  __shared__ int s_small[2][32];
+  __shared__ int s_hist[kBins];
+  __shared__ int s_small[32];
   __shared__ int s_wsum[kStepWaves];
   __shared__ int s_list[kStepMaxK];
-  __shared__ int s_misc[4];
-
-  if (tid == 0) s_misc[0] = atomicAdd(&ctl[0], 1);
-  __syncthreads();
-  const int wid = s_misc[0];
-  int role, unit, part;
-  if (wid >= total_wgs) {
-    // the start-order counter was not reset (an earlier launch did not
-    // finish): do nothing rather than touch memory for a role that does not
-    // exist; the caller re-zeroes the workspace
-    role = 0; unit = 0; part = 0;
-    if (tid == 0) atomicAdd(&ctl[2], 1);
-  } else if (wid < U * S) {
-    role = 1; unit = wid % U; part = wid / U;
-  } else if (wid < U * (S + n2)) {
-    role = 2; unit = (wid - U * S) % U; part = (wid - U * S) / U;
-  } else {
-    role = 3; unit = (wid - U * (S + n2)) % U; part = (wid - U * (S + n2)) / U;
-  }
-  const int b = unit / n_kv_heads, h = unit % n_kv_heads;
-  const int p = pos[b];
-  const bool valid_pos = (p >= 0 && p < nb * kBlock);
-  const int c = valid_pos ? p / kBlock : 0;
-  const typename T::storage* q_group = q + ((size_t)b * n_q_heads + (size_t)h * G) * D;
-  const float* eb = e_blk + (size_t)unit * nb;
-  int* xlist = xlist_all + (size_t)unit * (kq + 1);
-  int* ge = ge_all + (size_t)unit * (ke + 2);
-
+  __shared__ float s_own_m[kStepGMax], s_own_l[kStepGMax];
   const size_t kb = align256((size_t)nb * 4), lb = align256((size_t)nb * 2);
   uint32_t* key_q = reinterpret_cast<uint32_t*>(lds);
   uint32_t* key_e = reinterpret_cast<uint32_t*>(lds + kb);
-  uint16_t* blist_q = reinterpret_cast<uint16_t*>(lds + 2 * kb);
-  uint16_t* blist_e = reinterpret_cast<uint16_t*>(lds + 2 * kb + lb);
+  uint16_t* blist = reinterpret_cast<uint16_t*>(lds + 2 * kb);
   uint8_t* flag_q = lds + 2 * kb + 2 * lb;
   uint8_t* flag_e = flag_q + align256((size_t)nb);
 
-  if (role == 1) {
-    // ---------------- R1: scan, top-k, union, publish X
-    float* my_score = score_all + (size_t)unit * nb;
-    const int bps = (nb + S - 1) / S;
-    const int blk_lo = min(c, part * bps), blk_hi = min(c, blk_lo + bps);
-    if (blk_lo < blk_hi) {
-      const typename T::storage* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D;
-      scan_block_scores<T, D, kStepThreads>(q_group, G, kc, kSubsPerBlock * blk_lo, kSubsPerBlock * blk_hi, tid,
-                                            [&](int blk, float s) { store_coherent(&my_score[blk], s); });
-    }
-    wait_stores_done();
-    __syncthreads();
-    if (tid == 0) {
-      const int t = ticket_take(&sel_ticket[unit]);
-      s_misc[1] = (t == S - 1);
-      if (s_misc[1]) ticket_reset(&sel_ticket[unit]);
-    }
-    __syncthreads();
-    if (s_misc[1]) {
-      for (int j = tid; j < c; j += kStepThreads) {
-        key_q[j] = orderable(load_coherent(&my_score[j]));
-        key_e[j] = orderable(eb[j]);
-        flag_q[j] = 0;
-        flag_e[j] = 0;
-      }
-      __syncthreads();
-      const int half = tid / (kStepThreads / 2);
-      select_top<kStepThreads / 2>(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q,
-                                   s_hist[half], s_small[half], half ? blist_e : blist_q,
-                                   tid % (kStepThreads / 2));
-      // X = Gamma_q \ Gamma_e first (ascending): the R3 workgroups wait on it
-      const int nx = write_ids<kStepThreads>([&](int j) { return flag_q[j] && !flag_e[j]; }, c, s_list,
-                                             kq, s_wsum, tid);
-      __syncthreads();
-      for (int i = tid; i < nx; i += kStepThreads) store_coherent_i(&xlist[1 + i], s_list[i]);
-      if (tid == 0) store_coherent_i(&xlist[0], nx);
-      wait_stores_done();
-      __syncthreads();
-      if (tid == 0) store_coherent_i(&xflag[unit], 1);
-      // then the union (the call's selection output) and the Gamma_e cache
-      const int total = write_union<kStepThreads>(flag_q, flag_e, c, sel + (size_t)unit * k_cap, k_cap, s_wsum, tid);
-      if (tid == 0) n_sel[unit] = total;
-      if (tid == 0) s_misc[2] = load_coherent_i(&ge[0]);
-      __syncthreads();
-      if (s_misc[2] != c) {
-        const int nge = write_ids<kStepThreads>([&](int j) { return flag_e[j] != 0; }, c, s_list, ke,
-                                                s_wsum, tid);
-        __syncthreads();
-        for (int i = tid; i < nge; i += kStepThreads) store_coherent_i(&ge[2 + i], s_list[i]);
-        if (tid == 0) store_coherent_i(&ge[1], nge);
-        wait_stores_done();
-        __syncthreads();
-        if (tid == 0) store_coherent_i(&ge[0], c);
-      }
-    }
-  } else if (role != 0) {
-    // ---------------- R2 / R3: attention partials
-    int n_ent = 0, nge = 0;
-    if (role == 2) {
-      // Gamma_e from the cache, or recomputed here when the window moved
-      if (tid == 0) s_misc[2] = load_coherent_i(&ge[0]);
-      __syncthreads();
-      if (s_misc[2] == c) {
-        nge = min(max(load_coherent_i(&ge[1]), 0), min(ke, c));
-        for (int i = tid; i < nge; i += kStepThreads) s_list[i] = load_coherent_i(&ge[2 + i]);
-      } else {
-        for (int j = tid; j < c; j += kStepThreads) {
-          key_e[j] = orderable(eb[j]);
-          flag_e[j] = 0;
-        }
-        __syncthreads();
-        select_top<kStepThreads>(key_e, c, ke, flag_e, s_hist[0], s_small[0], blist_e, tid);
-        nge = write_union<kStepThreads>(flag_e, flag_e, c, s_list, ke, s_wsum, tid);
-      }
-      __syncthreads();
-      n_ent = valid_pos ? nge + 1 : 0;   // Gamma_e, then the window
-    } else {
-      // wait for R1 to publish X (bounded)
-      if (tid == 0) {
-        int it = 0;
-        while (load_coherent_i(&xflag[unit]) == 0 && it < kSpinLimit) {
-          __builtin_amdgcn_s_sleep(2);
-          ++it;
-        }
-        if (it == kSpinLimit) atomicAdd(&ctl[2], 1);
-        s_misc[3] = it == kSpinLimit ? 0 : min(max(load_coherent_i(&xlist[0]), 0), kq);
-      }
-      __syncthreads();
-      const int nx = s_misc[3];
-      for (int i = tid; i < nx; i += kStepThreads) s_list[i] = load_coherent_i(&xlist[1 + i]);
-      __syncthreads();
-      n_ent = nx;
-    }
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 o[ND];
+  // ---- prologue: the position, the launch counter, the Gamma_e cache and
+  // (Q workers) the unit's block scores are requested together; nothing waits
+  // for them before the scan's own loads are out
+  const int p_raw = pos[b];
+  const int e_raw = load_coherent_i(&epoch[unit]);
+  uint64_t gw[GER];
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int e = part * kStepWaves + wave;
-    if (e < n_ent) {
-      const typename T::storage* unit_kv = kv + (size_t)unit * nb * blk_elems;
-      int blk, len;
-      if (role == 2 && e == nge) {
-        blk = c;
-        len = p - c * kBlock + 1;
-      } else {
-        blk = s_list[e];
-        len = kBlock;
-      }
-      if (blk >= 0 && blk < nb)
-        attend_block<T, D>(q_group, G, unit_kv + (size_t)blk * blk_elems, len, scale_log2, lane, m_run, l_run, o);
-    }
-    auto& L = *reinterpret_cast<AttnLds<D, kStepWaves, 8>*>(lds);
-    const int n_part = n2 + n3;
-    const int my_part = role == 2 ? part : n2 + part;
-    float* pml = ml_all + (size_t)unit * n_part * G * 2;
-    float* po = o_all + (size_t)unit * n_part * G * D;
-    typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
-    // the unit's merger is its attention workgroup that starts last (R3's
-    // last part, else R2's): every other one has started before it, so its
-    // bounded wait for their partials ends; it keeps its own partial on chip
-    const bool merger = n3 > 0 ? (role == 3 && part == n3 - 1) : (role == 2 && part == n2 - 1);
-    if (n_part == 1) {
-      merge_waves<T, D, kStepWaves, 8>(L, m_run, l_run, o, G, tid, my_part, n_part, out_g, po, pml);
-    } else if (!merger) {
-      merge_waves<T, D, kStepWaves, 8>(L, m_run, l_run, o, G, tid, my_part, n_part, out_g, po, pml);
-      wait_stores_done();
-      __syncthreads();
-      if (tid == 0) ticket_take(&attn_ticket[unit]);
-    } else {
-      __shared__ float s_own_m[8], s_own_l[8];
-      float own[(8 * D + kStepThreads - 1) / kStepThreads];
-      merge_waves_keep<T, D, kStepWaves, 8>(L, m_run, l_run, o, G, tid, own, s_own_m, s_own_l);
-      if (tid == 0) {
-        int it = 0;
-        while (load_coherent_i(&attn_ticket[unit]) < n_part - 1 && it < kSpinLimit) {
-          __builtin_amdgcn_s_sleep(1);
-          ++it;
-        }
-        if (it == kSpinLimit) atomicAdd(&ctl[2], 1);
-        ticket_reset(&attn_ticket[unit]);
-      }
-      __syncthreads();
-      merge_splits<T, D, kStepWaves, 8>(L, G, tid, n_part, po, pml, out_g, my_part, own, s_own_m, s_own_l);
+  for (int r = 0; r < GER; ++r) {
+    const int i = tid + r * kStepThreads;
+    gw[r] = i <= ke ? ll_load(&ge[i]) : 0;
+  }
+  uint64_t w_sc[kScoreRegs];
+  if (is_q) {
+#pragma unroll
+    for (int i = 0; i < kScoreRegs; ++i) {
+      const int jj = tid + i * kStepThreads;
+      w_sc[i] = jj < nb ? ll_load(&score_ll[jj]) : 0;
     }
   }
 
-  // ---- the last workgroup to finish resets the start order and the flags
-  wait_stores_done();
-  __syncthreads();
-  if (tid == 0) s_misc[0] = atomicAdd(&ctl[1], 1);
-  __syncthreads();
-  if (s_misc[0] == total_wgs - 1) {
-    for (int u = tid; u < U; u += kStepThreads) store_coherent_i(&xflag[u], 0);
-    if (tid == 0) {
-      store_coherent_i(&ctl[0], 0);
-      store_coherent_i(&ctl[1], 0);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the scan of E worker j covers its slice of all nb blocks (scores of
+  // blocks past the window are computed and dropped), so its loads need
+  // nothing from the prologue
+  const int bps = (nb + nE - 1) / nE;
+  const int slice_lo = min(nb, j * bps), slice_hi = min(nb, slice_lo + bps);
+  float* s_sc = reinterpret_cast<float*>(lds);
+  if (!is_q && kq > 0 && slice_lo < slice_hi) {
+    const typename T::storage* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D;
+    scan_block_scores<T, D, kStepThreads>(q_group, G, kc, kSubsPerBlock * slice_lo, kSubsPerBlock * slice_hi, tid,
+                                          [&](int blk, float sc) { s_sc[blk - slice_lo] = sc; });
+  }
+
+  // ---- now the prologue values
+  const bool valid_pos = (p_raw >= 0 && p_raw < nb * kBlock);
+  const int c = valid_pos ? p_raw / kBlock : 0;
+  const int win_len = valid_pos ? p_raw - c * kBlock + 1 : 0;
+  // this launch's flag: the unit's launch counter + 1 (never 0, which is
+  // what a never-written word holds)
+  const uint32_t flag = (uint32_t)__builtin_amdgcn_readfirstlane(e_raw) + 1u;
+  const uint32_t ge_tag = (uint32_t)c + 1u;
+  const int ge_cap = min(ke, c);
+  // the cache is current when its count and every listed id carry this
+  // window block's tag
+  bool mine = true;
+#pragma unroll
+  for (int r = 0; r < GER; ++r) {
+    const int i = tid + r * kStepThreads;
+    if (i >= 1 && i <= ge_cap) mine = mine && ll_ok(gw[r], ge_tag);
+    if (i == 0) mine = mine && ll_ok(gw[r], ge_tag) && (int)(uint32_t)gw[r] == ge_cap;
+  }
+  if (!is_q && kq > 0) {
+    // publish this slice's scores of blocks before the window
+    __syncthreads();
+    const int pub_hi = min(slice_hi, c);
+    for (int i = tid; i < pub_hi - slice_lo; i += kStepThreads) ll_store(&score_ll[slice_lo + i], s_sc[i], flag);
+  }
+  const bool cache_ok = __syncthreads_or(mine ? 0 : 1) == 0;   // also: s_sc dead
+
+  if (!is_q) {
+    // ---------------- E worker: Gamma_e
+    int nge;
+    if (cache_ok) {
+      nge = ge_cap;
+#pragma unroll
+      for (int r = 0; r < GER; ++r) {
+        const int i = tid + r * kStepThreads;
+        if (i >= 1 && i <= ge_cap) s_list[i - 1] = (int)(uint32_t)gw[r];
+      }
+    } else {
+      for (int jj = tid; jj < c; jj += kStepThreads) {
+        key_e[jj] = orderable(eb[jj]);
+        flag_e[jj] = 0;
+      }
+      __syncthreads();
+      select_top<kStepThreads>(key_e, c, ke, flag_e, s_hist, s_small, blist, tid);
+      nge = write_ids<kStepThreads>([&](int jj) { return flag_e[jj] != 0; }, c, s_list, ke, s_wsum, tid);
+      if (j == 0) {
+        // refresh the cache (every word tagged, so no ordering is needed)
+        __syncthreads();
+        for (int i = tid; i < nge; i += kStepThreads) ll_store(&ge[1 + i], (uint32_t)s_list[i], ge_tag);
+        if (tid == 0) ll_store(&ge[0], (uint32_t)nge, ge_tag);
+      }
+    }
+    __syncthreads();
+    if (nQ == 0 && j == 0) {
+      // no query-aware budget: the selection output is Gamma_e
+      int32_t* su = sel + (size_t)unit * k_cap;
+      for (int i = tid; i < k_cap; i += kStepThreads) su[i] = i < nge ? s_list[i] : -1;
+      if (tid == 0) n_sel[unit] = nge;
+    }
+    // Gamma_e halves over the E workers' wavefronts (and the window's two
+    // halves when there are no Q workers)
+    const int n_half = 2 * nge + (nQ == 0 && valid_pos ? 2 : 0);
+    attend_halves<T, D>(q_group, G, unit_kv, nb, j * kStepWaves + wave, nE * kStepWaves, n_half,
+                        [&](int i) { return i < nge ? s_list[i] : c; },
+                        [&](int i) { return i < nge ? kBlock : win_len; }, scale_log2, lane, m_run, l_run, o);
+  } else {
+    // ---------------- Q worker
+    const int qj = j - nE;
+    // the window's halves first (first Q worker), while the scores arrive
+    if (qj == 0 && valid_pos && wave < 2) {
+      attend_halves<T, D>(q_group, G, unit_kv, nb, wave, 2, 2, [&](int) { return c; },
+                          [&](int) { return win_len; }, scale_log2, lane, m_run, l_run, o);
+    }
+    for (int jj = tid; jj < c; jj += kStepThreads) {
+      flag_q[jj] = 0;
+      flag_e[jj] = 0;
+      if (!cache_ok) key_e[jj] = orderable(eb[jj]);
+    }
+#pragma unroll
+    for (int i = 0; i < kScoreRegs; ++i) {
+      const int jj = tid + i * kStepThreads;
+      if (jj < c) key_q[jj] = orderable(ll_float(ll_wait(&score_ll[jj], w_sc[i], flag, kSpinLimit, err)));
+    }
+    __syncthreads();   // keys written, flags cleared
+    if (cache_ok) {
+#pragma unroll
+      for (int r = 0; r < GER; ++r) {
+        const int i = tid + r * kStepThreads;
+        const int id = (int)(uint32_t)gw[r];
+        if (i >= 1 && i <= ge_cap && id >= 0 && id < c) flag_e[id] = 1;
+      }
+    } else {
+      select_top<kStepThreads>(key_e, c, ke, flag_e, s_hist, s_small, blist, tid);
+    }
+    select_top<kStepThreads>(key_q, c, kq, flag_q, s_hist, s_small, blist, tid);
+    const int nx = write_ids<kStepThreads>([&](int jj) { return flag_q[jj] && !flag_e[jj]; }, c, s_list, kq,
+                                           s_wsum, tid);
+    __syncthreads();
+    attend_halves<T, D>(q_group, G, unit_kv, nb, qj * kStepWaves + wave, nQ * kStepWaves, 2 * nx,
+                        [&](int i) { return s_list[i]; }, [&](int) { return kBlock; }, scale_log2, lane, m_run,
+                        l_run, o);
+    if (qj == 0) {
+      // the call's selection output: Gamma_q U Gamma_e, ascending
+      const int total = write_union<kStepThreads>(flag_q, flag_e, c, sel + (size_t)unit * k_cap, k_cap, s_wsum, tid);
+      if (tid == 0) n_sel[unit] = total;
     }
   }
+
+  // ---------------- partials: publish, or (last workgroup) merge
+  auto& L = *reinterpret_cast<AttnLds<D, kStepWaves, kStepGMax>*>(lds);
+  uint64_t* recs = reinterpret_cast<uint64_t*>(ws + off_part) + (size_t)unit * W * REC;
+  typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
+  __syncthreads();   // the selection arrays in LDS are dead; L reuses the space
+  float own[PER];
+  merge_waves_keep<T, D, kStepWaves, kStepGMax>(L, m_run, l_run, o, G, tid, own, s_own_m, s_own_l);
+  if (j != W - 1) {
+    publish_part_ll<D, kStepWaves, kStepGMax>(G, tid, own, s_own_m, s_own_l, recs + (size_t)j * REC, flag);
+    return;
+  }
+  merge_parts_ll<T, D, kStepWaves, kStepGMax>(L, G, tid, W, j, own, s_own_m, s_own_l, recs, flag, kSpinLimit,
+                                              err, out_g);
+  // every workgroup of the unit has read this launch's flag: advance it
+  __syncthreads();
+  if (tid == 0) store_coherent_i(&epoch[unit], (int)(flag == 0xFFFFFFFFu ? 0u : flag));
 }
 
 template <class T, int D>
 static void launch(const LaunchStep& a) {
   const StepGeometry g = step_geometry(a.batch, a.n_q_heads, a.n_kv_heads, D, a.nb, a.kq, a.ke);
-  const int wgs = g.units * (g.S + g.n2 + g.n3);
+  const int wgs = g.units * g.W;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((step_kernel<T, D>), dim3(wgs), dim3(kStepThreads), step_lds_bytes<D>(a.nb), a.stream,
                      (const typename T::storage*)a.q, a.pos, (const typename T::storage*)a.k_comp,
                      a.e_blk, (const typename T::storage*)a.kv, a.n_q_heads, a.n_kv_heads, a.nb,
                      a.kq, a.ke, scale_log2, a.sel, a.n_sel, (typename T::storage*)a.out,
-                     (unsigned char*)a.ws, g.S, g.n2, g.n3, g.off_sel_ticket, g.off_attn_ticket,
-                     g.off_xflag, g.off_xlist, g.off_ge, g.off_score, g.off_ml, g.off_o);
+                     (unsigned char*)a.ws, g.W, g.nQ, g.off_err, g.off_ge, g.off_score, g.off_part);
 }
 
 void launch_step(const LaunchStep& a) {

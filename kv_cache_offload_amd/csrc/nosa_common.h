@@ -95,6 +95,45 @@ __device__ __forceinline__ int ticket_take(int* t) {
 __device__ __forceinline__ void ticket_reset(int* t) {
   __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_coherent_i(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Flagged words: a 32-bit payload and a 32-bit launch flag in one 8-byte
+// word, written and read with single 8-byte coherent accesses (which are
+// never torn).  A consumer polls the words themselves until they carry the
+// current launch's flag, so a hand-off costs no store wait, no ticket and
+// no separate flag load; nothing has to be reset between launches because
+// every launch uses a new flag.
+__device__ __forceinline__ void ll_store(uint64_t* p, uint32_t payload, uint32_t flag) {
+  __hip_atomic_store(p, ((uint64_t)flag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ll_store(uint64_t* p, float payload, uint32_t flag) {
+  ll_store(p, __float_as_uint(payload), flag);
+}
+__device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool ll_ok(uint64_t w, uint32_t flag) { return (uint32_t)(w >> 32) == flag; }
+__device__ __forceinline__ float ll_float(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ uint64_t ll_word(float v, uint32_t flag) {
+  return ((uint64_t)flag << 32) | __float_as_uint(v);
+}
+// Poll one flagged word (first load already issued) for at most `limit`
+// rounds; a timeout is counted in *err and the stale payload returned.
+__device__ __forceinline__ uint64_t ll_wait(const uint64_t* p, uint64_t w, uint32_t flag, int limit, int* err) {
+  int it = 0;
+  while (!ll_ok(w, flag) && it < limit) {
+    __builtin_amdgcn_s_sleep(1);
+    w = ll_load(p);
+    ++it;
+  }
+  if (!ll_ok(w, flag)) atomicAdd(err, 1);
+  return w;
+}
 
 // ---------------------------------------------------------------------------
 // KV block format: MFMA fragment order.
@@ -155,6 +194,41 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+// Wavefront-wide inclusive prefix sum (all 64 lanes active): Hillis-Steele
+// within rows of 16 lanes (row_shr 1, 2, 4, 8; lanes shifted in from outside
+// the row add 0), then the row totals added across rows.
+__device__ __forceinline__ int wave_incl_sum(int v, int lane) {
+  v += dpp_i32<0x111>(v);
+  v += dpp_i32<0x112>(v);
+  v += dpp_i32<0x114>(v);
+  v += dpp_i32<0x118>(v);
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+// Wavefront-wide min / max of uint32 (all 64 lanes active; result uniform).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)dpp_i32<0xB1>((int)v));
+  v = min(v, (uint32_t)dpp_i32<0x4E>((int)v));
+  v = min(v, (uint32_t)dpp_i32<0x141>((int)v));
+  v = min(v, (uint32_t)dpp_i32<0x140>((int)v));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i32<0xB1>((int)v));
+  v = max(v, (uint32_t)dpp_i32<0x4E>((int)v));
+  v = max(v, (uint32_t)dpp_i32<0x141>((int)v));
+  v = max(v, (uint32_t)dpp_i32<0x140>((int)v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 

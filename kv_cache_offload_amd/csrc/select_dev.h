@@ -37,11 +37,8 @@ __device__ void select_top(const uint32_t* keys, int n, int k, uint8_t* flag, in
     lo = min(lo, u);
     hi = max(hi, u);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   for (int i = tid; i < kBins; i += kHalf) hist[i] = 0;
   if (lane == 0) {
     small[2 * wv] = (int)lo;
@@ -67,12 +64,7 @@ __device__ void select_top(const uint32_t* keys, int n, int k, uint8_t* flag, in
     int cnt[4], local = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) { cnt[j] = hist[kBins - 1 - 4 * lane - j]; local += cnt[j]; }
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
+    const int incl = wave_incl_sum(local, lane);
     int run = incl - local;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -121,7 +113,7 @@ __device__ void select_top(const uint32_t* keys, int n, int k, uint8_t* flag, in
 // with NT threads; put(blk, score) receives every block score (called by
 // one lane per block).  qh: the G query heads of the KV head.
 template <class T, int D, int NT, class Put>
-__device__ __forceinline__ void scan_block_scores(const typename T::storage* qh, int G,
+__device__ __forceinline__ void scan_block_scores_fma(const typename T::storage* qh, int G,
                                                   const typename T::storage* kc_unit, int row_lo,
                                                   int row_hi, int tid, Put put) {
   constexpr int EPC = T::kPer16B;
@@ -131,7 +123,18 @@ __device__ __forceinline__ void scan_block_scores(const typename T::storage* qh,
   constexpr int ROWS_PER_ROUND = WAVES * kScanUnroll * RPW;
   const int lane = tid & 63, wave = tid >> 6;
   const int ch = lane % LPR;
-  // the query sum first: all G loads in flight at once, ahead of the key stream
+  const typename T::storage* kc = kc_unit + ch * EPC;
+  auto load_round = [&](uint4 (&raw)[kScanUnroll], int r0) {
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      const int rr = r0 + (wave * kScanUnroll + u) * RPW + lane / LPR;
+      raw[u] = (rr < row_hi) ? ld16(kc + (size_t)rr * D) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // the first round of keys and the G query rows go out together; the query
+  // sum only waits for the query loads
+  uint4 ra[kScanUnroll], rb[kScanUnroll];
+  load_round(ra, row_lo);
   float qs[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) qs[e] = 0.0f;
@@ -147,14 +150,6 @@ __device__ __forceinline__ void scan_block_scores(const typename T::storage* qh,
       for (int e = 0; e < EPC; ++e) qs[e] += v[e];
     }
   }
-  const typename T::storage* kc = kc_unit + ch * EPC;
-  auto load_round = [&](uint4 (&raw)[kScanUnroll], int r0) {
-#pragma unroll
-    for (int u = 0; u < kScanUnroll; ++u) {
-      const int rr = r0 + (wave * kScanUnroll + u) * RPW + lane / LPR;
-      raw[u] = (rr < row_hi) ? ld16(kc + (size_t)rr * D) : make_uint4(0, 0, 0, 0);
-    }
-  };
   auto score_round = [&](const uint4 (&raw)[kScanUnroll], int r0) {
     float pend = 0.0f;  // first half of a block when a row spans 32 lanes
 #pragma unroll
@@ -190,14 +185,86 @@ __device__ __forceinline__ void scan_block_scores(const typename T::storage* qh,
     }
   };
   // two rounds of loads in flight: round i+1 streams in while round i is scored
-  uint4 ra[kScanUnroll], rb[kScanUnroll];
-  load_round(ra, row_lo);
   for (int r0 = row_lo; r0 < row_hi; r0 += 2 * ROWS_PER_ROUND) {
     load_round(rb, r0 + ROWS_PER_ROUND);
     score_round(ra, r0);
+    if (r0 + ROWS_PER_ROUND >= row_hi) break;
     load_round(ra, r0 + 2 * ROWS_PER_ROUND);
     score_round(rb, r0 + ROWS_PER_ROUND);
   }
+}
+
+// bf16 scan on MFMA: a 16-row tile of compressed keys times the G query
+// heads (16x16x32 products, rows in the A operand, heads in B, fp32
+// accumulation), then the per-row sum over the heads (DPP within each
+// 16-lane row) and the maximum over the four rows of a block, which the
+// accumulator layout puts in one lane group.  Each head's dot product is
+// exact-product fp32 accumulation; the head sum is a fixed tree.
+template <int D, int NT, class Put>
+__device__ __forceinline__ void scan_block_scores_mfma(const uint16_t* qh, int G, const uint16_t* kc_unit,
+                                                       int row_lo, int row_hi, int tid, Put put) {
+  constexpr int NK = D / 32;      // k-steps of 32 dims
+  constexpr int WAVES = NT / 64;
+  constexpr int TPR = 2;          // tiles per wavefront per round
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int n_tiles = (row_hi - row_lo + 15) / 16;
+  auto load_round = [&](uint4 (&raw)[TPR][NK], int round) {
+#pragma unroll
+    for (int t = 0; t < TPR; ++t) {
+      const int tile = (round * TPR + t) * WAVES + wave;
+      const int row = row_lo + 16 * tile + col;
+#pragma unroll
+      for (int s = 0; s < NK; ++s)
+        raw[t][s] = (tile < n_tiles && row < row_hi) ? ld16(kc_unit + (size_t)row * D + 32 * s + 8 * grp)
+                                                     : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 ra[TPR][NK], rb[TPR][NK];
+  load_round(ra, 0);
+  bf16x8 qf[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    const uint4 u = col < G ? ld16(qh + (size_t)col * D + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0);
+    qf[s] = __builtin_bit_cast(bf16x8, u);
+  }
+  auto score_round = [&](const uint4 (&raw)[TPR][NK], int round) {
+#pragma unroll
+    for (int t = 0; t < TPR; ++t) {
+      const int tile = (round * TPR + t) * WAVES + wave;
+      if (tile >= n_tiles) continue;   // wavefront-uniform
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NK; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, raw[t][s]), qf[s], acc, 0, 0, 0);
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, group_sum<16>(acc[i]));
+      const int row0 = row_lo + 16 * tile + 4 * grp;   // first row of this lane group's block
+      if (col == 0 && row0 < row_hi) put(row0 / kSubsPerBlock, m);
+    }
+  };
+  const int n_rounds = (n_tiles + TPR * WAVES - 1) / (TPR * WAVES);
+  for (int r = 0; r < n_rounds; r += 2) {
+    if (r + 1 < n_rounds) load_round(rb, r + 1);
+    score_round(ra, r);
+    if (r + 1 >= n_rounds) break;
+    if (r + 2 < n_rounds) load_round(ra, r + 2);
+    score_round(rb, r + 1);
+  }
+}
+
+// Block scores of compressed-key rows [row_lo, row_hi) (whole blocks) of one
+// KV head with NT threads: put(blk, score) receives every block score (one
+// lane per block).  bf16 keys use the MFMA scan, fp32 keys the FMA scan.
+template <class T, int D, int NT, class Put>
+__device__ __forceinline__ void scan_block_scores(const typename T::storage* qh, int G,
+                                                  const typename T::storage* kc_unit, int row_lo,
+                                                  int row_hi, int tid, Put put) {
+  if constexpr (sizeof(typename T::storage) == 2)
+    scan_block_scores_mfma<D, NT>(qh, G, kc_unit, row_lo, row_hi, tid, put);
+  else
+    scan_block_scores_fma<T, D, NT>(qh, G, kc_unit, row_lo, row_hi, tid, put);
 }
 
 // Write the ids j in [0, c) with pick(j) in ascending order to out[0 ..
@@ -210,12 +277,7 @@ __device__ int write_ids(Pick pick, int c, int32_t* out, int k_cap, int* wsum, i
   const int lo = tid * per, hi = min(c, lo + per);
   int cnt = 0;
   for (int j = lo; j < hi; ++j) cnt += pick(j) ? 1 : 0;
-  int incl = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_incl_sum(cnt, lane);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int off = incl - cnt, total = 0;

@@ -177,6 +177,15 @@ class DecodeLayer:
         nb.decode_step(self.dims, q, pos, self.k_comp, self.e_blk, self.kq, self.ke, kv, self.scale,
                        self.sel, self.n_sel, self.out, self.ws_step, stream=stream)
 
+    def step_timeouts(self) -> int:
+        """Waits of the one-launch step that hit their bound so far (0 when
+        every hand-off completed); reads the workspace counter (synchronises)."""
+        if self.ws_step is None:
+            return 0
+        units = self.dims.batch * self.dims.n_kv_heads
+        off = (units * 4 + 255) // 256 * 256
+        return int(self.ws_step[off:off + 4].view(torch.int32).item())
+
     def step_offload(self, q, host_kv, window, pos, step: int, insert_block=None, insert_src=None,
                      side: Optional[torch.cuda.Stream] = None) -> None:
         """select -> fetch on the side stream -> attention, ordered with events."""

@@ -331,7 +331,8 @@ def test_fused_step_matches_oracle(wname, over):
     _banner(f"fused step {wname} {over}")
     w = NI.scaled(NI.WORKLOADS[wname], **over) if over else NI.WORKLOADS[wname]
     K, V, lam, q = NI.layer_inputs(w)
-    s1, n1, o1, _ = H.run_resident(w, K, V, lam, q, fused=True)
+    s1, n1, o1, layer = H.run_resident(w, K, V, lam, q, fused=True)
+    assert layer.step_timeouts() == 0
     s2, n2, o2, _ = H.run_resident(w, K, V, lam, q, fused=False)
     for a, b in zip(n1, n2):
         assert np.array_equal(a, b)
@@ -346,7 +347,8 @@ def test_fused_step_layer32k_full():
     _banner("fused step on the full layer32k workload")
     w = NI.WORKLOADS["layer32k"]
     K, V, lam, q = NI.layer_inputs(w)
-    s1, n1, o1, _ = H.run_resident(w, K, V, lam, q, fused=True)
+    s1, n1, o1, layer = H.run_resident(w, K, V, lam, q, fused=True)
+    assert layer.step_timeouts() == 0
     for b in range(w.batch):
         for h in range(w.n_kv_heads):
             H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
