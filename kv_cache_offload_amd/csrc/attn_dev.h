@@ -270,194 +270,180 @@ __device__ __forceinline__ void combine_partial(float& m_run, float& l_run, f32x
   m_run = M;
 }
 
-// Workgroup: merge the wavefront partials through LDS and keep the result
-// on chip: own[r] (numerator of output tid + r*NT, head-major) in registers,
-// the heads' maxima and sums in own_m / own_l (LDS).  Every thread reads all
-// the wavefront values it needs in one batch.
-template <class T, int D, int WAVES, int GMAX>
-__device__ void merge_waves_keep(AttnLds<D, WAVES, GMAX>& L, float m_run, float l_run,
-                                 const f32x4 (&o)[D / 16], int G, int tid,
-                                 float (&own)[(GMAX * D + 64 * WAVES - 1) / (64 * WAVES)],
-                                 float* own_m, float* own_l) {
+// ---- merging across the wavefronts and workgroups of one (b, h) unit
+// (one-launch step).  A partial is (unnormalised numerators of the G x D
+// outputs, per-head max in log2 units, per-head sum).  Thread tid owns the
+// output pair 2*tid, 2*tid+1 (head-major); the per-head weights of the
+// pieces are computed once, by one lane group per head.
+
+// Maximum over aligned groups of N lanes (N = 8 or 16), every lane of the
+// group ends with it.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+
+template <int D, int WAVES, int GMAX>
+struct MergeLds {
+  float o[WAVES][GMAX][D + 4];
+  float m[WAVES][GMAX];
+  float l[WAVES][GMAX];
+  float a[GMAX][16];      // weights of the pieces (wavefronts or records) per head
+  float M[GMAX], den[GMAX];
+};
+
+// Words of one flagged partial record: GMAX*D numerators (head-major), then
+// (max, sum) of each head.
+template <int D, int GMAX>
+constexpr int part_record_words() { return GMAX * D + 2 * GMAX; }
+
+// Workgroup: the WAVES wavefront partials (m_run = -inf for an idle
+// wavefront) -> one partial kept on chip: own[e] = numerator of output
+// 2*tid + e, L.M / L.den the heads' max and sum.
+template <int D, int WAVES, int GMAX>
+__device__ void merge_waves_keep(MergeLds<D, WAVES, GMAX>& L, float m_run, float l_run,
+                                 const f32x4 (&o)[D / 16], int G, int tid, float (&own)[2]) {
+  static_assert(WAVES == 8, "one 8-lane group per head");
+  static_assert(GMAX * D <= 2 * 64 * WAVES, "an output pair per thread");
   const int lane = tid & 63, wave = tid >> 6, col = lane & 15, grp = lane >> 4;
-  constexpr int NT = 64 * WAVES;
-  constexpr int PER = (GMAX * D + NT - 1) / NT;
   if (col < G) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) L.o[wave][col][16 * dt + 4 * grp + i] = o[dt][i];
+      *reinterpret_cast<float4*>(&L.o[wave][col][16 * dt + 4 * grp]) =
+          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
     if (grp == 0) {
       L.m[wave][col] = m_run;
       L.l[wave][col] = l_run;
     }
   }
   __syncthreads();
-  float mw[PER][WAVES], lw[PER][WAVES], ow[PER][WAVES];
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int idx = min(tid + r * NT, G * D - 1);
-    const int g = idx / D, d = idx % D;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      mw[r][w] = L.m[w][g];
-      lw[r][w] = L.l[w][g];
-      ow[r][w] = L.o[w][g][d];
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int idx = tid + r * NT;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[r][w]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      const float wt = (mw[r][w] == -INFINITY) ? 0.f : exp2f(mw[r][w] - M);
-      num += wt * ow[r][w];
-      den += wt * lw[r][w];
-    }
-    own[r] = idx < G * D ? num : 0.f;
-    if (idx < G * D && idx % D == 0) {
-      own_m[idx / D] = M;
-      own_l[idx / D] = den;
+  if (tid < 8 * GMAX) {
+    // lane group of 8 = one head, lane = wavefront
+    const int g = tid >> 3, w = tid & 7;
+    const float mw = g < G ? L.m[w][g] : -INFINITY;
+    const float lw = g < G ? L.l[w][g] : 0.f;
+    const float M = group_max<8>(mw);
+    const float a = mw == -INFINITY ? 0.f : exp2f(mw - M);
+    const float den = group_sum<8>(a * lw);
+    L.a[g][w] = a;
+    if (w == 0) {
+      L.M[g] = M;
+      L.den[g] = den;
     }
   }
   __syncthreads();
+  own[0] = own[1] = 0.f;
+  if (2 * tid < G * D) {
+    const int idx = 2 * tid, g = idx / D, d = idx % D;
+    float n0 = 0.f, n1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float a = L.a[g][w];
+      const float2 v = *reinterpret_cast<const float2*>(&L.o[w][g][d]);
+      n0 = fmaf(a, v.x, n0);
+      n1 = fmaf(a, v.y, n1);
+    }
+    own[0] = n0;
+    own[1] = n1;
+  }
 }
 
-// Words of one flagged partial record: GMAX*D numerators (head-major),
-// GMAX maxima, GMAX sums.
-template <int D, int GMAX>
-constexpr int part_record_words() { return GMAX * D + 2 * GMAX; }
-
-// Publish a workgroup's merged partial (from merge_waves_keep) as flagged
-// words; no wait: the merging workgroup polls the words themselves.
+// Publish a workgroup's partial (from merge_waves_keep) as flagged words;
+// no wait: the merging workgroup polls the words themselves.
 template <int D, int WAVES, int GMAX>
-__device__ void publish_part_ll(int G, int tid, const float (&own)[(GMAX * D + 64 * WAVES - 1) / (64 * WAVES)],
-                                const float* own_m, const float* own_l, uint64_t* rec, uint32_t flag) {
-  constexpr int NT = 64 * WAVES;
-  constexpr int PER = (GMAX * D + NT - 1) / NT;
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int idx = tid + r * NT;
-    if (idx < G * D) ll_store(&rec[idx], own[r], flag);
+__device__ void publish_part_ll(const MergeLds<D, WAVES, GMAX>& L, int G, int tid, const float (&own)[2],
+                                uint64_t* rec, uint32_t flag) {
+  if (2 * tid < G * D) {
+    ll_store(&rec[2 * tid], own[0], flag);
+    ll_store(&rec[2 * tid + 1], own[1], flag);
   }
   if (tid < G) {
-    ll_store(&rec[GMAX * D + tid], own_m[tid], flag);
-    ll_store(&rec[GMAX * D + GMAX + tid], own_l[tid], flag);
+    ll_store(&rec[GMAX * D + 2 * tid], L.M[tid], flag);
+    ll_store(&rec[GMAX * D + 2 * tid + 1], L.den[tid], flag);
   }
 }
 
-// The merging workgroup of a (b, h): combine its own partial (own, own_m,
-// own_l from merge_waves_keep, part own_part) with the other n_part - 1,
-// polled as flagged records (record s at recs + s * part_record_words), then
-// normalise and store.  All numerator words are requested at once (up to
-// kRegParts parts in registers; beyond that each word is polled in turn),
-// the maxima and sums go through LDS with one barrier.
-template <class T, int D, int WAVES, int GMAX>
-__device__ void merge_parts_ll(AttnLds<D, WAVES, GMAX>& L, int G, int tid, int n_part, int own_part,
-                               const float (&own)[(GMAX * D + 64 * WAVES - 1) / (64 * WAVES)],
-                               const float* own_m, const float* own_l, const uint64_t* recs,
-                               uint32_t flag, int spin_limit, int* err, typename T::storage* out_g) {
-  constexpr int NT = 64 * WAVES;
-  constexpr int PER = (GMAX * D + NT - 1) / NT;
+// The merging workgroup of a unit: its own partial (own, L.M, L.den; part
+// own_part) and the other n_part - 1 records (record s at recs + s *
+// part_record_words, polled until they carry `flag`), normalised and stored.
+// All numerator words are requested at once; the per-head weights come from
+// one 16-lane group per head (lane = part).
+template <class T, int D, int WAVES, int GMAX, int MAXP>
+__device__ void merge_parts_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int n_part, int own_part,
+                               const float (&own)[2], const uint64_t* recs, uint32_t flag, int spin_limit,
+                               int* err, typename T::storage* out_g) {
   constexpr int REC = part_record_words<D, GMAX>();
-  constexpr int kRegParts = 16;
-  float* fm = &L.o[0][0][0];   // [n_part][G] maxima, then [n_part][G] sums
-  float* fl = fm + n_part * G;
-  const bool in_regs = n_part <= kRegParts;
-  uint64_t w[PER][kRegParts];
-  if (in_regs) {
+  static_assert(MAXP <= 16, "one 16-lane group per head");
+  __syncthreads();   // merge_waves_keep's reads of L.a are done
+  const bool mine = 2 * tid < G * D;
+  const int idx = 2 * tid;
+  const uint64_t* base = recs + idx;
+  uint64_t w0[MAXP], w1[MAXP];
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int idx = tid + r * NT;
-#pragma unroll
-      for (int sp = 0; sp < kRegParts; ++sp) {
-        const bool need = idx < G * D && sp < n_part && sp != own_part;
-        w[r][sp] = need ? ll_load(&recs[(size_t)sp * REC + idx])
-                        : ll_word(sp == own_part ? own[r] : 0.f, flag);
+  for (int sp = 0; sp < MAXP; ++sp) {
+    if (sp < n_part && sp != own_part && mine) {
+      w0[sp] = ll_load(base + (size_t)sp * REC);
+      w1[sp] = ll_load(base + (size_t)sp * REC + 1);
+    } else {
+      w0[sp] = w1[sp] = ll_word(0.f, flag);
+    }
+  }
+  if (tid < 16 * GMAX) {
+    const int g = tid >> 4, sp = tid & 15;
+    float m = -INFINITY, l = 0.f;
+    if (g < G && sp < n_part) {
+      if (sp == own_part) {
+        m = L.M[g];
+        l = L.den[g];
+      } else {
+        const uint64_t* pm = recs + (size_t)sp * REC + GMAX * D + 2 * g;
+        uint64_t wm = ll_load(pm), wl = ll_load(pm + 1);
+        wm = ll_wait(pm, wm, flag, spin_limit, err);
+        wl = ll_wait(pm + 1, wl, flag, spin_limit, err);
+        m = ll_float(wm);
+        l = ll_float(wl);
       }
     }
+    const float M = group_max<16>(m);
+    const float a = m == -INFINITY ? 0.f : exp2f(m - M);
+    const float den = group_sum<16>(a * l);
+    L.a[g][sp] = den > 0.f ? a / den : 0.f;
   }
-  // maxima and sums: one word per thread
-  for (int i = tid; i < 2 * n_part * G; i += NT) {
-    const int which = i / (n_part * G), j = i % (n_part * G);   // 0: max, 1: sum
-    const int sp = j / G, g = j % G;
-    float v;
-    if (sp == own_part) {
-      v = which ? own_l[g] : own_m[g];
-    } else {
-      const uint64_t* pw = &recs[(size_t)sp * REC + GMAX * D + which * GMAX + g];
-      v = ll_float(ll_wait(pw, ll_load(pw), flag, spin_limit, err));
-    }
-    fm[i] = v;
-  }
-  if (in_regs) {
+  {
     int it = 0;
-    bool ok = false;
     while (true) {
-      ok = true;
+      bool ok = true;
 #pragma unroll
-      for (int r = 0; r < PER; ++r)
-#pragma unroll
-        for (int sp = 0; sp < kRegParts; ++sp) ok = ok && ll_ok(w[r][sp], flag);
-      if (ok || it >= spin_limit) break;
+      for (int sp = 0; sp < MAXP; ++sp) ok = ok && ll_ok(w0[sp], flag) && ll_ok(w1[sp], flag);
+      if (ok || it >= spin_limit) {
+        if (!ok) atomicAdd(err, 1);
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        const int idx = tid + r * NT;
-#pragma unroll
-        for (int sp = 0; sp < kRegParts; ++sp)
-          if (!ll_ok(w[r][sp], flag)) w[r][sp] = ll_load(&recs[(size_t)sp * REC + idx]);
+      for (int sp = 0; sp < MAXP; ++sp) {
+        if (!ll_ok(w0[sp], flag)) w0[sp] = ll_load(base + (size_t)sp * REC);
+        if (!ll_ok(w1[sp], flag)) w1[sp] = ll_load(base + (size_t)sp * REC + 1);
       }
       ++it;
     }
-    if (!ok) atomicAdd(err, 1);
   }
   __syncthreads();
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int idx = tid + r * NT;
-    if (idx >= G * D) break;
+  if (mine) {
     const int g = idx / D;
-    float num = 0.f, den = 0.f;
-    if (in_regs) {
-      // every part at a fixed register: all reads issued together
-      float mv[kRegParts], lv[kRegParts];
+    float n0 = 0.f, n1 = 0.f;
 #pragma unroll
-      for (int sp = 0; sp < kRegParts; ++sp) {
-        mv[sp] = sp < n_part ? fm[sp * G + g] : -INFINITY;
-        lv[sp] = sp < n_part ? fl[sp * G + g] : 0.f;
-      }
-      float M = -INFINITY;
-#pragma unroll
-      for (int sp = 0; sp < kRegParts; ++sp) M = fmaxf(M, mv[sp]);
-#pragma unroll
-      for (int sp = 0; sp < kRegParts; ++sp) {
-        const float wt = (mv[sp] == -INFINITY) ? 0.f : exp2f(mv[sp] - M);
-        den += wt * lv[sp];
-        num += wt * ll_float(w[r][sp]);
-      }
-    } else {
-      float M = -INFINITY;
-      for (int sp = 0; sp < n_part; ++sp) M = fmaxf(M, fm[sp * G + g]);
-      for (int sp = 0; sp < n_part; ++sp) {
-        const float ms = fm[sp * G + g];
-        const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        den += wt * fl[sp * G + g];
-        float v;
-        if (sp == own_part) {
-          v = own[r];
-        } else {
-          const uint64_t* pw = &recs[(size_t)sp * REC + idx];
-          v = ll_float(ll_wait(pw, ll_load(pw), flag, spin_limit, err));
-        }
-        num += wt * v;
-      }
+    for (int sp = 0; sp < MAXP; ++sp) {
+      const float a = L.a[g][sp];
+      n0 = fmaf(a, sp == own_part ? own[0] : ll_float(w0[sp]), n0);
+      n1 = fmaf(a, sp == own_part ? own[1] : ll_float(w1[sp]), n1);
     }
-    store_out(&out_g[idx], den > 0.f ? num / den : 0.f);
+    store_out(&out_g[idx], n0);
+    store_out(&out_g[idx + 1], n1);
   }
 }
 

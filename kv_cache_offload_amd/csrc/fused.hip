@@ -84,7 +84,7 @@ size_t step_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int
 
 template <int D>
 static size_t step_lds_bytes(int nb) {
-  const size_t a = sizeof(AttnLds<D, kStepWaves, kStepGMax>);
+  const size_t a = sizeof(MergeLds<D, kStepWaves, kStepGMax>);
   const size_t s = select_lds_bytes(nb);
   return a > s ? a : s;
 }
@@ -118,7 +118,6 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     typename T::storage* __restrict__ out, unsigned char* __restrict__ ws, int W, int nQ,
     size_t off_err, size_t off_ge, size_t off_score, size_t off_part) {
   constexpr int ND = D / 16;
-  constexpr int PER = (kStepGMax * D + kStepThreads - 1) / kStepThreads;
   constexpr int REC = part_record_words<D, kStepGMax>();
   constexpr int GER = (kStepMaxK + 1 + kStepThreads - 1) / kStepThreads;   // cache words per thread
   const int G = n_q_heads / n_kv_heads;
@@ -145,7 +144,6 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   __shared__ int s_small[32];
   __shared__ int s_wsum[kStepWaves];
   __shared__ int s_list[kStepMaxK];
-  __shared__ float s_own_m[kStepGMax], s_own_l[kStepGMax];
   const size_t kb = align256((size_t)nb * 4), lb = align256((size_t)nb * 2);
   uint32_t* key_q = reinterpret_cast<uint32_t*>(lds);
   uint32_t* key_e = reinterpret_cast<uint32_t*>(lds + kb);
@@ -298,18 +296,17 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   }
 
   // ---------------- partials: publish, or (last workgroup) merge
-  auto& L = *reinterpret_cast<AttnLds<D, kStepWaves, kStepGMax>*>(lds);
+  auto& L = *reinterpret_cast<MergeLds<D, kStepWaves, kStepGMax>*>(lds);
   uint64_t* recs = reinterpret_cast<uint64_t*>(ws + off_part) + (size_t)unit * W * REC;
   typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
   __syncthreads();   // the selection arrays in LDS are dead; L reuses the space
-  float own[PER];
-  merge_waves_keep<T, D, kStepWaves, kStepGMax>(L, m_run, l_run, o, G, tid, own, s_own_m, s_own_l);
+  float own[2];
+  merge_waves_keep<D, kStepWaves, kStepGMax>(L, m_run, l_run, o, G, tid, own);
   if (j != W - 1) {
-    publish_part_ll<D, kStepWaves, kStepGMax>(G, tid, own, s_own_m, s_own_l, recs + (size_t)j * REC, flag);
+    publish_part_ll<D, kStepWaves, kStepGMax>(L, G, tid, own, recs + (size_t)j * REC, flag);
     return;
   }
-  merge_parts_ll<T, D, kStepWaves, kStepGMax>(L, G, tid, W, j, own, s_own_m, s_own_l, recs, flag, kSpinLimit,
-                                              err, out_g);
+  merge_parts_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, j, own, recs, flag, kSpinLimit, err, out_g);
   // every workgroup of the unit has read this launch's flag: advance it
   __syncthreads();
   if (tid == 0) store_coherent_i(&epoch[unit], (int)(flag == 0xFFFFFFFFu ? 0u : flag));
