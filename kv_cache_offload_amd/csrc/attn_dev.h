@@ -146,17 +146,13 @@ __device__ __forceinline__ void block_pv(const Frags<T, D>& f, const float (&p)[
 }
 
 // One wavefront: the unnormalised attention partial of tiles t0 .. t0+NTL-1
-// of one block, whose first `len` tokens are valid.  m, l are per head (lane
-// column), o holds O^T[d = 16*dt + 4*(lane/16) + i][head = lane%16].
+// of one block whose operands are in f (load_tiles + load_q), the first
+// `len` tokens valid.  m, l are per head (lane column), o holds
+// O^T[d = 16*dt + 4*(lane/16) + i][head = lane%16].
 template <class T, int D, int NTL>
-__device__ __forceinline__ void attend_tiles(const typename T::storage* q_group, int G,
-                                             const typename T::storage* blk, int t0, int len,
-                                             float scale_log2, int lane, float& m_out,
-                                             float& l_out, f32x4 (&o)[D / 16]) {
+__device__ __forceinline__ void attend_frags(const Frags<T, D>& f, int t0, int len, float scale_log2, int lane,
+                                             float& m_out, float& l_out, f32x4 (&o)[D / 16]) {
   const int grp = lane >> 4;
-  Frags<T, D> f;
-  load_tiles<T, D, NTL>(f, blk, t0, lane);
-  load_q<T, D>(f, q_group, G, lane);
   f32x4 acc[4];
   block_scores<T, D, NTL>(f, acc);
   float x[4][4];
@@ -171,12 +167,14 @@ __device__ __forceinline__ void attend_tiles(const typename T::storage* q_group,
     }
   mb = fmaxf(mb, __shfl_xor(mb, 16));
   mb = fmaxf(mb, __shfl_xor(mb, 32));
+  // every token masked (the empty half of a short window): an empty partial
+  const float mref = mb == -INFINITY ? 0.f : mb;
   float pw[4][4], lb = 0.f;
 #pragma unroll
   for (int t = 0; t < NTL; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pw[t][i] = exp2f(x[t][i] - mb);
+      pw[t][i] = exp2f(x[t][i] - mref);
       lb += pw[t][i];
     }
   lb += __shfl_xor(lb, 16);
@@ -186,6 +184,17 @@ __device__ __forceinline__ void attend_tiles(const typename T::storage* q_group,
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   block_pv<T, D, NTL>(f, pw, o);
+}
+
+template <class T, int D, int NTL>
+__device__ __forceinline__ void attend_tiles(const typename T::storage* q_group, int G,
+                                             const typename T::storage* blk, int t0, int len,
+                                             float scale_log2, int lane, float& m_out,
+                                             float& l_out, f32x4 (&o)[D / 16]) {
+  Frags<T, D> f;
+  load_tiles<T, D, NTL>(f, blk, t0, lane);
+  load_q<T, D>(f, q_group, G, lane);
+  attend_frags<T, D, NTL>(f, t0, len, scale_log2, lane, m_out, l_out, o);
 }
 
 // A whole block (tiles 0..3).

@@ -260,17 +260,35 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
       attend_halves<T, D>(q_group, G, unit_kv, nb, wave, 2, 2, [&](int) { return c; },
                           [&](int) { return win_len; }, scale_log2, lane, m_run, l_run, o);
     }
+    uint8_t* bin_q = flag_q;   // per-candidate value bin of the query-aware score
     for (int jj = tid; jj < c; jj += kStepThreads) {
-      flag_q[jj] = 0;
       flag_e[jj] = 0;
       if (!cache_ok) key_e[jj] = orderable(eb[jj]);
     }
+    if (!cache_ok) {
+      __syncthreads();
+      select_top<kStepThreads>(key_e, c, ke, flag_e, s_hist, s_small, blist, tid);
+    }
+    // the scores (polled) with their range
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int i = 0; i < kScoreRegs; ++i) {
       const int jj = tid + i * kStepThreads;
-      if (jj < c) key_q[jj] = orderable(ll_float(ll_wait(&score_ll[jj], w_sc[i], flag, kSpinLimit, err)));
+      if (jj < c) {
+        const uint32_t k = orderable(ll_float(ll_wait(&score_ll[jj], w_sc[i], flag, kSpinLimit, err)));
+        key_q[jj] = k;
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+      }
     }
-    __syncthreads();   // keys written, flags cleared
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+      s_small[2 * wave] = (int)kmin;
+      s_small[2 * wave + 1] = (int)kmax;
+    }
+    for (int i = tid; i < kBins; i += kStepThreads) s_hist[i] = 0;
+    if (tid == 0) s_small[20] = 0;
     if (cache_ok) {
 #pragma unroll
       for (int r = 0; r < GER; ++r) {
@@ -278,21 +296,116 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
         const int id = (int)(uint32_t)gw[r];
         if (i >= 1 && i <= ge_cap && id >= 0 && id < c) flag_e[id] = 1;
       }
-    } else {
-      select_top<kStepThreads>(key_e, c, ke, flag_e, s_hist, s_small, blist, tid);
     }
-    select_top<kStepThreads>(key_q, c, kq, flag_q, s_hist, s_small, blist, tid);
-    const int nx = write_ids<kStepThreads>([&](int jj) { return flag_q[jj] && !flag_e[jj]; }, c, s_list, kq,
-                                           s_wsum, tid);
+    __syncthreads();   // keys, ranges, flags
+    // Gamma_q = the kq best of c (score desc, id asc): value bins between the
+    // scores' min and max (fp64, monotone in the score), the bin holding the
+    // kq-th best, and an exact rank inside that bin only
+    const bool all_q = kq >= c, none_q = kq <= 0 || c <= 0;
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int w = 0; w < kStepWaves; ++w) {
+      lo = min(lo, (uint32_t)s_small[2 * w]);
+      hi = max(hi, (uint32_t)s_small[2 * w + 1]);
+    }
+    const double vlo = key_value(lo), vhi = key_value(hi);
+    const double bscale = vhi > vlo ? (double)kBins / (vhi - vlo) : 0.0;
+    if (!all_q && !none_q) {
+      for (int jj = tid; jj < c; jj += kStepThreads) {
+        const int bi = min(kBins - 1, (int)(((double)key_value(key_q[jj]) - vlo) * bscale));
+        bin_q[jj] = (uint8_t)bi;
+        atomicAdd(&s_hist[bi], 1);
+      }
+    }
+    __syncthreads();
+    if (!all_q && !none_q && wave == 0) {
+      // lane owns bins 255-4*lane .. 252-4*lane (descending)
+      int cnt[4], local = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        cnt[t] = s_hist[kBins - 1 - 4 * lane - t];
+        local += cnt[t];
+      }
+      const int incl = wave_incl_sum(local, lane);
+      int run = incl - local;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (run < kq && run + cnt[t] >= kq) {
+          s_small[16] = kBins - 1 - 4 * lane - t;   // the bin holding the kq-th best
+          s_small[18] = kq - run;                   // how many of that bin to take
+        }
+        run += cnt[t];
+      }
+    }
+    __syncthreads();
+    const int bstar = (all_q || none_q) ? 0 : s_small[16];
+    const int take = (all_q || none_q) ? 0 : s_small[18];
+    if (!all_q && !none_q)
+      for (int jj = tid; jj < c; jj += kStepThreads)
+        if (bin_q[jj] == bstar) blist[atomicAdd(&s_small[20], 1)] = (uint16_t)jj;
+    __syncthreads();
+    const int n_tie = s_small[20];
+    auto in_q = [&](int jj) -> bool {
+      if (all_q) return true;
+      if (none_q) return false;
+      const int bi = bin_q[jj];
+      if (bi != bstar) return bi > bstar;
+      if (n_tie <= take) return true;
+      const uint32_t kj = key_q[jj];
+      int rank = 0;
+      for (int t = 0; t < n_tie; ++t) {
+        const int o2 = blist[t];
+        const uint32_t ko = key_q[o2];
+        rank += (ko > kj) || (ko == kj && o2 < jj);
+      }
+      return rank < take;
+    };
+    // X = Gamma_q \ Gamma_e (into LDS) and, from the first Q worker, the union
+    // (the call's selection output), both ascending, from one pass over each
+    // thread's run of at most kScoreRegs candidates
+    int nx;
+    {
+      const int per = (c + kStepThreads - 1) / kStepThreads;
+      const int lo_id = min(c, tid * per), hi_id = min(c, lo_id + per);
+      uint32_t mq = 0u, me = 0u;
+      for (int jj = lo_id; jj < hi_id; ++jj) {
+        if (in_q(jj)) mq |= 1u << (jj - lo_id);
+        if (flag_e[jj]) me |= 1u << (jj - lo_id);
+      }
+      const uint32_t mx = mq & ~me, mu = mq | me;
+      const int cx = __builtin_popcount(mx), cu = __builtin_popcount(mu);
+      const int ix = wave_incl_sum(cx, lane), iu = wave_incl_sum(cu, lane);
+      if (lane == 63) {
+        s_wsum[wave] = ix;
+        s_small[24 + wave] = iu;
+      }
+      __syncthreads();
+      int ox = ix - cx, ou = iu - cu, tx = 0, tu = 0;
+#pragma unroll
+      for (int w = 0; w < kStepWaves; ++w) {
+        if (w < wave) {
+          ox += s_wsum[w];
+          ou += s_small[24 + w];
+        }
+        tx += s_wsum[w];
+        tu += s_small[24 + w];
+      }
+      for (int jj = lo_id; jj < hi_id; ++jj) {
+        if (mx & (1u << (jj - lo_id))) s_list[ox++] = jj;
+      }
+      if (qj == 0) {
+        int32_t* su = sel + (size_t)unit * k_cap;
+        for (int jj = lo_id; jj < hi_id; ++jj)
+          if (mu & (1u << (jj - lo_id))) su[ou++] = jj;
+        for (int i = tu + tid; i < k_cap; i += kStepThreads) su[i] = -1;
+        if (tid == 0) n_sel[unit] = tu;
+      }
+      nx = min(tx, kq);
+    }
     __syncthreads();
     attend_halves<T, D>(q_group, G, unit_kv, nb, qj * kStepWaves + wave, nQ * kStepWaves, 2 * nx,
                         [&](int i) { return s_list[i]; }, [&](int) { return kBlock; }, scale_log2, lane, m_run,
                         l_run, o);
-    if (qj == 0) {
-      // the call's selection output: Gamma_q U Gamma_e, ascending
-      const int total = write_union<kStepThreads>(flag_q, flag_e, c, sel + (size_t)unit * k_cap, k_cap, s_wsum, tid);
-      if (tid == 0) n_sel[unit] = total;
-    }
   }
 
   // ---------------- partials: publish, or (last workgroup) merge

@@ -200,35 +200,47 @@ __device__ __forceinline__ void scan_block_scores_fma(const typename T::storage*
 // 16-lane row) and the maximum over the four rows of a block, which the
 // accumulator layout puts in one lane group.  Each head's dot product is
 // exact-product fp32 accumulation; the head sum is a fixed tree.
-template <int D, int NT, class Put>
-__device__ __forceinline__ void scan_block_scores_mfma(const uint16_t* qh, int G, const uint16_t* kc_unit,
-                                                       int row_lo, int row_hi, int tid, Put put) {
-  constexpr int NK = D / 32;      // k-steps of 32 dims
-  constexpr int WAVES = NT / 64;
-  constexpr int TPR = 2;          // tiles per wavefront per round
-  const int lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int n_tiles = (row_hi - row_lo + 15) / 16;
-  auto load_round = [&](uint4 (&raw)[TPR][NK], int round) {
+// The constructor issues the first round of loads (every load unconditional,
+// rows clamped into the range, so a caller can issue more loads behind them
+// and the compiler still waits for exactly these); finish() scores them and
+// any further rounds.  Requires row_lo < row_hi.
+template <int D, int NT>
+struct MfmaScan {
+  static constexpr int NK = D / 32;      // k-steps of 32 dims
+  static constexpr int WAVES = NT / 64;
+  static constexpr int TPR = 2;          // tiles per wavefront per round
+  const uint16_t* kc;
+  int row_lo, row_hi, n_tiles, n_rounds, wave, col, grp;
+  uint4 ra[TPR][NK];
+  bf16x8 qf[NK];
+
+  __device__ __forceinline__ MfmaScan(const uint16_t* qh, int G, const uint16_t* kc_unit, int row_lo_, int row_hi_,
+                                      int tid)
+      : kc(kc_unit), row_lo(row_lo_), row_hi(row_hi_) {
+    const int lane = tid & 63;
+    wave = tid >> 6;
+    col = lane & 15;
+    grp = lane >> 4;
+    n_tiles = (row_hi - row_lo + 15) / 16;
+    n_rounds = (n_tiles + TPR * WAVES - 1) / (TPR * WAVES);
+    load(ra, 0);
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const uint4 u = col < G ? ld16(qh + (size_t)col * D + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0);
+      qf[s] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  __device__ __forceinline__ void load(uint4 (&raw)[TPR][NK], int round) const {
 #pragma unroll
     for (int t = 0; t < TPR; ++t) {
       const int tile = (round * TPR + t) * WAVES + wave;
-      const int row = row_lo + 16 * tile + col;
+      const int row = min(row_lo + 16 * tile + col, row_hi - 1);
 #pragma unroll
-      for (int s = 0; s < NK; ++s)
-        raw[t][s] = (tile < n_tiles && row < row_hi) ? ld16(kc_unit + (size_t)row * D + 32 * s + 8 * grp)
-                                                     : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < NK; ++s) raw[t][s] = ld16(kc + (size_t)row * D + 32 * s + 8 * grp);
     }
-  };
-  uint4 ra[TPR][NK], rb[TPR][NK];
-  load_round(ra, 0);
-  bf16x8 qf[NK];
-#pragma unroll
-  for (int s = 0; s < NK; ++s) {
-    const uint4 u = col < G ? ld16(qh + (size_t)col * D + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0);
-    qf[s] = __builtin_bit_cast(bf16x8, u);
   }
-  auto score_round = [&](const uint4 (&raw)[TPR][NK], int round) {
+  template <class Put>
+  __device__ __forceinline__ void score(const uint4 (&raw)[TPR][NK], int round, Put put) const {
 #pragma unroll
     for (int t = 0; t < TPR; ++t) {
       const int tile = (round * TPR + t) * WAVES + wave;
@@ -243,15 +255,26 @@ __device__ __forceinline__ void scan_block_scores_mfma(const uint16_t* qh, int G
       const int row0 = row_lo + 16 * tile + 4 * grp;   // first row of this lane group's block
       if (col == 0 && row0 < row_hi) put(row0 / kSubsPerBlock, m);
     }
-  };
-  const int n_rounds = (n_tiles + TPR * WAVES - 1) / (TPR * WAVES);
-  for (int r = 0; r < n_rounds; r += 2) {
-    if (r + 1 < n_rounds) load_round(rb, r + 1);
-    score_round(ra, r);
-    if (r + 1 >= n_rounds) break;
-    if (r + 2 < n_rounds) load_round(ra, r + 2);
-    score_round(rb, r + 1);
   }
+  template <class Put>
+  __device__ __forceinline__ void finish(Put put) {
+    uint4 rb[TPR][NK];
+    for (int r = 0; r < n_rounds; r += 2) {
+      if (r + 1 < n_rounds) load(rb, r + 1);
+      score(ra, r, put);
+      if (r + 1 >= n_rounds) break;
+      if (r + 2 < n_rounds) load(ra, r + 2);
+      score(rb, r + 1, put);
+    }
+  }
+};
+
+template <int D, int NT, class Put>
+__device__ __forceinline__ void scan_block_scores_mfma(const uint16_t* qh, int G, const uint16_t* kc_unit,
+                                                       int row_lo, int row_hi, int tid, Put put) {
+  if (row_lo >= row_hi) return;
+  MfmaScan<D, NT> sc(qh, G, kc_unit, row_lo, row_hi, tid);
+  sc.finish(put);
 }
 
 // Block scores of compressed-key rows [row_lo, row_hi) (whole blocks) of one
