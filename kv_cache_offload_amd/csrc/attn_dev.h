@@ -282,8 +282,9 @@ __device__ __forceinline__ void combine_partial(float& m_run, float& l_run, f32x
 // ---- merging across the wavefronts and workgroups of one (b, h) unit
 // (one-launch step).  A partial is (unnormalised numerators of the G x D
 // outputs, per-head max in log2 units, per-head sum).  Thread tid owns the
-// output pair 2*tid, 2*tid+1 (head-major); the per-head weights of the
-// pieces are computed once, by one lane group per head.
+// outputs tid and tid + NT (head-major), so every flagged store and load
+// instruction covers contiguous words; the per-head weights of the pieces
+// are computed once, by one lane group per head.
 
 // Maximum over aligned groups of N lanes (N = 8 or 16), every lane of the
 // group ends with it.
@@ -311,13 +312,13 @@ template <int D, int GMAX>
 constexpr int part_record_words() { return GMAX * D + 2 * GMAX; }
 
 // Workgroup: the WAVES wavefront partials (m_run = -inf for an idle
-// wavefront) -> one partial kept on chip: own[e] = numerator of output
-// 2*tid + e, L.M / L.den the heads' max and sum.
+// wavefront) -> one partial kept on chip: own[r] = numerator of output
+// tid + r * 64 * WAVES, L.M / L.den the heads' max and sum.
 template <int D, int WAVES, int GMAX>
 __device__ void merge_waves_keep(MergeLds<D, WAVES, GMAX>& L, float m_run, float l_run,
                                  const f32x4 (&o)[D / 16], int G, int tid, float (&own)[2]) {
   static_assert(WAVES == 8, "one 8-lane group per head");
-  static_assert(GMAX * D <= 2 * 64 * WAVES, "an output pair per thread");
+  static_assert(GMAX * D <= 2 * 64 * WAVES, "two outputs per thread");
   const int lane = tid & 63, wave = tid >> 6, col = lane & 15, grp = lane >> 4;
   if (col < G) {
 #pragma unroll
@@ -345,19 +346,15 @@ __device__ void merge_waves_keep(MergeLds<D, WAVES, GMAX>& L, float m_run, float
     }
   }
   __syncthreads();
-  own[0] = own[1] = 0.f;
-  if (2 * tid < G * D) {
-    const int idx = 2 * tid, g = idx / D, d = idx % D;
-    float n0 = 0.f, n1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      const float a = L.a[g][w];
-      const float2 v = *reinterpret_cast<const float2*>(&L.o[w][g][d]);
-      n0 = fmaf(a, v.x, n0);
-      n1 = fmaf(a, v.y, n1);
+  for (int r = 0; r < 2; ++r) {
+    const int idx = tid + r * 64 * WAVES, g = idx / D, d = idx % D;
+    float n = 0.f;
+    if (idx < G * D) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) n = fmaf(L.a[g][w], L.o[w][g][d], n);
     }
-    own[0] = n0;
-    own[1] = n1;
+    own[r] = n;
   }
 }
 
@@ -366,9 +363,10 @@ __device__ void merge_waves_keep(MergeLds<D, WAVES, GMAX>& L, float m_run, float
 template <int D, int WAVES, int GMAX>
 __device__ void publish_part_ll(const MergeLds<D, WAVES, GMAX>& L, int G, int tid, const float (&own)[2],
                                 uint64_t* rec, uint32_t flag) {
-  if (2 * tid < G * D) {
-    ll_store(&rec[2 * tid], own[0], flag);
-    ll_store(&rec[2 * tid + 1], own[1], flag);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = tid + r * 64 * WAVES;
+    if (idx < G * D) ll_store(&rec[idx], own[r], flag);
   }
   if (tid < G) {
     ll_store(&rec[GMAX * D + 2 * tid], L.M[tid], flag);
@@ -388,18 +386,15 @@ __device__ void merge_parts_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
   constexpr int REC = part_record_words<D, GMAX>();
   static_assert(MAXP <= 16, "one 16-lane group per head");
   __syncthreads();   // merge_waves_keep's reads of L.a are done
-  const bool mine = 2 * tid < G * D;
-  const int idx = 2 * tid;
-  const uint64_t* base = recs + idx;
+  constexpr int NT = 64 * WAVES;
+  const bool has0 = tid < G * D, has1 = tid + NT < G * D;
+  const uint64_t* base = recs + tid;
   uint64_t w0[MAXP], w1[MAXP];
 #pragma unroll
   for (int sp = 0; sp < MAXP; ++sp) {
-    if (sp < n_part && sp != own_part && mine) {
-      w0[sp] = ll_load(base + (size_t)sp * REC);
-      w1[sp] = ll_load(base + (size_t)sp * REC + 1);
-    } else {
-      w0[sp] = w1[sp] = ll_word(0.f, flag);
-    }
+    const bool other = sp < n_part && sp != own_part;
+    w0[sp] = other && has0 ? ll_load(base + (size_t)sp * REC) : ll_word(0.f, flag);
+    w1[sp] = other && has1 ? ll_load(base + (size_t)sp * REC + NT) : ll_word(0.f, flag);
   }
   if (tid < 16 * GMAX) {
     const int g = tid >> 4, sp = tid & 15;
@@ -436,23 +431,24 @@ __device__ void merge_parts_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
 #pragma unroll
       for (int sp = 0; sp < MAXP; ++sp) {
         if (!ll_ok(w0[sp], flag)) w0[sp] = ll_load(base + (size_t)sp * REC);
-        if (!ll_ok(w1[sp], flag)) w1[sp] = ll_load(base + (size_t)sp * REC + 1);
+        if (!ll_ok(w1[sp], flag)) w1[sp] = ll_load(base + (size_t)sp * REC + NT);
       }
       ++it;
     }
   }
   __syncthreads();
-  if (mine) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = tid + r * NT;
+    if (idx >= G * D) continue;
     const int g = idx / D;
-    float n0 = 0.f, n1 = 0.f;
+    float n = 0.f;
 #pragma unroll
     for (int sp = 0; sp < MAXP; ++sp) {
-      const float a = L.a[g][sp];
-      n0 = fmaf(a, sp == own_part ? own[0] : ll_float(w0[sp]), n0);
-      n1 = fmaf(a, sp == own_part ? own[1] : ll_float(w1[sp]), n1);
+      const float v = sp == own_part ? own[r] : ll_float(r ? w1[sp] : w0[sp]);
+      n = fmaf(L.a[g][sp], v, n);
     }
-    store_out(&out_g[idx], n0);
-    store_out(&out_g[idx + 1], n1);
+    store_out(&out_g[idx], n);
   }
 }
 
