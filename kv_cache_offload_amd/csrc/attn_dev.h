@@ -452,6 +452,66 @@ __device__ void merge_parts_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
   }
 }
 
+// A merge workgroup of a unit: outputs [out_lo, out_lo + n_out) (n_out <=
+// 64*WAVES, one per thread) from the unit's n_part flagged records, polled
+// until they carry `flag`; per-head weights from one 16-lane group per head
+// (lane = record); normalised and stored.  Splitting a unit's outputs over
+// several such workgroups divides the record bytes each one reads.
+template <class T, int D, int WAVES, int GMAX, int MAXP>
+__device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int n_part, int out_lo, int n_out,
+                               const uint64_t* recs, uint32_t flag, int spin_limit, int* err,
+                               typename T::storage* out_g) {
+  constexpr int REC = part_record_words<D, GMAX>();
+  static_assert(MAXP <= 16, "one 16-lane group per head");
+  const int idx = out_lo + tid;
+  const bool has = tid < n_out;
+  uint64_t w[MAXP];
+#pragma unroll
+  for (int sp = 0; sp < MAXP; ++sp)
+    w[sp] = (sp < n_part && has) ? ll_load(recs + (size_t)sp * REC + idx) : ll_word(0.f, flag);
+  if (tid < 16 * GMAX) {
+    const int g = tid >> 4, sp = tid & 15;
+    float m = -INFINITY, l = 0.f;
+    if (g < G && sp < n_part) {
+      const uint64_t* pm = recs + (size_t)sp * REC + GMAX * D + 2 * g;
+      uint64_t wm = ll_load(pm), wl = ll_load(pm + 1);
+      wm = ll_wait(pm, wm, flag, spin_limit, err);
+      wl = ll_wait(pm + 1, wl, flag, spin_limit, err);
+      m = ll_float(wm);
+      l = ll_float(wl);
+    }
+    const float M = group_max<16>(m);
+    const float a = m == -INFINITY ? 0.f : exp2f(m - M);
+    const float den = group_sum<16>(a * l);
+    L.a[g][sp] = den > 0.f ? a / den : 0.f;
+  }
+  {
+    int it = 0;
+    while (true) {
+      bool ok = true;
+#pragma unroll
+      for (int sp = 0; sp < MAXP; ++sp) ok = ok && ll_ok(w[sp], flag);
+      if (ok || it >= spin_limit) {
+        if (!ok) atomicAdd(err, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int sp = 0; sp < MAXP; ++sp)
+        if (!ll_ok(w[sp], flag)) w[sp] = ll_load(recs + (size_t)sp * REC + idx);
+      ++it;
+    }
+  }
+  __syncthreads();
+  if (has) {
+    const int g = idx / D;
+    float n = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < MAXP; ++sp) n = fmaf(L.a[g][sp], ll_float(w[sp]), n);
+    store_out(&out_g[idx], n);
+  }
+}
+
 // The last workgroup of a (b, h): merge the n_split partials in one round
 // trip (split maxima and sums into LDS, numerators into registers), then
 // normalise and store.  Reuses L's merge buffer.  With own_part >= 0 the

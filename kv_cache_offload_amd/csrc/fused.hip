@@ -6,32 +6,36 @@
 // "1. Algorithme : NOSA": the eviction head scores KV pairs independently of
 // the query; ED-DMA selects on pre-exponential scores).  So the attention over
 // Gamma_e -- three quarters of the step's bytes at kq/k = 1/4 -- does not
-// wait for the query-aware scan.  Each (b, KV head) unit gets W workgroups:
-//   E workers (j < nE)  scan one slice of the unit's compressed keys and
-//                       publish the block scores, then attend their share of
-//                       Gamma_e (cached per unit in the workspace, keyed by
-//                       the window block, recomputed when the window moves);
-//   Q workers (j >= nE) attend the window while the scores arrive, then each
-//                       takes top-kq itself (the first one also writes the
-//                       union out) and attends its share of X = Gamma_q \
-//                       Gamma_e.
+// wait for the query-aware scan.  Each (b, KV head) unit gets W + nM
+// workgroups:
+//   E workers (j < nE)       scan one slice of the unit's compressed keys and
+//                            publish the block scores, then attend their
+//                            share of Gamma_e (cached per unit in the
+//                            workspace, tagged with the window block,
+//                            recomputed when the window moves);
+//   Q workers (nE <= j < W)  attend the window while the scores arrive, then
+//                            each takes top-kq itself (the first one also
+//                            writes the union out) and attends its share of
+//                            X = Gamma_q \ Gamma_e;
+//   merge workgroups (j >= W) each combine all W partials for one slice of
+//                            the unit's outputs and store it.
 // Work is dealt in 32-token halves of blocks, one per wavefront at a time.
-// The unit's last workgroup merges all partials, keeping its own on chip.
-// Spreading the scan over every E worker lets it finish while the chip's
-// bandwidth is still free, which shortens the scan -> select -> X chain.
+// Every E and Q worker publishes one partial (its wavefronts merged in LDS).
 //
 // Every hand-off between workgroups goes through flagged 8-byte words
 // (payload + launch flag; see nosa_common.h): producers store and move on,
-// consumers poll the words.  The flag is a per-unit launch counter that the
-// merging workgroup advances when it is done -- by then every workgroup of
-// the unit has read it, since the merge depends on all of them -- so the
-// workspace never needs resetting between launches.
+// consumers poll the words.  The flag is a per-unit launch counter; the last
+// merge workgroup advances it once every merge workgroup has read it (each
+// posts a start word), by which point every other workgroup of the unit has
+// read it too, since the merges depend on all of them.  The workspace never
+// needs resetting between launches.
 //
 // Workgroup j of unit u has index j * U + u, and every wait is on a
-// workgroup of lower index (Q workers wait on E workers, the merger on all
-// others), which the dispatcher has started earlier, so each wait ends; the
-// waits are bounded as well (a timeout is counted in the workspace and leaves
-// a wrong result, never a hang).
+// workgroup of lower index (Q workers wait on E workers, merge workgroups on
+// all the others), which the dispatcher has started earlier, so each wait
+// ends; the waits are bounded as well (a timeout is counted in the workspace
+// and leaves a wrong result, never a hang).  The merge workgroups come last
+// in the grid, so they occupy CUs only once E workers have finished.
 #include "nosa_common.h"
 #include "nosa_launch.h"
 #include "attn_dev.h"
@@ -48,13 +52,12 @@ constexpr int kScoreRegs = 8;         // score words polled per thread at once (
 constexpr int kStepWgsTarget = 256;   // workgroups per launch to aim for: one per CU
 
 struct StepGeometry {
-  int units, W, nQ, nE;
-  size_t off_epoch, off_err, off_ge, off_score, off_part, total;
+  int units, W, nQ, nE, nM;
+  size_t off_epoch, off_err, off_ge, off_score, off_part, off_mstart, total;
 };
 
 static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq,
                                   int ke) {
-  (void)n_q_heads;
   (void)ke;
   StepGeometry g{};
   g.units = batch * n_kv_heads;
@@ -66,6 +69,9 @@ static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int 
   nQ = nQ > W - 1 ? W - 1 : nQ;
   g.nQ = nQ;
   g.nE = W - nQ;
+  // merge workgroups: about 256 outputs each, at most 4
+  const int GD = (n_q_heads / n_kv_heads) * head_dim;
+  g.nM = GD >= 1024 ? 4 : (GD >= 512 ? 2 : 1);
   const size_t U = g.units;
   const size_t rec = (size_t)kStepGMax * head_dim + 2 * kStepGMax;
   size_t o = 0;
@@ -74,6 +80,7 @@ static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int 
   g.off_ge = o; o += align256(U * (kStepMaxK + 1) * 8);
   g.off_score = o; o += align256(U * (size_t)nb * 8);
   g.off_part = o; o += align256(U * (size_t)W * rec * 8);
+  g.off_mstart = o; o += align256(U * 4 * 8);
   g.total = o;
   return g;
 }
@@ -115,13 +122,13 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     const typename T::storage* __restrict__ k_comp, const float* __restrict__ e_blk,
     const typename T::storage* __restrict__ kv, int n_q_heads, int n_kv_heads, int nb, int kq,
     int ke, float scale_log2, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
-    typename T::storage* __restrict__ out, unsigned char* __restrict__ ws, int W, int nQ,
-    size_t off_err, size_t off_ge, size_t off_score, size_t off_part) {
+    typename T::storage* __restrict__ out, unsigned char* __restrict__ ws, int W, int nQ, int nM,
+    size_t off_err, size_t off_ge, size_t off_score, size_t off_part, size_t off_mstart) {
   constexpr int ND = D / 16;
   constexpr int REC = part_record_words<D, kStepGMax>();
   constexpr int GER = (kStepMaxK + 1 + kStepThreads - 1) / kStepThreads;   // cache words per thread
   const int G = n_q_heads / n_kv_heads;
-  const int U = gridDim.x / W;
+  const int U = gridDim.x / (W + nM);
   const int nE = W - nQ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k_cap = kq + ke;
@@ -131,6 +138,33 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   const int b = unit / n_kv_heads, h = unit % n_kv_heads;
   int* epoch = reinterpret_cast<int*>(ws);
   int* err = reinterpret_cast<int*>(ws + off_err);
+  const uint64_t* recs_all = reinterpret_cast<const uint64_t*>(ws + off_part);
+  constexpr int REC_ = part_record_words<D, kStepGMax>();
+
+  if (j >= W) {
+    // ---------------- merge workgroup m of the unit: a slice of the output
+    // from all W records.  Every other workgroup of the unit precedes it in
+    // index order.  The last merge workgroup advances the unit's launch
+    // counter once every merge workgroup has read it (a start word each).
+    extern __shared__ __align__(16) unsigned char lds_m[];
+    auto& L = *reinterpret_cast<MergeLds<D, kStepWaves, kStepGMax>*>(lds_m);
+    const int m = j - W;
+    const uint32_t flag = (uint32_t)__builtin_amdgcn_readfirstlane(load_coherent_i(&epoch[unit])) + 1u;
+    uint64_t* mstart = reinterpret_cast<uint64_t*>(ws + off_mstart) + (size_t)unit * 4;
+    if (tid == 0) ll_store(&mstart[m], 0u, flag);
+    const int GD = G * D, per = (GD + nM - 1) / nM;
+    const int lo = min(GD, m * per), n_out = min(per, GD - lo);
+    typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
+    merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs_all + (size_t)unit * W * REC_, flag,
+                                                    kSpinLimit, err, out_g);
+    if (m == nM - 1) {
+      if (tid < m) ll_wait(&mstart[tid], ll_load(&mstart[tid]), flag, kSpinLimit, err);
+      __syncthreads();
+      if (tid == 0) store_coherent_i(&epoch[unit], (int)(flag == 0xFFFFFFFFu ? 0u : flag));
+    }
+    return;
+  }
+
   uint64_t* score_ll = reinterpret_cast<uint64_t*>(ws + off_score) + (size_t)unit * nb;
   // Gamma_e cache: word 0 = count, words 1.. = ids, each tagged with the
   // window block + 1 it was computed for
@@ -415,26 +449,21 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   __syncthreads();   // the selection arrays in LDS are dead; L reuses the space
   float own[2];
   merge_waves_keep<D, kStepWaves, kStepGMax>(L, m_run, l_run, o, G, tid, own);
-  if (j != W - 1) {
-    publish_part_ll<D, kStepWaves, kStepGMax>(L, G, tid, own, recs + (size_t)j * REC, flag);
-    return;
-  }
-  merge_parts_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, j, own, recs, flag, kSpinLimit, err, out_g);
-  // every workgroup of the unit has read this launch's flag: advance it
-  __syncthreads();
-  if (tid == 0) store_coherent_i(&epoch[unit], (int)(flag == 0xFFFFFFFFu ? 0u : flag));
+  publish_part_ll<D, kStepWaves, kStepGMax>(L, G, tid, own, recs + (size_t)j * REC, flag);
+  (void)out_g;
 }
 
 template <class T, int D>
 static void launch(const LaunchStep& a) {
   const StepGeometry g = step_geometry(a.batch, a.n_q_heads, a.n_kv_heads, D, a.nb, a.kq, a.ke);
-  const int wgs = g.units * g.W;
+  const int wgs = g.units * (g.W + g.nM);
   const float scale_log2 = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((step_kernel<T, D>), dim3(wgs), dim3(kStepThreads), step_lds_bytes<D>(a.nb), a.stream,
                      (const typename T::storage*)a.q, a.pos, (const typename T::storage*)a.k_comp,
                      a.e_blk, (const typename T::storage*)a.kv, a.n_q_heads, a.n_kv_heads, a.nb,
                      a.kq, a.ke, scale_log2, a.sel, a.n_sel, (typename T::storage*)a.out,
-                     (unsigned char*)a.ws, g.W, g.nQ, g.off_err, g.off_ge, g.off_score, g.off_part);
+                     (unsigned char*)a.ws, g.W, g.nQ, g.nM, g.off_err, g.off_ge, g.off_score, g.off_part,
+                     g.off_mstart);
 }
 
 void launch_step(const LaunchStep& a) {
