@@ -326,7 +326,8 @@ def test_prefill128k_chunk_selection():
     ("layer32k", dict(batch=3, prompt_len=64 * 40 + 50, n_steps=100)),     # crosses block ends
     ("layer32k", dict(batch=2, prompt_len=64 * 200 + 7, n_steps=70, kq=5, ke=0)),
     ("layer32k", dict(batch=2, prompt_len=64 * 30 + 60, n_steps=10, kq=0, ke=9, head_dim=64, n_q_heads=4)),
-], ids=["tiny", "boundaries", "kq-only", "ke-only-D64"])
+    ("layer32k", dict(batch=2, prompt_len=64 * 10 + 5, n_steps=70)),          # fewer candidates than kq
+], ids=["tiny", "boundaries", "kq-only", "ke-only-D64", "short-context"])
 def test_fused_step_matches_oracle(wname, over):
     _banner(f"fused step {wname} {over}")
     w = NI.scaled(NI.WORKLOADS[wname], **over) if over else NI.WORKLOADS[wname]
@@ -350,5 +351,27 @@ def test_fused_step_layer32k_full():
     s1, n1, o1, layer = H.run_resident(w, K, V, lam, q, fused=True)
     assert layer.step_timeouts() == 0
     for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
+
+
+@pytest.mark.parametrize("batch", [32, 64], ids=["64-units", "128-units"])
+def test_fused_step_many_units(batch):
+    """Many (b, h) units: few workgroups per unit (a single E worker scanning
+    in several rounds, several halves per wavefront) and, at 128 units, more
+    workgroups than CUs, so later ones start only as earlier ones finish."""
+    _banner(f"fused step with {2 * batch} units")
+    w = NI.scaled(NI.WORKLOADS["layer32k"], batch=batch, prompt_len=64 * 100 + 10, n_steps=5)
+    K, V, lam, q = NI.layer_inputs(w)
+    s1, n1, o1, layer = H.run_resident(w, K, V, lam, q, fused=True)
+    assert layer.step_timeouts() == 0
+    s2, n2, o2, _ = H.run_resident(w, K, V, lam, q, fused=False)
+    for a, b in zip(n1, n2):
+        assert np.array_equal(a, b)
+    for a, b in zip(s1, s2):
+        assert np.array_equal(a, b)
+    for a, b in zip(o1, o2):
+        assert float(np.max(np.abs(a - b))) < 2e-2
+    for b in (0, batch - 1):
         for h in range(w.n_kv_heads):
             H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
