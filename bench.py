@@ -58,6 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-offload", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch each step instead of graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -270,6 +271,8 @@ def main():
 
     if not args.no_offload:
         result["offload"] = _offload_leg(torch, NI, R)
+    if not args.no_prefill:
+        result["prefill"] = _prefill_leg(torch, NI, R, nb)
     if not args.no_cpu:
         result["cpu_baseline"] = _cpu_baseline(NI, w, K, V, lam, q)
     print(json.dumps(result), flush=True)
@@ -359,6 +362,65 @@ def _offload_leg(torch, NI, R):
         "memcpy_h2d_gbps": round(link_ref, 2),
         "host_link_frac_of_memcpy": round(link / link_ref, 4),
         "cold_frac_of_memcpy": round(cold_link / link_ref, 4),
+    }
+
+
+def _prefill_leg(torch, NI, R, nb):
+    """The prefill128k workload: pool the compressed keys and eviction scores of
+    a 131072-token prompt, then select for the 64 query rows at its end (each
+    row a decode selection at its own position).  Both timed cold: a 1 GiB
+    scratch buffer is streamed before every timed launch, so neither the keys
+    (64 MiB) nor the compressed keys (4 MiB) sit in the 256 MB Infinity Cache."""
+    w = NI.WORKLOADS["prefill128k"]
+    t0 = time.perf_counter()
+    K, V, lam, q = NI.layer_inputs(w)
+    log(f"inputs {w.name}: {time.perf_counter() - t0:.1f}s")
+    kv, logits, qd, pos = _device_inputs(w, K, V, lam, q, R)
+    del K, V
+    NB = w.n_blocks
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, NB, w.dtype, w.kq, w.ke)
+    n_q = w.n_steps
+    qrows = qd.permute(1, 0, 2, 3).contiguous()             # [B, n_query, Hq, D]
+    posr = pos.t().contiguous()                             # [B, n_query]
+    sel = torch.full((w.batch, n_q, w.n_kv_heads, w.kq + w.ke), -1, dtype=torch.int32, device="cuda")
+    n_sel = torch.zeros((w.batch, n_q, w.n_kv_heads), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, w.kq, w.ke), dtype=torch.uint8,
+                     device="cuda")
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=20):
+        out = []
+        for _ in range(reps):
+            sink.copy_(scratch.sum())                           # read 1 GiB: clean, cold caches
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            out.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(out)), float(np.percentile(out, 10)), float(np.percentile(out, 90))
+
+    n_tok = w.prompt_len
+    units = w.batch * w.n_kv_heads
+    complete = n_tok // 64
+    pool_us, pool_p10, pool_p90 = timed(lambda: layer.pool_blocks(kv, logits, 0, complete))
+    D = w.head_dim
+    pool_bytes = units * complete * (64 * D * 2 + 64 * 4 + 4 * D * 2 + 4 * 4 + 4)
+    sel_us, sel_p10, sel_p90 = timed(lambda: nb.select_blocks(layer.dims, qrows, n_q, posr, layer.k_comp,
+                                                                layer.e_blk, w.kq, w.ke, sel, n_sel, ws))
+    c = int(w.positions()[0]) // 64
+    G = w.n_q_heads // w.n_kv_heads
+    sel_bytes = units * (n_q * 2 * G * D * 2 + 4 * c * D * 2 + 4 * c)
+    log(f"prefill: pooling {pool_us:.1f} us ({pool_bytes / pool_us / 1e3:.0f} GB/s), "
+        f"selection of {n_q} rows {sel_us:.1f} us")
+    return {
+        "workload": "prefill128k", "prompt": n_tok, "query_rows": n_q, "timing": "cold (1 GiB streamed first)",
+        "pool_us": round(pool_us, 2), "pool_us_p10_p90": [round(pool_p10, 2), round(pool_p90, 2)],
+        "pool_bytes": int(pool_bytes), "pool_gbps": round(pool_bytes / pool_us / 1e3, 1),
+        "pool_frac": round(pool_bytes / pool_us / 1e3 / HBM_PEAK_GBPS, 4),
+        "select_us": round(sel_us, 2), "select_us_p10_p90": [round(sel_p10, 2), round(sel_p90, 2)],
+        "select_bytes": int(sel_bytes),
     }
 
 
