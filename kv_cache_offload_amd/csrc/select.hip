@@ -139,6 +139,162 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   if (tid == 0) n_sel[row] = total;
 }
 
+// ---------------------------------------------------------------------------
+// Many query rows per KV head (a prefill chunk): the compressed keys are
+// scanned once per chunk of query rows instead of once per row.
+//   mscan_kernel  grid (splits, units, row chunks): a 16-row tile of K-bar
+//                 (MFMA operand A, loaded once) times the query heads of
+//                 16/G rows at a time (operand B), per-row head sums over G
+//                 lanes (DPP, the same tree as the single-row scan, so the
+//                 scores are identical), max over the block's four rows;
+//                 scores go to the workspace [row][block].
+//   mtopk_kernel  one workgroup per row: top-kq of its scores and top-ke of E
+//                 over its candidates, union ascending (as select_kernel).
+constexpr int kMRows = 8;          // query rows per scan workgroup (at least one MFMA column block)
+constexpr int kMThreads = 512;
+__host__ __device__ constexpr int mrows_per_chunk(int G) { return 16 / G > kMRows ? 16 / G : kMRows; }
+
+template <int G>
+__device__ __forceinline__ float head_sum(float v) {
+  if constexpr (G >= 16) return group_sum<16>(v);
+  else if constexpr (G >= 8) return group_sum<8>(v);
+  else if constexpr (G >= 4) return group_sum<4>(v);
+  else if constexpr (G >= 2) return group_sum<2>(v);
+  else return v;
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kMThreads) mscan_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
+                                                          const uint16_t* __restrict__ k_comp, int n_query,
+                                                          int n_q_heads, int n_kv_heads, int nb, float* __restrict__ score) {
+  constexpr int NK = D / 32;
+  constexpr int QPB = 16 / G;       // query rows per 16-column MFMA block
+  constexpr int RPC = mrows_per_chunk(G);
+  constexpr int NCB = RPC / QPB;    // column blocks per chunk
+  constexpr int WAVES = kMThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int n_split = gridDim.x;
+  const int unit = blockIdx.y;       // b * Hkv + h
+  const int b = unit / n_kv_heads, h = unit % n_kv_heads;
+  const int r0 = blockIdx.z * RPC;
+  // the scan covers blocks below the largest window of the chunk
+  int cmax = 0;
+  for (int r = r0; r < min(n_query, r0 + RPC); ++r) {
+    const int p = pos[(size_t)b * n_query + r];
+    const int c = (p >= 0 && p < nb * kBlock) ? p / kBlock : 0;
+    cmax = max(cmax, c);
+  }
+  const int bps = (nb + n_split - 1) / n_split;
+  const int blk_lo = min(cmax, (int)blockIdx.x * bps), blk_hi = min(cmax, blk_lo + bps);
+  if (blk_lo >= blk_hi) return;
+  const int row_lo = kSubsPerBlock * blk_lo, row_hi = kSubsPerBlock * blk_hi;
+  const uint16_t* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D;
+  // B operands of the chunk: column block cb, lane column col -> row r0 + cb*QPB + col/G, head col%G
+  bf16x8 qf[NCB][NK];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int r = r0 + cb * QPB + col / G;
+    const int hd = h * G + col % G;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const uint4 u = r < n_query ? ld16(q + (((size_t)b * n_query + r) * n_q_heads + hd) * D + 32 * s + 8 * grp)
+                                  : make_uint4(0, 0, 0, 0);
+      qf[cb][s] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  const int n_tiles = (row_hi - row_lo + 15) / 16;
+  for (int tile = wave; tile < n_tiles; tile += WAVES) {
+    const int row = min(row_lo + 16 * tile + col, row_hi - 1);
+    uint4 ka[NK];
+#pragma unroll
+    for (int s = 0; s < NK; ++s) ka[s] = ld16(kc + (size_t)row * D + 32 * s + 8 * grp);
+    const int rowb = row_lo + 16 * tile + 4 * grp;   // first row of this lane group's block
+    const int blk = rowb / kSubsPerBlock;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NK; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]), qf[cb][s], acc, 0, 0, 0);
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, head_sum<G>(acc[i]));
+      const int r = r0 + cb * QPB + col / G;
+      if (col % G == 0 && r < n_query && rowb < row_hi)
+        score[(((size_t)b * n_query + r) * n_kv_heads + h) * nb + blk] = m;
+    }
+  }
+}
+
+template <class T>
+__global__ void __launch_bounds__(kMThreads) mtopk_kernel(const int32_t* __restrict__ pos, const float* __restrict__ e_blk,
+                                                          const float* __restrict__ score, int n_query, int n_kv_heads,
+                                                          int nb, int kq, int ke, int32_t* __restrict__ sel,
+                                                          int32_t* __restrict__ n_sel) {
+  constexpr int kH = kMThreads / 2;
+  const int row = blockIdx.x;               // (b * n_query + r) * Hkv + h
+  const int h = row % n_kv_heads;
+  const int br = row / n_kv_heads;
+  const int b = br / n_query;
+  const int64_t unit = (int64_t)b * n_kv_heads + h;
+  const int tid = threadIdx.x;
+  const int k_cap = kq + ke;
+  const int p = pos[br];
+  const int c = (p >= 0 && p < nb * kBlock) ? p / kBlock : 0;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const size_t kb = align256((size_t)nb * 4), lb = align256((size_t)nb * 2);
+  uint32_t* key_q = reinterpret_cast<uint32_t*>(lds);
+  uint32_t* key_e = reinterpret_cast<uint32_t*>(lds + kb);
+  uint16_t* blist_q = reinterpret_cast<uint16_t*>(lds + 2 * kb);
+  uint16_t* blist_e = reinterpret_cast<uint16_t*>(lds + 2 * kb + lb);
+  uint8_t* flag_q = lds + 2 * kb + 2 * lb;
+  uint8_t* flag_e = flag_q + align256((size_t)nb);
+  __shared__ int s_hist[2][kBins];
+  __shared__ int s_small[2][32];
+  __shared__ int s_wsum[kMThreads / 64];
+  const float* sc = score + (size_t)row * nb;
+  const float* eb = e_blk + (size_t)unit * nb;
+  for (int j = tid; j < c; j += kMThreads) {
+    key_q[j] = orderable(sc[j]);
+    key_e[j] = orderable(eb[j]);
+    flag_q[j] = 0;
+    flag_e[j] = 0;
+  }
+  __syncthreads();
+  const int half = tid / kH;
+  select_top<kH>(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, s_hist[half], s_small[half],
+                 half ? blist_e : blist_q, tid % kH);
+  const int total = write_union<kMThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
+  if (tid == 0) n_sel[row] = total;
+}
+
+template <int D>
+static bool launch_multi(const LaunchSelect& a) {
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int rows = a.batch * a.n_query * a.n_kv_heads;
+  const int units = a.batch * a.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  const int chunks = (a.n_query + mrows_per_chunk(G) - 1) / mrows_per_chunk(G);
+  int splits = (a.nb + 127) / 128;
+  splits = splits < 1 ? 1 : (splits > 32 ? 32 : splits);
+  char* ws = (char*)a.ws;
+  float* score = (float*)(ws + align256((size_t)rows * sizeof(int32_t)));
+  const dim3 grid(splits, units, chunks);
+  const uint16_t* q = (const uint16_t*)a.q;
+  const uint16_t* kc = (const uint16_t*)a.k_comp;
+  switch (G) {
+    case 1: hipLaunchKernelGGL((mscan_kernel<D, 1>), grid, dim3(kMThreads), 0, a.stream, q, a.pos, kc, a.n_query, a.n_q_heads, a.n_kv_heads, a.nb, score); break;
+    case 2: hipLaunchKernelGGL((mscan_kernel<D, 2>), grid, dim3(kMThreads), 0, a.stream, q, a.pos, kc, a.n_query, a.n_q_heads, a.n_kv_heads, a.nb, score); break;
+    case 4: hipLaunchKernelGGL((mscan_kernel<D, 4>), grid, dim3(kMThreads), 0, a.stream, q, a.pos, kc, a.n_query, a.n_q_heads, a.n_kv_heads, a.nb, score); break;
+    case 8: hipLaunchKernelGGL((mscan_kernel<D, 8>), grid, dim3(kMThreads), 0, a.stream, q, a.pos, kc, a.n_query, a.n_q_heads, a.n_kv_heads, a.nb, score); break;
+    default: return false;
+  }
+  hipLaunchKernelGGL((mtopk_kernel<Bf16>), dim3(rows), dim3(kMThreads), select_lds_bytes(a.nb), a.stream, a.pos,
+                     a.e_blk, score, a.n_query, a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel);
+  return true;
+}
+
 template <class T, int D>
 static void launch(const LaunchSelect& a) {
   const int rows = a.batch * a.n_query * a.n_kv_heads;
@@ -153,6 +309,10 @@ static void launch(const LaunchSelect& a) {
 }
 
 void launch_select(const LaunchSelect& a) {
+  if (a.bf16 && a.n_query >= kMRows) {
+    const bool done = a.head_dim == 128 ? launch_multi<128>(a) : launch_multi<64>(a);
+    if (done) return;
+  }
   if (a.bf16) {
     if (a.head_dim == 128) launch<Bf16, 128>(a); else launch<Bf16, 64>(a);
   } else {

@@ -320,6 +320,57 @@ def test_prefill128k_chunk_selection():
             assert got == S or H.selection_ok(got, s_q, E, c, w.kq, w.ke), (h, r)
 
 
+MULTI_CASES = [
+    # name, workload overrides, n_query, kq, ke
+    ("D128 G8", dict(), 13, 16, 48),
+    ("D64 G4", dict(head_dim=64, n_q_heads=8), 21, 12, 20),
+    ("D128 G1", dict(n_q_heads=2), 19, 8, 8),
+    ("D64 G2 kq only", dict(head_dim=64, n_q_heads=4), 9, 30, 0),
+]
+
+
+@pytest.mark.parametrize("name,over,n_q,kq,ke", MULTI_CASES, ids=[c[0] for c in MULTI_CASES])
+def test_select_many_rows_matches_oracle(name, over, n_q, kq, ke):
+    """Chunks of query rows share one scan of the compressed keys; every row
+    keeps its own window, including rows whose position is out of range."""
+    _banner(f"select many rows {name}")
+    T = 64 * 640 + 11
+    w = _w("layer32k", batch=2, prompt_len=T, n_steps=1, kq=kq, ke=ke, prefill=True, **over)
+    K, V, lam, _ = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, kq, ke)
+    layer.pool_blocks(kv, logits, 0, T // 64)
+    rng = np.random.default_rng(5)
+    qn = NI.round_to_bf16(rng.standard_normal((w.batch, n_q, w.n_q_heads, w.head_dim)).astype(np.float32))
+    posn = rng.integers(0, T, size=(w.batch, n_q)).astype(np.int32)
+    posn[0, 0], posn[1, n_q - 1], posn[0, n_q // 2] = -1, 64 * w.n_blocks + 5, 63
+    qd = torch.from_numpy(qn).cuda().to(torch.bfloat16)
+    posd = torch.from_numpy(posn).cuda()
+    k_cap = kq + ke
+    sel = torch.full((w.batch, n_q, w.n_kv_heads, k_cap), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((w.batch, n_q, w.n_kv_heads), -7, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, kq, ke), dtype=torch.uint8, device="cuda")
+    nb.select_blocks(layer.dims, qd, n_q, posd, layer.k_comp, layer.e_blk, kq, ke, sel, n_sel, ws)
+    sel = sel.cpu().numpy()
+    n_sel = n_sel.cpu().numpy()
+    ties = 0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            kbar = O.subblock_key_means(K[b, h], bf16=True)
+            E = O.block_eviction_scores(O.subblock_logit_means(lam[b, h]))
+            for r in range(n_q):
+                p = int(posn[b, r])
+                c = p // 64 if 0 <= p < 64 * w.n_blocks else 0
+                s_q = O.query_block_scores(qn[b, r, h * w.group:(h + 1) * w.group], kbar, c)
+                _, _, S = O.select_blocks(s_q, E, c, kq, ke)
+                got = list(sel[b, r, h, : n_sel[b, r, h]])
+                assert np.all(sel[b, r, h, n_sel[b, r, h]:] == -1), (b, r, h)
+                if got != S:
+                    assert H.selection_ok(got, s_q, E, c, kq, ke), (b, r, h, p, got, S)
+                    ties += 1
+    assert ties <= 2
+
+
 # ---------------------------------------------------- one-launch decode step
 @pytest.mark.parametrize("wname,over", [
     ("tiny", {}),
