@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-offload", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 28-layer offload stack (about 2 min of input generation)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch each step instead of graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -271,8 +272,15 @@ def main():
 
     if not args.no_offload:
         result["offload"] = _offload_leg(torch, NI, R)
+        torch._C._host_emptyCache()          # hand the offload leg's pinned cache back
     if not args.no_prefill:
         result["prefill"] = _prefill_leg(torch, NI, R, nb)
+    if not args.no_stack:
+        try:
+            result["stack"] = _stack_leg(torch, NI, R)
+        except RuntimeError as e:            # e.g. not enough pinned host memory for 56 GiB of caches
+            log(f"stack leg failed: {e}")
+            result["stack"] = {"workload": "stack128k", "error": str(e).splitlines()[0][:200]}
     if not args.no_cpu:
         result["cpu_baseline"] = _cpu_baseline(NI, w, K, V, lam, q)
     print(json.dumps(result), flush=True)
@@ -362,6 +370,127 @@ def _offload_leg(torch, NI, R):
         "memcpy_h2d_gbps": round(link_ref, 2),
         "host_link_frac_of_memcpy": round(link / link_ref, 4),
         "cold_frac_of_memcpy": round(cold_link / link_ref, 4),
+    }
+
+
+def _locality(sels, nsels, blocks):
+    """Mean over steps t >= 1 and units of the block-level overlap
+    |S(t) & (S(t-1) | {window block of t-1})| / |S(t)| (steps with an empty
+    S(t) are skipped)."""
+    vals = []
+    for t in range(1, len(sels)):
+        prev, cur = sels[t - 1], sels[t]
+        for idx in np.ndindex(cur.shape[:-1]):
+            n = int(nsels[t][idx])
+            if n == 0:
+                continue
+            a = set(cur[idx][:n].tolist())
+            b = set(prev[idx][: int(nsels[t - 1][idx])].tolist()) | {blocks[t - 1]}
+            vals.append(len(a & b) / n)
+    return float(np.mean(vals)) if vals else float("nan")
+
+
+def _memcpy_h2d_gbps(torch, host):
+    """Rate of one 1 GiB pinned host -> HBM copy (the host-link reference)."""
+    src = host.reshape(-1)[: (1 << 29)]
+    dst = torch.empty_like(src, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    dst.copy_(src, non_blocking=True)
+    b.record()
+    b.synchronize()
+    return src.numel() * src.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+def _stack_leg(torch, NI, R):
+    """The stack128k workload: 28 layers, batch 16, 131072-token context, each
+    layer's KV cache in pinned host memory (2 GiB per layer) with an HBM pool
+    of 80 blocks per KV head.  A decode step runs the layers in order, each
+    select -> fetch (side stream) -> attention.  The pools start empty, so
+    step 0 (cold, 64 misses per KV head per layer) is reported apart."""
+    w = NI.WORKLOADS["stack128k"]
+    workers = NI.host_workers()
+    positions = w.positions()
+    blocks = [int(p) // 64 for p in positions]
+    stack = R.OffloadStack(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype,
+                           w.kq, w.ke, w.pool_slots)
+    qs = []
+    t0 = time.perf_counter()
+    for l in range(w.n_layers):
+        K, V, lam, q = NI.layer_inputs(w, l, workers=workers)
+        stack.load_layer(l, K, V, lam, blocks[0], sorted(set(blocks)))
+        qs.append(torch.from_numpy(q).cuda().to(R.torch_dtype(w.dtype)))
+        del K, V, lam
+        if l % 4 == 3 or l == w.n_layers - 1:
+            log(f"stack: {l + 1} layers loaded, {time.perf_counter() - t0:.0f}s")
+    setup_s = time.perf_counter() - t0
+    pos = torch.from_numpy(np.repeat(positions[:, None], w.batch, axis=1).astype(np.int32)).cuda()
+    torch.cuda.synchronize()
+    link_ref = _memcpy_h2d_gbps(torch, stack.host[0])
+
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    fetch_ev = [[] for _ in range(w.n_layers)]
+    step_ev = []
+    rec_sel, rec_n, rec_miss = [], [], []
+
+    def on_layer(l, L):
+        rec_sel.append(L.sel.clone())
+        rec_n.append(L.n_sel.clone())
+        rec_miss.append(L.n_miss.clone())
+
+    for t in range(w.n_steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer, fetch_ev)
+        e1.record(main)
+        step_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    nL = w.n_layers
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
+    fetch_ms = np.array([[a.elapsed_time(b) for a, b in fetch_ev[l]] for l in range(nL)]).T   # [t, l]
+    n_sel = np.stack([x.cpu().numpy() for x in rec_n]).reshape(w.n_steps, nL, w.batch, w.n_kv_heads)
+    n_miss = np.stack([x.cpu().numpy() for x in rec_miss]).reshape(w.n_steps, nL, w.batch, w.n_kv_heads)
+    sels = np.stack([x.cpu().numpy() for x in rec_sel]).reshape(w.n_steps, nL, w.batch, w.n_kv_heads, -1)
+    gamma = _locality([sels[t] for t in range(w.n_steps)], [n_sel[t] for t in range(w.n_steps)], blocks)
+
+    blk_bytes = 2 * 64 * w.head_dim * 2
+    warm = slice(1, None)
+    ms = float(np.median(step_ms[warm]))
+    # algorithmic HBM bytes of the warm steps, per layer-step, from the logged set sizes and misses
+    hbm = []
+    for t in range(1, w.n_steps):
+        sb, ab = step_bytes(w, list(n_sel[t]), [positions[t]] * nL)
+        hbm.append(sb.sum() + ab.sum() + n_miss[t].sum() * blk_bytes)     # + pool writes
+    hbm_gbps = float(np.mean(hbm)) / (ms * 1e-3) / 1e9
+    miss_bytes = n_miss.sum(axis=(2, 3)).astype(np.float64) * blk_bytes          # [t, l]
+    link = float(miss_bytes[warm].sum() / (fetch_ms[warm].sum() * 1e-3) / 1e9)
+    cold_link = float(miss_bytes[0].sum() / (fetch_ms[0].sum() * 1e-3) / 1e9)
+    fetch_share = float(fetch_ms[warm].sum() / step_ms[warm].sum())
+    log(f"stack: step {ms:.3f} ms ({ms / nL * 1e3:.1f} us per layer), cold step {step_ms[0]:.2f} ms, "
+        f"misses/unit/layer-step {n_miss[warm].mean():.2f}, gamma {gamma:.3f}, link {link:.1f} GB/s "
+        f"(cold {cold_link:.1f}; memcpy {link_ref:.1f}), HBM {hbm_gbps:.0f} GB/s")
+    return {
+        "workload": "stack128k", "layers": nL, "batch": w.batch, "context": w.prompt_len,
+        "pool_slots": w.pool_slots, "steps": w.n_steps, "graph": False,
+        "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+        "layer_tokens_per_s": round(w.batch * nL / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 4),
+        "ms_per_step_p10_p90": [round(float(np.percentile(step_ms[warm], 10)), 4),
+                                round(float(np.percentile(step_ms[warm], 90)), 4)],
+        "us_per_layer_step": round(ms / nL * 1e3, 2),
+        "cold_step_ms": round(float(step_ms[0]), 3),
+        "hbm_gbps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "misses_per_unit_layer_step": round(float(n_miss[warm].mean()), 3),
+        "miss_fraction": round(float(n_miss[warm].sum() / n_sel[warm].sum()), 4),
+        "locality_gamma": round(gamma, 4),
+        "host_link_gbps": round(link, 2), "cold_step_host_link_gbps": round(cold_link, 2),
+        "memcpy_h2d_gbps": round(link_ref, 2), "host_link_frac_of_memcpy": round(link / link_ref, 4),
+        "cold_frac_of_memcpy": round(cold_link / link_ref, 4),
+        "fetch_share_of_step": round(fetch_share, 4),
+        "setup_seconds": round(setup_s, 1),
     }
 
 

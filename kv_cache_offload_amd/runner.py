@@ -200,6 +200,82 @@ class DecodeLayer:
         self.attend_pool(q, window, pos, main)
 
 
+class OffloadStack:
+    """Several attention layers decoding together in offload mode.
+
+    Each layer keeps its KV cache in pinned host memory, its own HBM pool of
+    `pool_slots` blocks per KV head and its own compressed keys; a decode
+    step runs the layers one after another (select -> fetch -> attention per
+    layer), the order a model's layers impose, since a layer's query exists
+    only once the layer below has produced its output.
+    """
+
+    def __init__(self, n_layers: int, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                 n_blocks: int, dtype: str, kq: int, ke: int, pool_slots: int, device: str = "cuda"):
+        self.layers = [DecodeLayer(batch, n_q_heads, n_kv_heads, head_dim, n_blocks, dtype, kq, ke,
+                                   pool_slots=pool_slots, device=device) for _ in range(n_layers)]
+        L0 = self.layers[0]
+        # one pinned allocation for every layer: torch's pinned allocator rounds each
+        # request up to a power of two, which would nearly double 28 separate caches
+        self.host_all = torch.empty((n_layers, batch, n_kv_heads, n_blocks, L0.blk_elems), dtype=L0.tdt,
+                                    pin_memory=True)
+        self.host = [self.host_all[l] for l in range(n_layers)]     # pinned [B, Hkv, NB, block]
+        self.logits = [None] * n_layers      # device [B, Hkv, NB * 64] fp32
+        self.windows = [{} for _ in range(n_layers)]
+        self.block = None                    # window block of the last step
+
+    def load_layer(self, l: int, K: np.ndarray, V: np.ndarray, lam: np.ndarray, prompt_blocks: int,
+                   window_blocks) -> None:
+        """Layer l's cache from K, V [B, Hkv, T, D] and logits [B, Hkv, T]
+        (float32 arrays holding cache-dtype values): the compressed keys of
+        blocks [0, prompt_blocks) are pooled on the GPU, the listed window
+        blocks stay in HBM, and the packed cache moves to pinned host memory."""
+        L = self.layers[l]
+        kv = to_device_blocks(K, V, L.NB, L.dtype, device=L.dev)
+        logits = pad_logits(torch.from_numpy(lam).to(L.dev), L.NB)
+        L.pool_blocks(kv, logits, 0, prompt_blocks)
+        self.windows[l] = {int(c): kv[:, :, int(c)].clone() for c in window_blocks}
+        self.host[l].copy_(kv)
+        self.logits[l] = logits
+        self.block = prompt_blocks if self.block is None else self.block
+        del kv
+
+    def step(self, t: int, qs, pos: torch.Tensor, block: int, side: Optional[torch.cuda.Stream] = None,
+             on_layer=None, fetch_events=None) -> None:
+        """Decode step t of every layer: qs[l] is layer l's query [B, Hq, D],
+        pos [B] int32 the positions, all inside window block `block`.  When
+        the window has moved on, the block it left is complete: its compressed
+        keys are built and it enters the pool.  on_layer(l, layer) runs after
+        each layer is enqueued; fetch_events[l] (a list) gets the (start, end)
+        event pair around that layer's fetch."""
+        main = torch.cuda.current_stream()
+        done = self.block if block > self.block else None
+        for l, L in enumerate(self.layers):
+            ins_blk = ins_src = None
+            if done is not None:
+                L.pool_window(self.windows[l][done], self.logits[l], done, main)
+                ins_blk = torch.full((L.B,), done, dtype=torch.int32, device=L.dev)
+                ins_src = self.windows[l][done]
+            L.select(qs[l], pos, main)
+            fs = side if side is not None else main
+            if side is not None:
+                side.wait_stream(main)
+            ev = None
+            if fetch_events is not None:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[0].record(fs)
+            L.fetch(self.host[l], t, ins_blk, ins_src, fs)
+            if ev is not None:
+                ev[1].record(fs)
+                fetch_events[l].append(ev)
+            if side is not None:
+                main.wait_stream(side)
+            L.attend_pool(qs[l], self.windows[l][block], pos, main)
+            if on_layer is not None:
+                on_layer(l, L)
+        self.block = block
+
+
 def to_device_blocks(K: np.ndarray, V: np.ndarray, n_blocks: int, dtype: str, device="cuda") -> torch.Tensor:
     """numpy K, V [B, Hkv, T, D] (float32 holding cache-dtype values) -> packed device blocks."""
     tdt = torch_dtype(dtype)

@@ -35,8 +35,10 @@ Recipe (identical for every workload):
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -103,9 +105,12 @@ def scaled(w: Workload, **changes) -> Workload:
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return (u.astype(np.uint32) << 16).view(np.float32)
+    u = x.view(np.uint32)
+    r = (u >> 16) & 1          # ties go to the even neighbour
+    r += 0x7FFF
+    r += u                     # no wrap for finite inputs: at most 0xFF807FFF
+    r &= 0xFFFF0000
+    return r.view(np.float32)
 
 
 def _seed(w: Workload, layer: int) -> int:
@@ -151,13 +156,34 @@ def queries(w: Workload, layer: int = 0) -> np.ndarray:
     return _quantise(w, q)
 
 
-def layer_inputs(w: Workload, layer: int = 0, n_tokens: Optional[int] = None):
-    """Whole-layer inputs: K, V [B, Hkv, T, D], logits [B, Hkv, T], q [n, B, Hq, D]."""
+def layer_inputs(w: Workload, layer: int = 0, n_tokens: Optional[int] = None, workers: int = 1):
+    """Whole-layer inputs: K, V [B, Hkv, T, D], logits [B, Hkv, T], q [n, B, Hq, D].
+
+    Every (batch, KV head) unit has its own stream, so ``workers`` > 1 draws
+    units on that many threads with identical results."""
     T = w.total_tokens if n_tokens is None else n_tokens
     K = np.empty((w.batch, w.n_kv_heads, T, w.head_dim), np.float32)
     V = np.empty_like(K)
     lam = np.empty((w.batch, w.n_kv_heads, T), np.float32)
-    for b in range(w.batch):
-        for h in range(w.n_kv_heads):
-            K[b, h], V[b, h], lam[b, h] = unit_kv(w, b, h, layer, T)
+
+    def fill(u):
+        b, h = divmod(u, w.n_kv_heads)
+        K[b, h], V[b, h], lam[b, h] = unit_kv(w, b, h, layer, T)
+
+    units = range(w.batch * w.n_kv_heads)
+    if workers > 1:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, units))
+    else:
+        for u in units:
+            fill(u)
     return K, V, lam, queries(w, layer)
+
+
+def host_workers() -> int:
+    """Threads for input generation: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))

@@ -1,0 +1,28 @@
+"""Host-side helpers of bench.py (no GPU): the locality figure it reports
+from GPU selections must agree with the oracle's definition."""
+import numpy as np
+
+import bench
+from oracle import nosa_oracle as O
+
+
+def test_locality_matches_oracle_definition():
+    rng = np.random.default_rng(3)
+    steps, units, k = 6, 5, 8
+    sels = np.full((steps, units, k), -1, np.int32)
+    nsel = np.zeros((steps, units), np.int32)
+    blocks = [40, 40, 41, 41, 41, 42]
+    for t in range(steps):
+        for u in range(units):
+            n = int(rng.integers(0, k + 1)) if u else k
+            ids = np.sort(rng.choice(blocks[t], size=n, replace=False))
+            sels[t, u, :n] = ids
+            nsel[t, u] = n
+    ref = []
+    for t in range(1, steps):
+        for u in range(units):
+            if nsel[t, u]:
+                ref.append(O.locality(list(sels[t - 1, u, : nsel[t - 1, u]]), blocks[t - 1],
+                                      list(sels[t, u, : nsel[t, u]])))
+    got = bench._locality(list(sels), list(nsel), blocks)
+    assert abs(got - float(np.mean(ref))) < 1e-12

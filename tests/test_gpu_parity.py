@@ -290,6 +290,48 @@ def test_offload_workload_sampled_units():
         _pool_consistent(layer, host, b, h)
 
 
+def test_stack128k_sampled_layers():
+    """Two layers of the 28-layer stack (the first and the last, with their
+    own seeds) at full size: B=16, 131072-token context, pool of 80, 32 steps,
+    run by the stack driver the bench times; sampled units of both layers
+    against the oracle, pools against the host caches."""
+    _banner("stack128k: layers 0 and 27 at full size (B=16, 128K context, pool 80, 32 steps), sampled units")
+    w = NI.WORKLOADS["stack128k"]
+    layer_ids = (0, w.n_layers - 1)
+    positions = w.positions()
+    blocks = [int(p) // 64 for p in positions]
+    stack = R.OffloadStack(len(layer_ids), w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks,
+                           w.dtype, w.kq, w.ke, w.pool_slots)
+    inputs, qs = [], []
+    for i, lid in enumerate(layer_ids):
+        K, V, lam, q = NI.layer_inputs(w, lid, workers=NI.host_workers())
+        stack.load_layer(i, K, V, lam, blocks[0], sorted(set(blocks)))
+        inputs.append((K, V, lam, q))
+        qs.append(torch.from_numpy(q).cuda().to(torch.bfloat16))
+    pos = torch.from_numpy(np.repeat(positions[:, None], w.batch, axis=1).astype(np.int32)).cuda()
+    keys = ("sel", "n_sel", "phys", "miss_list", "n_miss")
+    rec = [{k: [] for k in keys + ("out",)} for _ in layer_ids]
+
+    def on_layer(i, L):
+        for k in keys:
+            rec[i][k].append(getattr(L, k).clone())
+        rec[i]["out"].append(L.out.float().clone())
+
+    side = torch.cuda.Stream()
+    for t in range(w.n_steps):
+        stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer)
+    torch.cuda.synchronize()
+    for i, lid in enumerate(layer_ids):
+        r = {k: [x.cpu().numpy() for x in v] for k, v in rec[i].items()}
+        K, V, lam, q = inputs[i]
+        misses = 0
+        for b, h in ((0, 0), (9, 1), (15, 1)):
+            st = H.check_offload_unit(w, K, V, lam, q, r, b, h)
+            misses += st["misses"]
+            _pool_consistent(stack.layers[i], stack.host[i], b, h)
+        assert misses >= 3 * (w.kq + w.ke), (lid, misses)     # at least the cold step's
+
+
 def test_prefill128k_chunk_selection():
     _banner("prefill128k: pool 131072 tokens, select for 64 query rows")
     w = NI.WORKLOADS["prefill128k"]
