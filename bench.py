@@ -296,40 +296,21 @@ def _device_inputs(w, K, V, lam, q, R):
     return kv, logits, qd, pos
 
 
-def _offload_leg(torch, NI, R):
-    """The offload workload: KV in pinned host memory, HBM pool of 80 blocks."""
-    w = NI.WORKLOADS["offload"]
-    t0 = time.perf_counter()
-    K, V, lam, q = NI.layer_inputs(w)
-    log(f"inputs {w.name}: {time.perf_counter() - t0:.1f}s")
-    kv_dev, logits, qd, pos = _device_inputs(w, K, V, lam, q, R)
-    del K, V
-    host = kv_dev.cpu().pin_memory()
-    positions = w.positions()
-    windows = {c: kv_dev[:, :, c].clone() for c in sorted({int(p) // 64 for p in positions})}
-    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq,
-                          w.ke, pool_slots=w.pool_slots)
-    c_prev = int(positions[0]) // 64
-    layer.pool_blocks(kv_dev, logits, 0, c_prev)
-    del kv_dev
-    torch.cuda.synchronize()
-    # host-link reference: one 1 GiB pinned -> HBM copy
-    ref_src = host.view(-1)[: (1 << 29)]
-    ref_dst = torch.empty_like(ref_src, device="cuda")
-    ref_dst.copy_(ref_src, non_blocking=True)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    ref_dst.copy_(ref_src, non_blocking=True)
-    b.record()
-    b.synchronize()
-    link_ref = ref_src.numel() * ref_src.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
-    del ref_dst
+KQ_SWEEP = (8, 16, 32, 64)        # kq at k = kq + ke = 64: kq/k = 0.125, 0.25, 0.5, 1.0
 
+
+def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos):
+    """One offload decode run from a cold pool; per-step events, no host sync
+    inside the loop.  Returns step and fetch times (ms), misses, set sizes and
+    selections per step."""
+    positions = w.positions()
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, kq, ke,
+                          pool_slots=w.pool_slots)
+    c_prev = int(positions[0]) // 64
+    layer.pool_blocks(kv_dev, logits, 0, c_prev)       # prefill: compressed keys of the prompt
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
-    blk_bytes = 2 * 64 * w.head_dim * 2
-    step_ms, fetch_ms, misses = [], [], []
+    ev, rec = [], []
     for t in range(w.n_steps):
         c = int(positions[t]) // 64
         ins_blk = ins_src = None
@@ -347,30 +328,85 @@ def _offload_leg(torch, NI, R):
         main.wait_stream(side)
         layer.attend_pool(qd[t], windows[c], pos[t], main)
         e1.record(main)
-        e1.synchronize()
-        step_ms.append(e0.elapsed_time(e1))
-        fetch_ms.append(f0.elapsed_time(f1))
-        misses.append(int(layer.n_miss.sum().item()))
+        ev.append((e0, e1, f0, f1))
+        rec.append((layer.n_miss.clone(), layer.n_sel.clone(), layer.sel.clone()))
         c_prev = c
-    warm = slice(1, None)                  # step 0 fills the cold pool
-    ms = float(np.mean(step_ms[warm]))
-    miss_bytes = np.array(misses, np.float64) * blk_bytes
-    link = float(miss_bytes[warm].sum() / (np.sum(fetch_ms[warm]) * 1e-3) / 1e9)
-    cold_link = float(miss_bytes[0] / (fetch_ms[0] * 1e-3) / 1e9)
+    torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(b) for a, b, _, _ in ev])
+    fetch_ms = np.array([a.elapsed_time(b) for _, _, a, b in ev])
+    misses = np.array([int(m.sum().item()) for m, _, _ in rec])
+    nsel = [n.cpu().numpy() for _, n, _ in rec]
+    sels = [x.cpu().numpy() for _, _, x in rec]
+    return step_ms, fetch_ms, misses, nsel, sels
+
+
+def _offload_leg(torch, NI, R):
+    """The offload workload: KV in pinned host memory, HBM pool of 80 blocks
+    per KV head, kq = 16 + ke = 48; then the kq/k sweep at k = 64 on the same
+    inputs (each point from a cold pool)."""
+    w = NI.WORKLOADS["offload"]
+    t0 = time.perf_counter()
+    K, V, lam, q = NI.layer_inputs(w, workers=NI.host_workers())
+    log(f"inputs {w.name}: {time.perf_counter() - t0:.1f}s")
+    kv_dev, logits, qd, pos = _device_inputs(w, K, V, lam, q, R)
+    del K, V
+    host = torch.empty(kv_dev.shape, dtype=kv_dev.dtype, pin_memory=True)
+    host.copy_(kv_dev)
+    positions = w.positions()
+    windows = {c: kv_dev[:, :, c].clone() for c in sorted({int(p) // 64 for p in positions})}
+    torch.cuda.synchronize()
+    link_ref = _memcpy_h2d_gbps(torch, host)
+    blocks = [int(p) // 64 for p in positions]
+    blk_bytes = 2 * 64 * w.head_dim * 2
     units = w.batch * w.n_kv_heads
-    log(f"offload: step {ms:.3f} ms, misses/unit/step {np.mean(misses[1:]) / units:.2f}, "
-        f"link {link:.1f} GB/s (cold step {cold_link:.1f}), memcpy ref {link_ref:.1f} GB/s")
-    return {
-        "workload": "offload", "batch": w.batch, "context": w.prompt_len, "pool_slots": w.pool_slots,
-        "steps": w.n_steps, "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
-        "ms_per_step": round(ms, 4), "cold_step_ms": round(step_ms[0], 4),
-        "misses_per_unit_step": round(float(np.mean(misses[1:])) / units, 3),
-        "miss_fraction": round(float(np.mean(misses[1:])) / (units * (w.kq + w.ke)), 4),
-        "host_link_gbps": round(link, 2), "cold_step_host_link_gbps": round(cold_link, 2),
-        "memcpy_h2d_gbps": round(link_ref, 2),
-        "host_link_frac_of_memcpy": round(link / link_ref, 4),
-        "cold_frac_of_memcpy": round(cold_link / link_ref, 4),
-    }
+    warm = slice(1, None)                      # step 0 fills the cold pool
+
+    def summary(kq, ke, step_ms, fetch_ms, misses, nsel, sels):
+        ms = float(np.median(step_ms[warm]))
+        miss_bytes = misses.astype(np.float64) * blk_bytes
+        link = float(miss_bytes[warm].sum() / (fetch_ms[warm].sum() * 1e-3) / 1e9)
+        return {
+            "kq": kq, "ke": ke, "kq_over_k": round(kq / (kq + ke), 4),
+            "tokens_per_s": round(w.batch / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "ms_per_step_p10_p90": [round(float(np.percentile(step_ms[warm], 10)), 4),
+                                    round(float(np.percentile(step_ms[warm], 90)), 4)],
+            "cold_step_ms": round(float(step_ms[0]), 4),
+            "misses_per_unit_step": round(float(misses[warm].mean()) / units, 3),
+            "miss_fraction": round(float(misses[warm].sum() / sum(n.sum() for n in nsel[1:])), 4),
+            "locality_gamma": round(_locality(sels, nsel, blocks), 4),
+            "host_link_gbps": round(link, 2), "host_link_frac_of_memcpy": round(link / link_ref, 4),
+            "cold_step_host_link_gbps": round(float(miss_bytes[0] / (fetch_ms[0] * 1e-3) / 1e9), 2),
+            "fetch_share_of_step": round(float(fetch_ms[warm].sum() / step_ms[warm].sum()), 4),
+        }
+
+    points = []
+    for kq in KQ_SWEEP:
+        ke = 64 - kq
+        pt = summary(kq, ke, *_offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos))
+        log(f"offload kq={kq:2d} ke={ke:2d}: step {pt['ms_per_step']:.3f} ms, misses/unit/step "
+            f"{pt['misses_per_unit_step']:.2f}, gamma {pt['locality_gamma']:.3f}, link {pt['host_link_gbps']:.1f} GB/s")
+        points.append(pt)
+    main_pt = next(p for p in points if p["kq"] == w.kq and p["ke"] == w.ke)
+    out = {"workload": "offload", "batch": w.batch, "context": w.prompt_len, "pool_slots": w.pool_slots,
+           "steps": w.n_steps, "graph": False, "memcpy_h2d_gbps": round(link_ref, 2)}
+    out.update(main_pt)
+    out["kq_sweep"] = [{k: v for k, v in p.items() if k not in ("ms_per_step_p10_p90",)} for p in points]
+    del windows, kv_dev
+    return out
+
+
+def _memcpy_h2d_gbps(torch, host):
+    """Rate of one 1 GiB pinned host -> HBM copy (the host-link reference)."""
+    src = host.reshape(-1)[: (1 << 29)]
+    dst = torch.empty_like(src, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    dst.copy_(src, non_blocking=True)
+    b.record()
+    b.synchronize()
+    return src.numel() * src.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
 def _locality(sels, nsels, blocks):
@@ -388,20 +424,6 @@ def _locality(sels, nsels, blocks):
             b = set(prev[idx][: int(nsels[t - 1][idx])].tolist()) | {blocks[t - 1]}
             vals.append(len(a & b) / n)
     return float(np.mean(vals)) if vals else float("nan")
-
-
-def _memcpy_h2d_gbps(torch, host):
-    """Rate of one 1 GiB pinned host -> HBM copy (the host-link reference)."""
-    src = host.reshape(-1)[: (1 << 29)]
-    dst = torch.empty_like(src, device="cuda")
-    dst.copy_(src, non_blocking=True)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    dst.copy_(src, non_blocking=True)
-    b.record()
-    b.synchronize()
-    return src.numel() * src.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
 def _stack_leg(torch, NI, R):
