@@ -200,6 +200,33 @@ class DecodeLayer:
         self.attend_pool(q, window, pos, main)
 
 
+class PinnedHost:
+    """Pinned host memory of an exact size (hipHostMalloc through the HIP
+    runtime torch has loaded), viewed as a CPU tensor.  torch's own pinned
+    allocator rounds every request up to a power of two, which turns a
+    56 GiB multi-layer cache into 64 GiB.  Keep this object alive as long as
+    the tensor is used."""
+
+    def __init__(self, shape, dtype: torch.dtype):
+        import ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so.7")      # the copy already in the process
+        n = int(np.prod(shape))
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        ptr = ctypes.c_void_p()
+        rc = self._hip.hipHostMalloc(ctypes.byref(ptr), ctypes.c_size_t(nbytes), ctypes.c_uint(0))
+        if rc != 0 or not ptr.value:
+            raise RuntimeError(f"hipHostMalloc of {nbytes} bytes failed (error {rc})")
+        self._ptr = ptr
+        raw = np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctypes.c_uint8)), shape=(nbytes,))
+        self.tensor = torch.from_numpy(raw).view(dtype).view(*shape)
+
+    def __del__(self):
+        if getattr(self, "_ptr", None) is not None and self._ptr.value:
+            self.tensor = None
+            self._hip.hipHostFree(self._ptr)
+            self._ptr = None
+
+
 class OffloadStack:
     """Several attention layers decoding together in offload mode.
 
@@ -215,10 +242,9 @@ class OffloadStack:
         self.layers = [DecodeLayer(batch, n_q_heads, n_kv_heads, head_dim, n_blocks, dtype, kq, ke,
                                    pool_slots=pool_slots, device=device) for _ in range(n_layers)]
         L0 = self.layers[0]
-        # one pinned allocation for every layer: torch's pinned allocator rounds each
-        # request up to a power of two, which would nearly double 28 separate caches
-        self.host_all = torch.empty((n_layers, batch, n_kv_heads, n_blocks, L0.blk_elems), dtype=L0.tdt,
-                                    pin_memory=True)
+        # one pinned allocation of the exact size for every layer
+        self._pinned = PinnedHost((n_layers, batch, n_kv_heads, n_blocks, L0.blk_elems), L0.tdt)
+        self.host_all = self._pinned.tensor
         self.host = [self.host_all[l] for l in range(n_layers)]     # pinned [B, Hkv, NB, block]
         self.logits = [None] * n_layers      # device [B, Hkv, NB * 64] fp32
         self.windows = [{} for _ in range(n_layers)]
