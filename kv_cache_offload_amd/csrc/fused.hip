@@ -289,20 +289,30 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   } else {
     // ---------------- Q worker
     const int qj = j - nE;
+    // Gamma_e membership per candidate (from the cache, or selected here),
+    // cleared first behind a barrier: the window's wavefronts reach the
+    // later phases well after the others
+    for (int jj = tid; jj < c; jj += kStepThreads) {
+      flag_e[jj] = 0;
+      if (!cache_ok) key_e[jj] = orderable(eb[jj]);
+    }
+    __syncthreads();
+    if (cache_ok) {
+#pragma unroll
+      for (int r = 0; r < GER; ++r) {
+        const int i = tid + r * kStepThreads;
+        const int id = (int)(uint32_t)gw[r];
+        if (i >= 1 && i <= ge_cap && id >= 0 && id < c) flag_e[id] = 1;
+      }
+    } else {
+      select_top<kStepThreads>(key_e, c, ke, flag_e, s_hist, s_small, blist, tid);
+    }
     // the window's halves first (first Q worker), while the scores arrive
     if (qj == 0 && valid_pos && wave < 2) {
       attend_halves<T, D>(q_group, G, unit_kv, nb, wave, 2, 2, [&](int) { return c; },
                           [&](int) { return win_len; }, scale_log2, lane, m_run, l_run, o);
     }
     uint8_t* bin_q = flag_q;   // per-candidate value bin of the query-aware score
-    for (int jj = tid; jj < c; jj += kStepThreads) {
-      flag_e[jj] = 0;
-      if (!cache_ok) key_e[jj] = orderable(eb[jj]);
-    }
-    if (!cache_ok) {
-      __syncthreads();
-      select_top<kStepThreads>(key_e, c, ke, flag_e, s_hist, s_small, blist, tid);
-    }
     // the scores (polled) with their range
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -323,14 +333,6 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     }
     for (int i = tid; i < kBins; i += kStepThreads) s_hist[i] = 0;
     if (tid == 0) s_small[20] = 0;
-    if (cache_ok) {
-#pragma unroll
-      for (int r = 0; r < GER; ++r) {
-        const int i = tid + r * kStepThreads;
-        const int id = (int)(uint32_t)gw[r];
-        if (i >= 1 && i <= ge_cap && id >= 0 && id < c) flag_e[id] = 1;
-      }
-    }
     __syncthreads();   // keys, ranges, flags
     // Gamma_q = the kq best of c (score desc, id asc): value bins between the
     // scores' min and max (fp64, monotone in the score), the bin holding the
