@@ -469,26 +469,19 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
 #pragma unroll
   for (int sp = 0; sp < MAXP; ++sp)
     w[sp] = (sp < n_part && has) ? ll_load(recs + (size_t)sp * REC + idx) : ll_word(0.f, flag);
-  if (tid < 16 * GMAX) {
-    const int g = tid >> 4, sp = tid & 15;
-    float m = -INFINITY, l = 0.f;
-    if (g < G && sp < n_part) {
-      const uint64_t* pm = recs + (size_t)sp * REC + GMAX * D + 2 * g;
-      uint64_t wm = ll_load(pm), wl = ll_load(pm + 1);
-      wm = ll_wait(pm, wm, flag, spin_limit, err);
-      wl = ll_wait(pm + 1, wl, flag, spin_limit, err);
-      m = ll_float(wm);
-      l = ll_float(wl);
-    }
-    const float M = group_max<16>(m);
-    const float a = m == -INFINITY ? 0.f : exp2f(m - M);
-    const float den = group_sum<16>(a * l);
-    L.a[g][sp] = den > 0.f ? a / den : 0.f;
-  }
+  // lanes of the first 16 * GMAX threads also own the (max, sum) words of
+  // record sp = tid % 16 for head g = tid / 16
+  const int g_ml = tid >> 4, sp_ml = tid & 15;
+  const bool has_ml = tid < 16 * GMAX && g_ml < G && sp_ml < n_part;
+  const uint64_t* pm = recs + (size_t)sp_ml * REC + GMAX * D + 2 * g_ml;
+  uint64_t wm = has_ml ? ll_load(pm) : ll_word(-INFINITY, flag);
+  uint64_t wl = has_ml ? ll_load(pm + 1) : ll_word(0.f, flag);
   {
+    // one loop for every word this thread waits on, so a record that lands
+    // late costs one reload round, not one per word kind
     int it = 0;
     while (true) {
-      bool ok = true;
+      bool ok = ll_ok(wm, flag) && ll_ok(wl, flag);
 #pragma unroll
       for (int sp = 0; sp < MAXP; ++sp) ok = ok && ll_ok(w[sp], flag);
       if (ok || it >= spin_limit) {
@@ -496,11 +489,21 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
         break;
       }
       __builtin_amdgcn_s_sleep(1);
+      if (!ll_ok(wm, flag)) wm = ll_load(pm);
+      if (!ll_ok(wl, flag)) wl = ll_load(pm + 1);
 #pragma unroll
       for (int sp = 0; sp < MAXP; ++sp)
         if (!ll_ok(w[sp], flag)) w[sp] = ll_load(recs + (size_t)sp * REC + idx);
       ++it;
     }
+  }
+  if (tid < 16 * GMAX) {
+    const float m = has_ml ? ll_float(wm) : -INFINITY;
+    const float l = has_ml ? ll_float(wl) : 0.f;
+    const float M = group_max<16>(m);
+    const float a = m == -INFINITY ? 0.f : exp2f(m - M);
+    const float den = group_sum<16>(a * l);
+    L.a[g_ml][sp_ml] = den > 0.f ? a / den : 0.f;
   }
   __syncthreads();
   if (has) {

@@ -313,13 +313,33 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
                           [&](int) { return win_len; }, scale_log2, lane, m_run, l_run, o);
     }
     uint8_t* bin_q = flag_q;   // per-candidate value bin of the query-aware score
-    // the scores (polled) with their range
+    // the scores (polled together: one reload round per late word, whatever
+    // its position) with their range
+    {
+      int it = 0;
+      while (true) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < kScoreRegs; ++i) ok = ok && (tid + i * kStepThreads >= c || ll_ok(w_sc[i], flag));
+        if (ok || it >= kSpinLimit) {
+          if (!ok) atomicAdd(err, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int i = 0; i < kScoreRegs; ++i) {
+          const int jj = tid + i * kStepThreads;
+          if (jj < c && !ll_ok(w_sc[i], flag)) w_sc[i] = ll_load(&score_ll[jj]);
+        }
+        ++it;
+      }
+    }
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int i = 0; i < kScoreRegs; ++i) {
       const int jj = tid + i * kStepThreads;
       if (jj < c) {
-        const uint32_t k = orderable(ll_float(ll_wait(&score_ll[jj], w_sc[i], flag, kSpinLimit, err)));
+        const uint32_t k = orderable(ll_float(w_sc[i]));
         key_q[jj] = k;
         kmin = min(kmin, k);
         kmax = max(kmax, k);
