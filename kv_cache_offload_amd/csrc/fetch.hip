@@ -150,19 +150,38 @@ __global__ void __launch_bounds__(64) pool_update_kernel(
   }
   const int need_v = m - n_free;
   if (need_v > 0) {
-    for (int s = lane; s < P; s += 64) {
-      if (s_blk[s] < 0 || s_prot[s]) continue;
-      const uint64_t k = lru_key(s_lu[s], s_blk[s]);
-      int r = 0;
-      for (int s2 = 0; s2 < P; ++s2)
-        if (s_blk[s2] >= 0 && !s_prot[s2] && lru_key(s_lu[s2], s_blk[s2]) < k) ++r;
-      if (r < need_v) s_vict[r] = s;
+    // the need_v evictable slots (resident, not in S) in (last_use, block)
+    // order: keys in registers (slot lane + 64 i), one wavefront minimum per
+    // victim; keys are distinct because resident blocks are
+    constexpr int kRegs = kMaxSlots / 64;
+    const int n_regs = (P + 63) / 64;
+    for (int r = lane; r < need_v; r += 64) s_vict[r] = -1;
+    uint64_t key[kRegs];
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) {
+      const int s = lane + 64 * i;
+      key[i] = ~0ull;
+      if (i < n_regs && s < P && s_blk[s] >= 0 && !s_prot[s]) key[i] = lru_key(s_lu[s], s_blk[s]);
+    }
+    for (int r = 0; r < need_v; ++r) {
+      uint64_t best = ~0ull;
+#pragma unroll
+      for (int i = 0; i < kRegs; ++i)
+        if (i < n_regs) best = key[i] < best ? key[i] : best;
+      best = wave_min_u64(best);
+      if (best == ~0ull) break;   // fewer evictable slots than misses (k > P is rejected on the host)
+#pragma unroll
+      for (int i = 0; i < kRegs; ++i)
+        if (i < n_regs && key[i] == best) {
+          s_vict[r] = lane + 64 * i;
+          key[i] = ~0ull;
+        }
     }
   }
   __syncthreads();
   int evicted_ins = 0;
   if (miss) {
-    const int ts = (rank < n_free) ? s_free[rank] : s_vict[rank - n_free];
+    const int ts = (rank < n_free) ? s_free[rank] : s_vict[rank - n_free];   // >= 0: pool_slots > k_cap
     const int old = s_blk[ts];
     if (old >= 0 && old != ins) bt[old] = -1;
     evicted_ins = (ins >= 0 && old == ins);
