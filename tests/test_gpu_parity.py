@@ -332,6 +332,45 @@ def test_stack128k_sampled_layers():
         assert misses >= 3 * (w.kq + w.ke), (lid, misses)     # at least the cold step's
 
 
+def test_stack_small_crosses_blocks():
+    """The stack driver across block boundaries: three layers, a ragged
+    prompt and 150 steps, so the window completes blocks that enter every
+    layer's pool; every unit of every layer against the oracle."""
+    _banner("stack: 3 layers, B=2, ragged prompt, 150 steps across blocks, pool 20")
+    w = _w("stack128k", batch=2, prompt_len=64 * 30 + 41, n_steps=150, kq=6, ke=8, pool_slots=20, n_layers=3)
+    positions = w.positions()
+    blocks = [int(p) // 64 for p in positions]
+    stack = R.OffloadStack(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype,
+                           w.kq, w.ke, w.pool_slots)
+    inputs, qs = [], []
+    for l in range(w.n_layers):
+        K, V, lam, q = NI.layer_inputs(w, l)
+        stack.load_layer(l, K, V, lam, blocks[0], sorted(set(blocks)))
+        inputs.append((K, V, lam, q))
+        qs.append(torch.from_numpy(q).cuda().to(torch.bfloat16))
+    pos = torch.from_numpy(np.repeat(positions[:, None], w.batch, axis=1).astype(np.int32)).cuda()
+    keys = ("sel", "n_sel", "phys", "miss_list", "n_miss")
+    rec = [{k: [] for k in keys + ("out",)} for _ in range(w.n_layers)]
+
+    def on_layer(i, L):
+        for k in keys:
+            rec[i][k].append(getattr(L, k).clone())
+        rec[i]["out"].append(L.out.float().clone())
+
+    side = torch.cuda.Stream()
+    for t in range(w.n_steps):
+        stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer)
+    torch.cuda.synchronize()
+    assert blocks[-1] > blocks[0] + 1
+    for l in range(w.n_layers):
+        r = {k: [x.cpu().numpy() for x in v] for k, v in rec[l].items()}
+        K, V, lam, q = inputs[l]
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                H.check_offload_unit(w, K, V, lam, q, r, b, h)
+                _pool_consistent(stack.layers[l], stack.host[l], b, h)
+
+
 def test_prefill128k_chunk_selection():
     _banner("prefill128k: pool 131072 tokens, select for 64 query rows")
     w = NI.WORKLOADS["prefill128k"]
