@@ -30,19 +30,13 @@ __device__ __forceinline__ uint64_t lru_key(int last_use, int block) {
   return ((uint64_t)((uint32_t)last_use ^ 0x80000000u) << 32) | (uint32_t)block;
 }
 
-__device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
-  return v;
-}
 
+// Minimum over the wavefront of a 64-bit key: the high words first, then the
+// low words of the lanes holding that high word (two DPP reductions).
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off);
-    v = o < v ? o : v;
-  }
-  return v;
+  const uint32_t hi = wave_min_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_min_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0xffffffffu);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __global__ void __launch_bounds__(64) pool_update_kernel(
@@ -103,7 +97,7 @@ __global__ void __launch_bounds__(64) pool_update_kernel(
     int fs = kMaxSlots;
     for (int s = lane; s < P; s += 64)
       if (s_blk[s] < 0) fs = min(fs, s);
-    fs = wave_min_int(fs);
+    fs = (int)wave_min_u32((uint32_t)fs);   // slots and kMaxSlots are non-negative
     if (fs < kMaxSlots) {
       ins_slot = fs;
     } else {
