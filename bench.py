@@ -321,12 +321,16 @@ def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos):
             ins_blk = torch.full((w.batch,), c_prev, dtype=torch.int32, device="cuda")
             ins_src = windows[c_prev]
         layer.select(qd[t], pos[t], main)
+        # pool update, then the gather on the side stream while the attention
+        # over the blocks already resident runs (the runner's offload step)
+        f0.record(main)
+        layer.update_pool(t, ins_blk, main)
         side.wait_stream(main)
-        f0.record(side)
-        layer.fetch(host, t, ins_blk, ins_src, side)
+        layer.gather(host, ins_src, side)
         f1.record(side)
+        layer.attend_pool_part(qd[t], windows[c], pos[t], 0, main)
         main.wait_stream(side)
-        layer.attend_pool(qd[t], windows[c], pos[t], main)
+        layer.attend_pool_part(qd[t], windows[c], pos[t], 1, main)
         e1.record(main)
         ev.append((e0, e1, f0, f1))
         rec.append((layer.n_miss.clone(), layer.n_sel.clone(), layer.sel.clone()))

@@ -200,6 +200,25 @@ int nosa_fetch_blocks(const nosa_dims* dims, const void* host_kv, void* pool,
                       int32_t* n_miss, void* stream);
 
 /*
+ * nosa_update_pool, nosa_gather_blocks -- the two phases of
+ * nosa_fetch_blocks as separate calls, so that work that needs only the
+ * updated tables (the attention over the blocks already resident, see
+ * nosa_sparse_decode_attn_pool) can run while the gather copies the misses.
+ * nosa_update_pool runs steps 1-3 (tables, phys, miss list); nosa_gather_blocks
+ * runs step 4 from the miss list, on any stream ordered after the update.
+ * Arguments and errors as for nosa_fetch_blocks; the pair has exactly its
+ * effect.  insert_src goes to the gather and is required there whenever the
+ * update was given insert_block (else the inserted slot is not filled).
+ */
+int nosa_update_pool(const nosa_dims* dims, int32_t pool_slots, int32_t* block_table,
+                     int32_t* slot_block, int32_t* slot_last_use, int32_t step, const int32_t* sel,
+                     const int32_t* n_sel, int32_t k_cap, const int32_t* insert_block, int32_t* phys,
+                     int32_t* miss_list, int32_t* n_miss, void* stream);
+int nosa_gather_blocks(const nosa_dims* dims, const void* host_kv, void* pool, int32_t pool_slots,
+                       int32_t k_cap, const void* insert_src, const int32_t* miss_list,
+                       const int32_t* n_miss, void* stream);
+
+/*
  * nosa_sparse_decode_attn -- exact attention over the selected blocks.
  *
  * Defined by the wmrh.cn NOSA-1B post ("工程实现亮点": two-stage attention,
@@ -236,6 +255,32 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
                             int64_t window_head_stride, int64_t window_block_stride,
                             const int32_t* pos, float scale, void* out, void* ws,
                             size_t ws_bytes, void* stream);
+
+/*
+ * nosa_sparse_decode_attn_pool -- nosa_sparse_decode_attn over the HBM pool
+ * of an offload step, in two parts around the fetch's gather.  Same result
+ * and arguments (blocks = the pool, blocks_per_head = pool_slots, phys from
+ * nosa_update_pool), plus that call's miss_list and n_miss:
+ *   part 0  attends the selected blocks whose slots this step's gather does
+ *           not write (the hits) and the window; it writes partials to ws
+ *           only.  Needs nosa_update_pool done, not the gather: run it
+ *           while the gather runs.
+ *   part 1  attends the slots the gather filled (the misses, and the block
+ *           the window completed when it is selected), then merges with
+ *           part 0's partials into out.  Needs part 0 and the gather done.
+ * Communication is the bottleneck of offloaded decoding (montaan summary,
+ * "Empirical Results and Analysis"; gist.science "Résultats
+ * Expérimentaux"), so the attention over the hits is moved off its path.
+ *   part       0 or 1
+ *   ws         as for nosa_sparse_decode_attn, shared by the two parts of a
+ *              step; part 1 leaves it ready for the next step.
+ */
+int nosa_sparse_decode_attn_pool(const nosa_dims* dims, const void* q, const void* pool,
+                                 int32_t pool_slots, const int32_t* phys, const int32_t* n_sel,
+                                 int32_t k_cap, const int32_t* miss_list, const int32_t* n_miss,
+                                 const void* window_kv, int64_t window_head_stride,
+                                 int64_t window_block_stride, const int32_t* pos, float scale,
+                                 int32_t part, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * nosa_decode_step -- one decode step of a resident cache in one launch:

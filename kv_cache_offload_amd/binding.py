@@ -23,7 +23,8 @@ OP_SELECT, OP_ATTN, OP_STEP = 1, 2, 3
 
 EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_sparse_decode_attn", "nosa_decode_step", "nosa_workspace_size",
-           "nosa_status_str", "nosa_last_error")
+           "nosa_status_str", "nosa_last_error", "nosa_update_pool", "nosa_gather_blocks",
+           "nosa_sparse_decode_attn_pool")
 
 
 class NosaError(RuntimeError):
@@ -57,13 +58,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_sparse_decode_attn.argtypes = [D, P, P, I32, P, P, I32, P, I64, I64, P, F, P, P, SZ, P]
     lib.nosa_decode_step.argtypes = [D, P, P, P, P, I32, I32, P, F, P, P, P, P, SZ, P]
     lib.nosa_workspace_size.argtypes = [D, I32, I32, I32, I32]
+    lib.nosa_update_pool.argtypes = [D, I32, P, P, P, I32, P, P, I32, P, P, P, P, P]
+    lib.nosa_gather_blocks.argtypes = [D, P, P, I32, I32, P, P, P, P]
+    lib.nosa_sparse_decode_attn_pool.argtypes = [D, P, P, I32, P, P, I32, P, P, P, I64, I64, P, F, I32, P, P, SZ, P]
     lib.nosa_workspace_size.restype = SZ
     lib.nosa_status_str.argtypes = [I32]
     lib.nosa_status_str.restype = ctypes.c_char_p
     lib.nosa_last_error.argtypes = []
     lib.nosa_last_error.restype = ctypes.c_char_p
     for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
-                 "nosa_decode_step"):
+                 "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -129,6 +133,36 @@ def fetch_blocks(d: Dims, host_kv, pool, pool_slots: int, block_table, slot_bloc
                                   _ptr(insert_src), _ptr(phys), _ptr(miss_list), _ptr(n_miss),
                                   _stream(stream))
     _check("nosa_fetch_blocks", rc)
+
+
+def update_pool(d: Dims, pool_slots: int, block_table, slot_block, slot_last_use, step: int, sel, n_sel,
+                k_cap: int, insert_block, phys, miss_list, n_miss, stream=None) -> None:
+    rc = load().nosa_update_pool(ctypes.byref(d), pool_slots, _ptr(block_table), _ptr(slot_block),
+                                 _ptr(slot_last_use), step, _ptr(sel), _ptr(n_sel), k_cap, _ptr(insert_block),
+                                 _ptr(phys), _ptr(miss_list), _ptr(n_miss), _stream(stream))
+    _check("nosa_update_pool", rc)
+
+
+def gather_blocks(d: Dims, host_kv, pool, pool_slots: int, k_cap: int, insert_src, miss_list, n_miss,
+                  stream=None) -> None:
+    rc = load().nosa_gather_blocks(ctypes.byref(d), _ptr(host_kv), _ptr(pool), pool_slots, k_cap,
+                                   _ptr(insert_src), _ptr(miss_list), _ptr(n_miss), _stream(stream))
+    _check("nosa_gather_blocks", rc)
+
+
+def sparse_decode_attn_pool(d: Dims, q, pool, pool_slots: int, phys, n_sel, k_cap: int, miss_list, n_miss,
+                            window_kv, window_head_stride: int, window_block_stride: int, pos,
+                            scale: Optional[float], part: int, out, ws, ws_bytes: Optional[int] = None,
+                            stream=None) -> None:
+    if scale is None:
+        scale = 1.0 / math.sqrt(d.head_dim)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = load().nosa_sparse_decode_attn_pool(ctypes.byref(d), _ptr(q), _ptr(pool), pool_slots, _ptr(phys),
+                                             _ptr(n_sel), k_cap, _ptr(miss_list), _ptr(n_miss), _ptr(window_kv),
+                                             window_head_stride, window_block_stride, _ptr(pos), scale, part,
+                                             _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+    _check("nosa_sparse_decode_attn_pool", rc)
 
 
 def sparse_decode_attn(d: Dims, q, blocks, blocks_per_head: int, phys, n_sel, k_cap: int,

@@ -38,26 +38,42 @@ static inline int attn_splits(int k_cap, int G) { return (k_cap + 1 + attn_waves
 size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap) {
   const size_t units = (size_t)batch * n_kv_heads;
   const size_t G = n_q_heads / n_kv_heads;
-  const size_t splits = attn_splits(k_cap, (int)G);
+  const size_t splits = attn_splits(k_cap, (int)G) + 1;   // + the fetched part of a pool step
   return align256(units * sizeof(int32_t)) + align256(units * splits * G * 2 * sizeof(float)) +
          align256(units * splits * G * head_dim * sizeof(float));
 }
 
-template <class T, int D, int WAVES, int GMAX>
+// Whether a pool slot is being filled by this step's fetch (a miss, or the
+// block the window just completed): its contents are not there until the
+// gather is done.
+__device__ __forceinline__ bool slot_fetched(int slot, const int32_t* ml, int n_miss, int k_cap) {
+  if (slot == ml[2 * k_cap + 1]) return true;
+  for (int i = 0; i < n_miss; ++i)
+    if (ml[2 * i + 1] == slot) return true;
+  return false;
+}
+
+// PART -1: the whole attention (splits merged by the last workgroup).
+// PART 0: a pool step's entries already resident plus the window, while the
+//         fetch's gather runs; partials only (splits 0 .. S-1).
+// PART 1: one workgroup per unit, the fetched entries, then the merge of its
+//         partial (split S) with part 0's.
+template <class T, int D, int WAVES, int GMAX, int PART>
 __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ blocks,
     int blocks_per_head, const int32_t* __restrict__ phys, const int32_t* __restrict__ n_sel,
     int k_cap, const typename T::storage* __restrict__ window_kv, int64_t win_head_stride,
     int64_t win_block_stride, const int32_t* __restrict__ pos, float scale_log2, int n_q_heads,
     int n_kv_heads, int nb, typename T::storage* __restrict__ out, int32_t* __restrict__ ticket,
-    float* __restrict__ part_ml, float* __restrict__ part_o) {
+    float* __restrict__ part_ml, float* __restrict__ part_o, const int32_t* __restrict__ miss_list,
+    const int32_t* __restrict__ n_miss_p, int n_split_main) {
   constexpr int ND = D / 16;
   const int G = n_q_heads / n_kv_heads;
   // grid (units, splits): workgroups are dispatched x-fastest, so every
   // unit's first split starts before any unit's second and the light last
   // splits (often just the window) go last
-  const int n_split = gridDim.y;
-  const int split = blockIdx.y;
+  const int n_split = PART < 0 ? (int)gridDim.y : n_split_main + 1;   // partial slots per unit
+  const int split = PART == 1 ? n_split_main : (int)blockIdx.y;
   const int unit = blockIdx.x;  // b * Hkv + h
   const int b = unit / n_kv_heads;
   const int h = unit % n_kv_heads;
@@ -76,28 +92,55 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   f32x4 o[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int e = split * WAVES + wave;
-  const typename T::storage* blk = nullptr;
-  int len = 0;
-  if (e < ns) {
-    const int pb = phys[(size_t)unit * k_cap + e];
-    if (pb >= 0 && pb < blocks_per_head) {
-      blk = blocks + ((size_t)unit * blocks_per_head + pb) * blk_elems;
-      len = kBlock;
-    }
-  } else if (e < n_ent) {
-    blk = window_kv + (int64_t)unit * win_head_stride + (int64_t)c * win_block_stride;
-    len = p - c * kBlock + 1;
-  }
   const typename T::storage* q_group = q + ((size_t)b * n_q_heads + (size_t)h * G) * D;
-  if (blk != nullptr) attend_block<T, D>(q_group, G, blk, len, scale_log2, lane, m_run, l_run, o);
+  const int32_t* ml = miss_list + (size_t)unit * (k_cap + 1) * 2;
+  int nm = 0;
+  if (PART >= 0) {
+    nm = n_miss_p[unit];
+    nm = nm < 0 ? 0 : (nm > k_cap ? k_cap : nm);
+  }
+  if (PART == 1) {
+    // the fetched entries, spread over the wavefronts
+    for (int e = wave; e < ns; e += WAVES) {
+      const int pb = phys[(size_t)unit * k_cap + e];
+      if (pb < 0 || pb >= blocks_per_head || !slot_fetched(pb, ml, nm, k_cap)) continue;
+      float mb, lb;
+      f32x4 ob[ND];
+      attend_block<T, D>(q_group, G, blocks + ((size_t)unit * blocks_per_head + pb) * blk_elems, kBlock, scale_log2,
+                         lane, mb, lb, ob);
+      combine_partial<ND>(m_run, l_run, o, mb, lb, ob);
+    }
+  } else {
+    const int e = split * WAVES + wave;
+    const typename T::storage* blk = nullptr;
+    int len = 0;
+    if (e < ns) {
+      const int pb = phys[(size_t)unit * k_cap + e];
+      if (pb >= 0 && pb < blocks_per_head && !(PART == 0 && slot_fetched(pb, ml, nm, k_cap))) {
+        blk = blocks + ((size_t)unit * blocks_per_head + pb) * blk_elems;
+        len = kBlock;
+      }
+    } else if (e < n_ent) {
+      blk = window_kv + (int64_t)unit * win_head_stride + (int64_t)c * win_block_stride;
+      len = p - c * kBlock + 1;
+    }
+    if (blk != nullptr) attend_block<T, D>(q_group, G, blk, len, scale_log2, lane, m_run, l_run, o);
+  }
 
   __shared__ AttnLds<D, WAVES, GMAX> L;
   typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
   float* pml = part_ml + (size_t)unit * n_split * G * 2;
   float* po = part_o + (size_t)unit * n_split * G * D;
   merge_waves<T, D, WAVES, GMAX>(L, m_run, l_run, o, G, tid, split, n_split, out_g, po, pml);
-  if (n_split == 1) return;
+  if (PART == 0 || n_split == 1) return;
+  if (PART == 1) {
+    // part 0's partials come from an earlier launch; this workgroup's own
+    // were just stored: wait for them, then merge all
+    wait_stores_done();
+    __syncthreads();
+    merge_splits<T, D, WAVES, GMAX>(L, G, tid, n_split, po, pml, out_g);
+    return;
+  }
 
   // ---- the last workgroup of this (b, h) merges the splits
   __shared__ int s_last;
@@ -121,14 +164,21 @@ static void launch_w(const LaunchAttn& a) {
   char* ws = (char*)a.ws;
   int32_t* ticket = (int32_t*)ws;
   float* part_ml = (float*)(ws + align256((size_t)units * sizeof(int32_t)));
-  float* part_o = (float*)((char*)part_ml + align256((size_t)units * splits * G * 2 * sizeof(float)));
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX>), dim3(units, splits), dim3(64 * WAVES), 0,
-                     a.stream, (const typename T::storage*)a.q, (const typename T::storage*)a.blocks,
-                     a.blocks_per_head, a.phys, a.n_sel, a.k_cap,
-                     (const typename T::storage*)a.window_kv, a.window_head_stride,
-                     a.window_block_stride, a.pos, scale_log2, a.n_q_heads, a.n_kv_heads, a.nb,
-                     (typename T::storage*)a.out, ticket, part_ml, part_o);
+  // partial slots are laid out for splits + 1 per unit in every mode
+  float* part_o = (float*)((char*)part_ml + align256((size_t)units * (splits + 1) * G * 2 * sizeof(float)));
+#define NOSA_ATTN_ARGS                                                                                        \
+  a.stream, (const typename T::storage*)a.q, (const typename T::storage*)a.blocks, a.blocks_per_head, a.phys, \
+      a.n_sel, a.k_cap, (const typename T::storage*)a.window_kv, a.window_head_stride, a.window_block_stride,  \
+      a.pos, scale_log2, a.n_q_heads, a.n_kv_heads, a.nb, (typename T::storage*)a.out, ticket, part_ml,        \
+      part_o, a.miss_list, a.n_miss, splits
+  if (a.part < 0)
+    hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, -1>), dim3(units, splits), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
+  else if (a.part == 0)
+    hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, 0>), dim3(units, splits), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, 1>), dim3(units, 1), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
+#undef NOSA_ATTN_ARGS
 }
 
 template <class T, int D>

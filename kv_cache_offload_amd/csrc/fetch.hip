@@ -252,9 +252,11 @@ __global__ void __launch_bounds__(kGatherThreads) gather_kernel(
 
 void launch_fetch(const LaunchFetch& a) {
   const int units = a.batch * a.n_kv_heads;
-  hipLaunchKernelGGL(pool_update_kernel, dim3(units), dim3(64), 0, a.stream, a.n_kv_heads, a.nb,
-                     a.pool_slots, a.k_cap, a.step, a.block_table, a.slot_block, a.slot_last_use,
-                     a.sel, a.n_sel, a.insert_block, a.phys, a.miss_list, a.n_miss);
+  if (a.phases & 1)
+    hipLaunchKernelGGL(pool_update_kernel, dim3(units), dim3(64), 0, a.stream, a.n_kv_heads, a.nb,
+                       a.pool_slots, a.k_cap, a.step, a.block_table, a.slot_block, a.slot_last_use,
+                       a.sel, a.n_sel, a.insert_block, a.phys, a.miss_list, a.n_miss);
+  if (!(a.phases & 2)) return;
   const int esize = a.bf16 ? 2 : 4;
   const int blk16 = 2 * kBlock * a.head_dim * esize / 16;
   hipLaunchKernelGGL(gather_kernel, dim3(a.k_cap + 1, units), dim3(kGatherThreads), 0, a.stream,

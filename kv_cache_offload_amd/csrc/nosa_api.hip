@@ -128,21 +128,22 @@ int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query, co
   return check_launch(fn);
 }
 
-int nosa_fetch_blocks(const nosa_dims* dims, const void* host_kv, void* pool, int32_t pool_slots,
-                      int32_t* block_table, int32_t* slot_block, int32_t* slot_last_use,
-                      int32_t step, const int32_t* sel, const int32_t* n_sel, int32_t k_cap,
-                      const int32_t* insert_block, const void* insert_src, int32_t* phys,
-                      int32_t* miss_list, int32_t* n_miss, void* stream) {
-  static const char* fn = "nosa_fetch_blocks";
+// nosa_fetch_blocks and its two phases (1: tables, 2: gather)
+static int fetch_phases(const char* fn, int phases, const nosa_dims* dims, const void* host_kv, void* pool,
+                        int32_t pool_slots, int32_t* block_table, int32_t* slot_block, int32_t* slot_last_use,
+                        int32_t step, const int32_t* sel, const int32_t* n_sel, int32_t k_cap,
+                        const int32_t* insert_block, const void* insert_src, int32_t* phys, int32_t* miss_list,
+                        int32_t* n_miss, void* stream) {
   if (int rc = check_dims(dims, fn)) return rc;
   if (k_cap < 0 || k_cap > kMaxFetchK)
     return fail(NOSA_ERR_UNSUPPORTED, fn, "k_cap must be in [0, 64]");
   if (pool_slots <= k_cap) return fail(NOSA_ERR_ARG, fn, "pool_slots must exceed k_cap = kq + ke");
   if (pool_slots > kMaxPoolSlots) return fail(NOSA_ERR_UNSUPPORTED, fn, "pool_slots above 1024");
-  if (!host_kv || !pool || !block_table || !slot_block || !slot_last_use || !n_sel || !miss_list ||
-      !n_miss || (k_cap > 0 && (!sel || !phys)))
+  if (!miss_list || !n_miss) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if ((phases & 1) && (!block_table || !slot_block || !slot_last_use || !n_sel || (k_cap > 0 && (!sel || !phys))))
     return fail(NOSA_ERR_ARG, fn, "NULL buffer");
-  if (insert_block && !insert_src) return fail(NOSA_ERR_ARG, fn, "insert_block needs insert_src");
+  if ((phases & 2) && (!host_kv || !pool)) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (phases == 3 && insert_block && !insert_src) return fail(NOSA_ERR_ARG, fn, "insert_block needs insert_src");
   if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
     return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_kv_heads above 65535");
   nosa::LaunchFetch a{};
@@ -166,22 +167,50 @@ int nosa_fetch_blocks(const nosa_dims* dims, const void* host_kv, void* pool, in
   a.phys = phys;
   a.miss_list = miss_list;
   a.n_miss = n_miss;
+  a.phases = phases;
   a.stream = (hipStream_t)stream;
   nosa::launch_fetch(a);
   return check_launch(fn);
 }
 
-int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* blocks,
-                            int32_t blocks_per_head, const int32_t* phys, const int32_t* n_sel,
-                            int32_t k_cap, const void* window_kv, int64_t window_head_stride,
-                            int64_t window_block_stride, const int32_t* pos, float scale, void* out,
-                            void* ws, size_t ws_bytes, void* stream) {
-  static const char* fn = "nosa_sparse_decode_attn";
+int nosa_fetch_blocks(const nosa_dims* dims, const void* host_kv, void* pool, int32_t pool_slots,
+                      int32_t* block_table, int32_t* slot_block, int32_t* slot_last_use,
+                      int32_t step, const int32_t* sel, const int32_t* n_sel, int32_t k_cap,
+                      const int32_t* insert_block, const void* insert_src, int32_t* phys,
+                      int32_t* miss_list, int32_t* n_miss, void* stream) {
+  return fetch_phases("nosa_fetch_blocks", 3, dims, host_kv, pool, pool_slots, block_table, slot_block,
+                      slot_last_use, step, sel, n_sel, k_cap, insert_block, insert_src, phys, miss_list, n_miss,
+                      stream);
+}
+
+int nosa_update_pool(const nosa_dims* dims, int32_t pool_slots, int32_t* block_table, int32_t* slot_block,
+                     int32_t* slot_last_use, int32_t step, const int32_t* sel, const int32_t* n_sel,
+                     int32_t k_cap, const int32_t* insert_block, int32_t* phys, int32_t* miss_list,
+                     int32_t* n_miss, void* stream) {
+  return fetch_phases("nosa_update_pool", 1, dims, nullptr, nullptr, pool_slots, block_table, slot_block,
+                      slot_last_use, step, sel, n_sel, k_cap, insert_block, nullptr, phys, miss_list, n_miss,
+                      stream);
+}
+
+int nosa_gather_blocks(const nosa_dims* dims, const void* host_kv, void* pool, int32_t pool_slots, int32_t k_cap,
+                       const void* insert_src, const int32_t* miss_list, const int32_t* n_miss, void* stream) {
+  return fetch_phases("nosa_gather_blocks", 2, dims, host_kv, pool, pool_slots, nullptr, nullptr, nullptr, 0,
+                      nullptr, nullptr, k_cap, nullptr, insert_src, nullptr, const_cast<int32_t*>(miss_list),
+                      const_cast<int32_t*>(n_miss), stream);
+}
+
+static int sparse_attn(const char* fn, int part, const nosa_dims* dims, const void* q, const void* blocks,
+                       int32_t blocks_per_head, const int32_t* phys, const int32_t* n_sel, int32_t k_cap,
+                       const int32_t* miss_list, const int32_t* n_miss, const void* window_kv,
+                       int64_t window_head_stride, int64_t window_block_stride, const int32_t* pos, float scale,
+                       void* out, void* ws, size_t ws_bytes, void* stream) {
   if (int rc = check_dims(dims, fn)) return rc;
   if (k_cap < 0 || k_cap > 512) return fail(NOSA_ERR_UNSUPPORTED, fn, "k_cap must be in [0, 512]");
   if (blocks_per_head < 1 && k_cap > 0) return fail(NOSA_ERR_ARG, fn, "blocks_per_head must be >= 1");
   if (!q || !window_kv || !pos || !out || !n_sel || !ws || (k_cap > 0 && (!blocks || !phys)))
     return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (part >= 0 && (!miss_list || !n_miss)) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (part > 1) return fail(NOSA_ERR_ARG, fn, "part must be 0 or 1");
   if (window_head_stride < 0 || window_block_stride < 0)
     return fail(NOSA_ERR_ARG, fn, "window strides must be >= 0");
   if (!(scale == scale)) return fail(NOSA_ERR_ARG, fn, "scale is NaN");
@@ -209,9 +238,33 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
   a.scale = scale;
   a.out = out;
   a.ws = ws;
+  a.part = part;
+  a.miss_list = miss_list;
+  a.n_miss = n_miss;
   a.stream = (hipStream_t)stream;
   nosa::launch_attn(a);
   return check_launch(fn);
+}
+
+int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* blocks,
+                            int32_t blocks_per_head, const int32_t* phys, const int32_t* n_sel,
+                            int32_t k_cap, const void* window_kv, int64_t window_head_stride,
+                            int64_t window_block_stride, const int32_t* pos, float scale, void* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return sparse_attn("nosa_sparse_decode_attn", -1, dims, q, blocks, blocks_per_head, phys, n_sel, k_cap,
+                     nullptr, nullptr, window_kv, window_head_stride, window_block_stride, pos, scale, out, ws,
+                     ws_bytes, stream);
+}
+
+int nosa_sparse_decode_attn_pool(const nosa_dims* dims, const void* q, const void* pool, int32_t pool_slots,
+                                 const int32_t* phys, const int32_t* n_sel, int32_t k_cap,
+                                 const int32_t* miss_list, const int32_t* n_miss, const void* window_kv,
+                                 int64_t window_head_stride, int64_t window_block_stride, const int32_t* pos,
+                                 float scale, int32_t part, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (part < 0) return fail(NOSA_ERR_ARG, "nosa_sparse_decode_attn_pool", "part must be 0 or 1");
+  return sparse_attn("nosa_sparse_decode_attn_pool", part, dims, q, pool, pool_slots, phys, n_sel, k_cap,
+                     miss_list, n_miss, window_kv, window_head_stride, window_block_stride, pos, scale, out, ws,
+                     ws_bytes, stream);
 }
 
 int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,

@@ -54,6 +54,7 @@ struct LaunchFetch {
   int32_t* phys;
   int32_t* miss_list;
   int32_t* n_miss;
+  int phases;                  // 1: pool update, 2: gather, 3: both
   hipStream_t stream;
 };
 
@@ -73,6 +74,9 @@ struct LaunchAttn {
   float scale;
   void* out;
   void* ws;
+  int part;                    // -1 whole step; 0 / 1 the two parts of a pool step
+  const int32_t* miss_list;    // parts 0 and 1: the fetch's miss list and counts
+  const int32_t* n_miss;
   hipStream_t stream;
 };
 

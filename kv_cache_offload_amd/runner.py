@@ -188,16 +188,38 @@ class DecodeLayer:
 
     def step_offload(self, q, host_kv, window, pos, step: int, insert_block=None, insert_src=None,
                      side: Optional[torch.cuda.Stream] = None) -> None:
-        """select -> fetch on the side stream -> attention, ordered with events."""
+        """One offload step.  Without a side stream: select -> fetch -> attention
+        on one stream.  With one: select -> pool update, then the gather on the
+        side stream while the attention over the blocks already resident (and
+        the window) runs on the compute stream; then the attention over the
+        fetched blocks merges both."""
         main = torch.cuda.current_stream()
         self.select(q, pos, main)
         if side is None:
             self.fetch(host_kv, step, insert_block, insert_src, main)
-        else:
-            side.wait_stream(main)
-            self.fetch(host_kv, step, insert_block, insert_src, side)
-            main.wait_stream(side)
-        self.attend_pool(q, window, pos, main)
+            self.attend_pool(q, window, pos, main)
+            return
+        self.update_pool(step, insert_block, main)
+        side.wait_stream(main)
+        self.gather(host_kv, insert_src, side)
+        self.attend_pool_part(q, window, pos, 0, main)
+        main.wait_stream(side)
+        self.attend_pool_part(q, window, pos, 1, main)
+
+    def update_pool(self, step: int, insert_block: Optional[torch.Tensor] = None, stream=None) -> None:
+        nb.update_pool(self.dims, self.pool_slots, self.block_table, self.slot_block, self.slot_last_use, step,
+                       self.sel, self.n_sel, self.k, insert_block, self.phys, self.miss_list, self.n_miss,
+                       stream=stream)
+
+    def gather(self, host_kv: torch.Tensor, insert_src: Optional[torch.Tensor] = None, stream=None) -> None:
+        nb.gather_blocks(self.dims, host_kv, self.pool, self.pool_slots, self.k, insert_src, self.miss_list,
+                         self.n_miss, stream=stream)
+
+    def attend_pool_part(self, q: torch.Tensor, window: torch.Tensor, pos: torch.Tensor, part: int,
+                         stream=None) -> None:
+        nb.sparse_decode_attn_pool(self.dims, q, self.pool, self.pool_slots, self.phys, self.n_sel, self.k,
+                                   self.miss_list, self.n_miss, window, self.blk_elems, 0, pos, self.scale, part,
+                                   self.out, self.ws_attn, stream=stream)
 
 
 class PinnedHost:
@@ -283,20 +305,29 @@ class OffloadStack:
                 ins_blk = torch.full((L.B,), done, dtype=torch.int32, device=L.dev)
                 ins_src = self.windows[l][done]
             L.select(qs[l], pos, main)
-            fs = side if side is not None else main
-            if side is not None:
-                side.wait_stream(main)
             ev = None
             if fetch_events is not None:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[0].record(fs)
-            L.fetch(self.host[l], t, ins_blk, ins_src, fs)
-            if ev is not None:
-                ev[1].record(fs)
-                fetch_events[l].append(ev)
-            if side is not None:
+                ev[0].record(main)
+            window = self.windows[l][block]
+            if side is None:
+                L.fetch(self.host[l], t, ins_blk, ins_src, main)
+                if ev is not None:
+                    ev[1].record(main)
+                L.attend_pool(qs[l], window, pos, main)
+            else:
+                # the gather on the side stream, the attention over the resident
+                # blocks meanwhile (see DecodeLayer.step_offload)
+                L.update_pool(t, ins_blk, main)
+                side.wait_stream(main)
+                L.gather(self.host[l], ins_src, side)
+                if ev is not None:
+                    ev[1].record(side)
+                L.attend_pool_part(qs[l], window, pos, 0, main)
                 main.wait_stream(side)
-            L.attend_pool(qs[l], self.windows[l][block], pos, main)
+                L.attend_pool_part(qs[l], window, pos, 1, main)
+            if ev is not None:
+                fetch_events[l].append(ev)
             if on_layer is not None:
                 on_layer(l, L)
         self.block = block

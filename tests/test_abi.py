@@ -146,6 +146,36 @@ def test_attn_checks(lib):
     assert "scale" in lib.nosa_last_error().decode()
 
 
+def test_split_fetch_and_pool_attention_checks(lib):
+    d = _d()
+    with pytest.raises(nb.NosaError) as e:                # pool must exceed k
+        nb.update_pool(d, 64, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 64, None, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:                # the tables are required
+        nb.update_pool(d, 80, None, FAKE, FAKE, 0, FAKE, FAKE, 64, None, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:                # the host cache is required
+        nb.gather_blocks(d, None, FAKE, 80, 64, None, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.gather_blocks(d, FAKE, FAKE, 2000, 8, None, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+    need = nb.workspace_size(d, nb.OP_ATTN, 1, 64, 0)
+    base = [d, FAKE, FAKE, 80, FAKE, FAKE, 64, FAKE, FAKE, FAKE, 32768, 0, FAKE, None]
+    for part in (-1, 2):
+        with pytest.raises(nb.NosaError) as e:
+            nb.sparse_decode_attn_pool(*base, part, FAKE, FAKE, ws_bytes=need, stream=0)
+        assert e.value.code == nb.ERR_ARG
+    bad = list(base)
+    bad[7] = None                                         # the miss list is required
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_decode_attn_pool(*bad, 0, FAKE, FAKE, ws_bytes=need, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_decode_attn_pool(*base, 1, FAKE, FAKE, ws_bytes=need - 1, stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
+
+
 def test_step_checks(lib):
     d = _d()
     need = nb.workspace_size(d, nb.OP_STEP, 1, 16, 48)
