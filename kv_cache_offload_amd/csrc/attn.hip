@@ -38,7 +38,7 @@ static inline int attn_splits(int k_cap, int G) { return (k_cap + 1 + attn_waves
 size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap) {
   const size_t units = (size_t)batch * n_kv_heads;
   const size_t G = n_q_heads / n_kv_heads;
-  const size_t splits = attn_splits(k_cap, (int)G) + 1;   // + the fetched part of a pool step
+  const size_t splits = 2 * attn_splits(k_cap, (int)G);   // both parts of a pool step
   return align256(units * sizeof(int32_t)) + align256(units * splits * G * 2 * sizeof(float)) +
          align256(units * splits * G * head_dim * sizeof(float));
 }
@@ -55,9 +55,9 @@ __device__ __forceinline__ bool slot_fetched(int slot, const int32_t* ml, int n_
 
 // PART -1: the whole attention (splits merged by the last workgroup).
 // PART 0: a pool step's entries already resident plus the window, while the
-//         fetch's gather runs; partials only (splits 0 .. S-1).
-// PART 1: one workgroup per unit, the fetched entries, then the merge of its
-//         partial (split S) with part 0's.
+//         fetch's gather runs; partials only (slots 0 .. S-1).
+// PART 1: the same split of the entries, the fetched ones only (slots S ..
+//         2S-1); the last workgroup of the unit merges all 2S partials.
 template <class T, int D, int WAVES, int GMAX, int PART>
 __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ blocks,
@@ -72,8 +72,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   // grid (units, splits): workgroups are dispatched x-fastest, so every
   // unit's first split starts before any unit's second and the light last
   // splits (often just the window) go last
-  const int n_split = PART < 0 ? (int)gridDim.y : n_split_main + 1;   // partial slots per unit
-  const int split = PART == 1 ? n_split_main : (int)blockIdx.y;
+  const int n_split = PART < 0 ? (int)gridDim.y : 2 * n_split_main;   // partial slots per unit
+  const int split = PART == 1 ? n_split_main + (int)blockIdx.y : (int)blockIdx.y;
   const int unit = blockIdx.x;  // b * Hkv + h
   const int b = unit / n_kv_heads;
   const int h = unit % n_kv_heads;
@@ -99,28 +99,21 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     nm = n_miss_p[unit];
     nm = nm < 0 ? 0 : (nm > k_cap ? k_cap : nm);
   }
-  if (PART == 1) {
-    // the fetched entries, spread over the wavefronts
-    for (int e = wave; e < ns; e += WAVES) {
-      const int pb = phys[(size_t)unit * k_cap + e];
-      if (pb < 0 || pb >= blocks_per_head || !slot_fetched(pb, ml, nm, k_cap)) continue;
-      float mb, lb;
-      f32x4 ob[ND];
-      attend_block<T, D>(q_group, G, blocks + ((size_t)unit * blocks_per_head + pb) * blk_elems, kBlock, scale_log2,
-                         lane, mb, lb, ob);
-      combine_partial<ND>(m_run, l_run, o, mb, lb, ob);
-    }
-  } else {
-    const int e = split * WAVES + wave;
+  {
+    // entry e of this split: part 0 skips the fetched slots, part 1 takes
+    // only those (and no window)
+    const int e = (int)blockIdx.y * WAVES + wave;
     const typename T::storage* blk = nullptr;
     int len = 0;
     if (e < ns) {
       const int pb = phys[(size_t)unit * k_cap + e];
-      if (pb >= 0 && pb < blocks_per_head && !(PART == 0 && slot_fetched(pb, ml, nm, k_cap))) {
+      bool take = pb >= 0 && pb < blocks_per_head;
+      if (PART >= 0 && take) take = slot_fetched(pb, ml, nm, k_cap) == (PART == 1);
+      if (take) {
         blk = blocks + ((size_t)unit * blocks_per_head + pb) * blk_elems;
         len = kBlock;
       }
-    } else if (e < n_ent) {
+    } else if (e < n_ent && PART != 1) {
       blk = window_kv + (int64_t)unit * win_head_stride + (int64_t)c * win_block_stride;
       len = p - c * kBlock + 1;
     }
@@ -133,14 +126,6 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   float* po = part_o + (size_t)unit * n_split * G * D;
   merge_waves<T, D, WAVES, GMAX>(L, m_run, l_run, o, G, tid, split, n_split, out_g, po, pml);
   if (PART == 0 || n_split == 1) return;
-  if (PART == 1) {
-    // part 0's partials come from an earlier launch; this workgroup's own
-    // were just stored: wait for them, then merge all
-    wait_stores_done();
-    __syncthreads();
-    merge_splits<T, D, WAVES, GMAX>(L, G, tid, n_split, po, pml, out_g);
-    return;
-  }
 
   // ---- the last workgroup of this (b, h) merges the splits
   __shared__ int s_last;
@@ -148,7 +133,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   __syncthreads();
   if (tid == 0) {
     const int t = ticket_take(&ticket[unit]);
-    s_last = (t == n_split - 1);
+    s_last = (t == (int)gridDim.y - 1);
     if (s_last) ticket_reset(&ticket[unit]);
   }
   __syncthreads();
@@ -165,8 +150,8 @@ static void launch_w(const LaunchAttn& a) {
   int32_t* ticket = (int32_t*)ws;
   float* part_ml = (float*)(ws + align256((size_t)units * sizeof(int32_t)));
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  // partial slots are laid out for splits + 1 per unit in every mode
-  float* part_o = (float*)((char*)part_ml + align256((size_t)units * (splits + 1) * G * 2 * sizeof(float)));
+  // partial slots are laid out for 2 * splits per unit in every mode
+  float* part_o = (float*)((char*)part_ml + align256((size_t)units * 2 * splits * G * 2 * sizeof(float)));
 #define NOSA_ATTN_ARGS                                                                                        \
   a.stream, (const typename T::storage*)a.q, (const typename T::storage*)a.blocks, a.blocks_per_head, a.phys, \
       a.n_sel, a.k_cap, (const typename T::storage*)a.window_kv, a.window_head_stride, a.window_block_stride,  \
@@ -177,7 +162,7 @@ static void launch_w(const LaunchAttn& a) {
   else if (a.part == 0)
     hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, 0>), dim3(units, splits), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
   else
-    hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, 1>), dim3(units, 1), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
+    hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, 1>), dim3(units, splits), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
 #undef NOSA_ATTN_ARGS
 }
 
