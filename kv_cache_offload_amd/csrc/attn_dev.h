@@ -374,84 +374,6 @@ __device__ void publish_part_ll(const MergeLds<D, WAVES, GMAX>& L, int G, int ti
   }
 }
 
-// The merging workgroup of a unit: its own partial (own, L.M, L.den; part
-// own_part) and the other n_part - 1 records (record s at recs + s *
-// part_record_words, polled until they carry `flag`), normalised and stored.
-// All numerator words are requested at once; the per-head weights come from
-// one 16-lane group per head (lane = part).
-template <class T, int D, int WAVES, int GMAX, int MAXP>
-__device__ void merge_parts_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int n_part, int own_part,
-                               const float (&own)[2], const uint64_t* recs, uint32_t flag, int spin_limit,
-                               int* err, typename T::storage* out_g) {
-  constexpr int REC = part_record_words<D, GMAX>();
-  static_assert(MAXP <= 16, "one 16-lane group per head");
-  __syncthreads();   // merge_waves_keep's reads of L.a are done
-  constexpr int NT = 64 * WAVES;
-  const bool has0 = tid < G * D, has1 = tid + NT < G * D;
-  const uint64_t* base = recs + tid;
-  uint64_t w0[MAXP], w1[MAXP];
-#pragma unroll
-  for (int sp = 0; sp < MAXP; ++sp) {
-    const bool other = sp < n_part && sp != own_part;
-    w0[sp] = other && has0 ? ll_load(base + (size_t)sp * REC) : ll_word(0.f, flag);
-    w1[sp] = other && has1 ? ll_load(base + (size_t)sp * REC + NT) : ll_word(0.f, flag);
-  }
-  if (tid < 16 * GMAX) {
-    const int g = tid >> 4, sp = tid & 15;
-    float m = -INFINITY, l = 0.f;
-    if (g < G && sp < n_part) {
-      if (sp == own_part) {
-        m = L.M[g];
-        l = L.den[g];
-      } else {
-        const uint64_t* pm = recs + (size_t)sp * REC + GMAX * D + 2 * g;
-        uint64_t wm = ll_load(pm), wl = ll_load(pm + 1);
-        wm = ll_wait(pm, wm, flag, spin_limit, err);
-        wl = ll_wait(pm + 1, wl, flag, spin_limit, err);
-        m = ll_float(wm);
-        l = ll_float(wl);
-      }
-    }
-    const float M = group_max<16>(m);
-    const float a = m == -INFINITY ? 0.f : exp2f(m - M);
-    const float den = group_sum<16>(a * l);
-    L.a[g][sp] = den > 0.f ? a / den : 0.f;
-  }
-  {
-    int it = 0;
-    while (true) {
-      bool ok = true;
-#pragma unroll
-      for (int sp = 0; sp < MAXP; ++sp) ok = ok && ll_ok(w0[sp], flag) && ll_ok(w1[sp], flag);
-      if (ok || it >= spin_limit) {
-        if (!ok) atomicAdd(err, 1);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int sp = 0; sp < MAXP; ++sp) {
-        if (!ll_ok(w0[sp], flag)) w0[sp] = ll_load(base + (size_t)sp * REC);
-        if (!ll_ok(w1[sp], flag)) w1[sp] = ll_load(base + (size_t)sp * REC + NT);
-      }
-      ++it;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int idx = tid + r * NT;
-    if (idx >= G * D) continue;
-    const int g = idx / D;
-    float n = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < MAXP; ++sp) {
-      const float v = sp == own_part ? own[r] : ll_float(r ? w1[sp] : w0[sp]);
-      n = fmaf(L.a[g][sp], v, n);
-    }
-    store_out(&out_g[idx], n);
-  }
-}
-
 // A merge workgroup of a unit: outputs [out_lo, out_lo + n_out) (n_out <=
 // 64*WAVES, one per thread) from the unit's n_part flagged records, polled
 // until they carry `flag`; per-head weights from one 16-lane group per head
@@ -517,26 +439,17 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
 
 // The last workgroup of a (b, h): merge the n_split partials in one round
 // trip (split maxima and sums into LDS, numerators into registers), then
-// normalise and store.  Reuses L's merge buffer.  With own_part >= 0 the
-// partial of that split is this workgroup's own, taken from own / own_m /
-// own_l instead of memory.
+// normalise and store.  Reuses L's merge buffer.
 template <class T, int D, int WAVES, int GMAX>
 __device__ void merge_splits(AttnLds<D, WAVES, GMAX>& L, int G, int tid, int n_split,
-                             const float* po, const float* pml, typename T::storage* out_g,
-                             int own_part = -1, const float* own = nullptr,
-                             const float* own_m = nullptr, const float* own_l = nullptr) {
+                             const float* po, const float* pml, typename T::storage* out_g) {
   constexpr int NT = 64 * WAVES;
   constexpr int kMaxSplitRegs = 20;
   float* fm = &L.o[0][0][0];
   float* fl = fm + n_split * G;
   for (int i = tid; i < n_split * G; i += NT) {
-    if (i / G == own_part) {
-      fm[i] = own_m[i % G];
-      fl[i] = own_l[i % G];
-    } else {
-      fm[i] = load_coherent(&pml[2 * i]);
-      fl[i] = load_coherent(&pml[2 * i + 1]);
-    }
+    fm[i] = load_coherent(&pml[2 * i]);
+    fl[i] = load_coherent(&pml[2 * i + 1]);
   }
   constexpr int PER = (GMAX * D + NT - 1) / NT;  // outputs per thread
   float v[PER][kMaxSplitRegs];
@@ -548,9 +461,7 @@ __device__ void merge_splits(AttnLds<D, WAVES, GMAX>& L, int G, int tid, int n_s
       const int g = idx / D, d = idx % D;
 #pragma unroll
       for (int s = 0; s < kMaxSplitRegs; ++s)
-        v[r][s] = (idx < G * D && s < n_split)
-                      ? (s == own_part ? own[r] : load_coherent(&po[((size_t)s * G + g) * D + d]))
-                      : 0.f;
+        v[r][s] = (idx < G * D && s < n_split) ? load_coherent(&po[((size_t)s * G + g) * D + d]) : 0.f;
     }
   }
   __syncthreads();
@@ -579,7 +490,7 @@ __device__ void merge_splits(AttnLds<D, WAVES, GMAX>& L, int G, int tid, int n_s
         if (s < n_split) num += fm[s * G + g] * v[r][s];
     } else {
       for (int s = 0; s < n_split; ++s)
-        num += fm[s * G + g] * (s == own_part ? own[r] : load_coherent(&po[((size_t)s * G + g) * D + d]));
+        num += fm[s * G + g] * load_coherent(&po[((size_t)s * G + g) * D + d]);
     }
     const float den = L.den[g];
     store_out(&out_g[idx], den > 0.f ? num / den : 0.f);
