@@ -567,8 +567,32 @@ def _prefill_leg(torch, NI, R, nb):
     c = int(w.positions()[0]) // 64
     G = w.n_q_heads // w.n_kv_heads
     sel_bytes = units * (n_q * 2 * G * D * 2 + 4 * c * D * 2 + 4 * c)
+    # exact attention of the 64 rows, each over its own selection and window
+    k_cap = w.kq + w.ke
+    out = torch.zeros((w.batch, n_q, w.n_q_heads, D), dtype=torch.bfloat16, device="cuda")
+    wsa = torch.zeros(nb.workspace_size(layer.dims, nb.OP_ATTN, n_q, k_cap, 0), dtype=torch.uint8, device="cuda")
+    attn_us, attn_p10, attn_p90 = timed(lambda: nb.sparse_chunk_attn(layer.dims, qrows, n_q, kv, sel, n_sel, k_cap,
+                                                                     posr, None, out, wsa))
+    torch.cuda.synchronize()
+    # HBM bytes the method must move: every distinct selected block of a KV
+    # head once (the rows' selections overlap: Gamma_e is shared), the window
+    # blocks, q and out; per-row bytes count each row's blocks separately
+    sel_h, n_h = sel.cpu().numpy(), n_sel.cpu().numpy()
+    blk_bytes = 64 * 2 * D * 2
+    distinct = 0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            ids = set()
+            for r in range(n_q):
+                ids.update(int(x) for x in sel_h[b, r, h, : n_h[b, r, h]])
+            distinct += len(ids)
+    windows = units * len({int(p) // 64 for p in w.positions()}) * blk_bytes
+    qo = units * n_q * 2 * G * D * 2
+    attn_bytes = distinct * blk_bytes + windows + qo
+    attn_row_bytes = int(n_h.sum()) * blk_bytes + units * n_q * blk_bytes + qo
     log(f"prefill: pooling {pool_us:.1f} us ({pool_bytes / pool_us / 1e3:.0f} GB/s), "
-        f"selection of {n_q} rows {sel_us:.1f} us")
+        f"selection of {n_q} rows {sel_us:.1f} us, their attention {attn_us:.1f} us "
+        f"({attn_bytes / attn_us / 1e3:.0f} GB/s of distinct blocks)")
     return {
         "workload": "prefill128k", "prompt": n_tok, "query_rows": n_q, "timing": "cold (1 GiB streamed first)",
         "pool_us": round(pool_us, 2), "pool_us_p10_p90": [round(pool_p10, 2), round(pool_p90, 2)],
@@ -576,6 +600,10 @@ def _prefill_leg(torch, NI, R, nb):
         "pool_frac": round(pool_bytes / pool_us / 1e3 / HBM_PEAK_GBPS, 4),
         "select_us": round(sel_us, 2), "select_us_p10_p90": [round(sel_p10, 2), round(sel_p90, 2)],
         "select_bytes": int(sel_bytes),
+        "attn_us": round(attn_us, 2), "attn_us_p10_p90": [round(attn_p10, 2), round(attn_p90, 2)],
+        "attn_bytes": int(attn_bytes), "attn_gbps": round(attn_bytes / attn_us / 1e3, 1),
+        "attn_frac": round(attn_bytes / attn_us / 1e3 / HBM_PEAK_GBPS, 4),
+        "attn_row_bytes": int(attn_row_bytes), "attn_distinct_blocks": distinct,
     }
 
 

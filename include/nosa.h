@@ -283,6 +283,32 @@ int nosa_sparse_decode_attn_pool(const nosa_dims* dims, const void* q, const voi
                                  int32_t part, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * nosa_sparse_chunk_attn -- exact attention for n_query rows of one batch
+ * entry (a prefill chunk), each row over its own selection and its own
+ * causal window, from the resident cache.
+ *
+ * Defined by the same passages as nosa_sparse_decode_attn, per query row:
+ * row r of batch entry b at position p = pos[b][r] attends the blocks
+ * sel[b][r][h][0 .. n_sel[b][r][h]-1] (as written by nosa_select_blocks with
+ * the same n_query) plus tokens 64c .. p of block c = p / 64, read from kv.
+ *
+ *   q        device [B][n_query][Hq][D], cache dtype
+ *   kv       device cache [B][Hkv][NB][block]
+ *   sel, n_sel  device int32 [B][n_query][Hkv][k_cap], [B][n_query][Hkv]
+ *            (k_cap <= 512); entries outside [0, NB) are skipped
+ *   pos      device int32 [B][n_query]; rows outside [0, NB*64) give zeros
+ *   out      device [B][n_query][Hq][D], cache dtype                (written)
+ *   ws       device workspace of at least
+ *            nosa_workspace_size(dims, NOSA_OP_ATTN, n_query, k_cap, 0) bytes,
+ *            zero-filled once before its first use.
+ * Errors as nosa_sparse_decode_attn; also -1 for n_query < 1 and -2 when
+ * B * n_query * Hkv exceeds 65535.
+ */
+int nosa_sparse_chunk_attn(const nosa_dims* dims, const void* q, int32_t n_query, const void* kv,
+                           const int32_t* sel, const int32_t* n_sel, int32_t k_cap, const int32_t* pos,
+                           float scale, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * nosa_decode_step -- one decode step of a resident cache in one launch:
  * nosa_select_blocks (n_query = 1) followed by nosa_sparse_decode_attn over
  * the cache, with the same results.

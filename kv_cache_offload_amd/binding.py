@@ -24,7 +24,7 @@ OP_SELECT, OP_ATTN, OP_STEP = 1, 2, 3
 EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_sparse_decode_attn", "nosa_decode_step", "nosa_workspace_size",
            "nosa_status_str", "nosa_last_error", "nosa_update_pool", "nosa_gather_blocks",
-           "nosa_sparse_decode_attn_pool")
+           "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn")
 
 
 class NosaError(RuntimeError):
@@ -61,13 +61,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_update_pool.argtypes = [D, I32, P, P, P, I32, P, P, I32, P, P, P, P, P]
     lib.nosa_gather_blocks.argtypes = [D, P, P, I32, I32, P, P, P, P]
     lib.nosa_sparse_decode_attn_pool.argtypes = [D, P, P, I32, P, P, I32, P, P, P, I64, I64, P, F, I32, P, P, SZ, P]
+    lib.nosa_sparse_chunk_attn.argtypes = [D, P, I32, P, P, P, I32, P, F, P, P, SZ, P]
     lib.nosa_workspace_size.restype = SZ
     lib.nosa_status_str.argtypes = [I32]
     lib.nosa_status_str.restype = ctypes.c_char_p
     lib.nosa_last_error.argtypes = []
     lib.nosa_last_error.restype = ctypes.c_char_p
     for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
-                 "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool"):
+                 "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool",
+                 "nosa_sparse_chunk_attn"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -163,6 +165,17 @@ def sparse_decode_attn_pool(d: Dims, q, pool, pool_slots: int, phys, n_sel, k_ca
                                              window_head_stride, window_block_stride, _ptr(pos), scale, part,
                                              _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
     _check("nosa_sparse_decode_attn_pool", rc)
+
+
+def sparse_chunk_attn(d: Dims, q, n_query: int, kv, sel, n_sel, k_cap: int, pos, scale: Optional[float], out, ws,
+                      ws_bytes: Optional[int] = None, stream=None) -> None:
+    if scale is None:
+        scale = 1.0 / math.sqrt(d.head_dim)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = load().nosa_sparse_chunk_attn(ctypes.byref(d), _ptr(q), n_query, _ptr(kv), _ptr(sel), _ptr(n_sel), k_cap,
+                                       _ptr(pos), scale, _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+    _check("nosa_sparse_chunk_attn", rc)
 
 
 def sparse_decode_attn(d: Dims, q, blocks, blocks_per_head: int, phys, n_sel, k_cap: int,

@@ -35,8 +35,8 @@ namespace nosa {
 static inline int attn_waves(int G) { return G <= 8 ? 8 : 4; }
 static inline int attn_splits(int k_cap, int G) { return (k_cap + 1 + attn_waves(G) - 1) / attn_waves(G); }
 
-size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap) {
-  const size_t units = (size_t)batch * n_kv_heads;
+size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap, int n_query) {
+  const size_t units = (size_t)batch * n_query * n_kv_heads;
   const size_t G = n_q_heads / n_kv_heads;
   const size_t splits = 2 * attn_splits(k_cap, (int)G);   // both parts of a pool step
   return align256(units * sizeof(int32_t)) + align256(units * splits * G * 2 * sizeof(float)) +
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     int64_t win_block_stride, const int32_t* __restrict__ pos, float scale_log2, int n_q_heads,
     int n_kv_heads, int nb, typename T::storage* __restrict__ out, int32_t* __restrict__ ticket,
     float* __restrict__ part_ml, float* __restrict__ part_o, const int32_t* __restrict__ miss_list,
-    const int32_t* __restrict__ n_miss_p, int n_split_main) {
+    const int32_t* __restrict__ n_miss_p, int n_split_main, int n_query) {
   constexpr int ND = D / 16;
   const int G = n_q_heads / n_kv_heads;
   // grid (units, splits): workgroups are dispatched x-fastest, so every
@@ -74,13 +74,18 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   // splits (often just the window) go last
   const int n_split = PART < 0 ? (int)gridDim.y : 2 * n_split_main;   // partial slots per unit
   const int split = PART == 1 ? n_split_main + (int)blockIdx.y : (int)blockIdx.y;
-  const int unit = blockIdx.x;  // b * Hkv + h
-  const int b = unit / n_kv_heads;
+  // a unit is one query row of one KV head: unit = (b * n_query + r) * Hkv + h
+  // (q, pos, phys / n_sel, out, the ticket and the partials are per unit);
+  // the rows of batch entry b share its cache (cache unit b * Hkv + h)
+  const int unit = blockIdx.x;
   const int h = unit % n_kv_heads;
+  const int br = unit / n_kv_heads;                 // b * n_query + r
+  const int b = br / n_query;
+  const int cunit = b * n_kv_heads + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t blk_elems = (size_t)2 * kBlock * D;
 
-  const int p = pos[b];
+  const int p = pos[br];
   const bool valid_pos = (p >= 0 && p < nb * kBlock);
   const int c = valid_pos ? p / kBlock : 0;
   int ns = valid_pos ? n_sel[unit] : -1;
@@ -92,7 +97,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   f32x4 o[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const typename T::storage* q_group = q + ((size_t)b * n_q_heads + (size_t)h * G) * D;
+  const typename T::storage* q_group = q + ((size_t)br * n_q_heads + (size_t)h * G) * D;
   const int32_t* ml = miss_list + (size_t)unit * (k_cap + 1) * 2;
   int nm = 0;
   if (PART >= 0) {
@@ -110,18 +115,18 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
       bool take = pb >= 0 && pb < blocks_per_head;
       if (PART >= 0 && take) take = slot_fetched(pb, ml, nm, k_cap) == (PART == 1);
       if (take) {
-        blk = blocks + ((size_t)unit * blocks_per_head + pb) * blk_elems;
+        blk = blocks + ((size_t)cunit * blocks_per_head + pb) * blk_elems;
         len = kBlock;
       }
     } else if (e < n_ent && PART != 1) {
-      blk = window_kv + (int64_t)unit * win_head_stride + (int64_t)c * win_block_stride;
+      blk = window_kv + (int64_t)cunit * win_head_stride + (int64_t)c * win_block_stride;
       len = p - c * kBlock + 1;
     }
     if (blk != nullptr) attend_block<T, D>(q_group, G, blk, len, scale_log2, lane, m_run, l_run, o);
   }
 
   __shared__ AttnLds<D, WAVES, GMAX> L;
-  typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
+  typename T::storage* out_g = out + ((size_t)br * n_q_heads + (size_t)h * G) * D;
   float* pml = part_ml + (size_t)unit * n_split * G * 2;
   float* po = part_o + (size_t)unit * n_split * G * D;
   merge_waves<T, D, WAVES, GMAX>(L, m_run, l_run, o, G, tid, split, n_split, out_g, po, pml);
@@ -143,7 +148,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
 
 template <class T, int D, int WAVES, int GMAX>
 static void launch_w(const LaunchAttn& a) {
-  const int units = a.batch * a.n_kv_heads;
+  const int units = a.batch * a.n_query * a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int splits = attn_splits(a.k_cap, G);
   char* ws = (char*)a.ws;
@@ -156,7 +161,7 @@ static void launch_w(const LaunchAttn& a) {
   a.stream, (const typename T::storage*)a.q, (const typename T::storage*)a.blocks, a.blocks_per_head, a.phys, \
       a.n_sel, a.k_cap, (const typename T::storage*)a.window_kv, a.window_head_stride, a.window_block_stride,  \
       a.pos, scale_log2, a.n_q_heads, a.n_kv_heads, a.nb, (typename T::storage*)a.out, ticket, part_ml,        \
-      part_o, a.miss_list, a.n_miss, splits
+      part_o, a.miss_list, a.n_miss, splits, a.n_query
   if (a.part < 0)
     hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, -1>), dim3(units, splits), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
   else if (a.part == 0)

@@ -199,7 +199,7 @@ int nosa_gather_blocks(const nosa_dims* dims, const void* host_kv, void* pool, i
                       const_cast<int32_t*>(n_miss), stream);
 }
 
-static int sparse_attn(const char* fn, int part, const nosa_dims* dims, const void* q, const void* blocks,
+static int sparse_attn(const char* fn, int part, int n_query, const nosa_dims* dims, const void* q, const void* blocks,
                        int32_t blocks_per_head, const int32_t* phys, const int32_t* n_sel, int32_t k_cap,
                        const int32_t* miss_list, const int32_t* n_miss, const void* window_kv,
                        int64_t window_head_stride, int64_t window_block_stride, const int32_t* pos, float scale,
@@ -214,9 +214,10 @@ static int sparse_attn(const char* fn, int part, const nosa_dims* dims, const vo
   if (window_head_stride < 0 || window_block_stride < 0)
     return fail(NOSA_ERR_ARG, fn, "window strides must be >= 0");
   if (!(scale == scale)) return fail(NOSA_ERR_ARG, fn, "scale is NaN");
-  if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
-    return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_kv_heads above 65535");
-  const size_t need = nosa_workspace_size(dims, NOSA_OP_ATTN, 1, k_cap, 0);
+  if (n_query < 1) return fail(NOSA_ERR_ARG, fn, "n_query must be >= 1");
+  if ((int64_t)dims->batch * n_query * dims->n_kv_heads > 65535)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_query * n_kv_heads above 65535");
+  const size_t need = nosa_workspace_size(dims, NOSA_OP_ATTN, n_query, k_cap, 0);
   if (ws_bytes < need) return fail(NOSA_ERR_WORKSPACE, fn, "workspace too small");
   nosa::LaunchAttn a{};
   a.bf16 = dims->dtype == NOSA_BF16;
@@ -238,6 +239,7 @@ static int sparse_attn(const char* fn, int part, const nosa_dims* dims, const vo
   a.scale = scale;
   a.out = out;
   a.ws = ws;
+  a.n_query = n_query;
   a.part = part;
   a.miss_list = miss_list;
   a.n_miss = n_miss;
@@ -251,7 +253,7 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
                             int32_t k_cap, const void* window_kv, int64_t window_head_stride,
                             int64_t window_block_stride, const int32_t* pos, float scale, void* out,
                             void* ws, size_t ws_bytes, void* stream) {
-  return sparse_attn("nosa_sparse_decode_attn", -1, dims, q, blocks, blocks_per_head, phys, n_sel, k_cap,
+  return sparse_attn("nosa_sparse_decode_attn", -1, 1, dims, q, blocks, blocks_per_head, phys, n_sel, k_cap,
                      nullptr, nullptr, window_kv, window_head_stride, window_block_stride, pos, scale, out, ws,
                      ws_bytes, stream);
 }
@@ -262,9 +264,20 @@ int nosa_sparse_decode_attn_pool(const nosa_dims* dims, const void* q, const voi
                                  int64_t window_head_stride, int64_t window_block_stride, const int32_t* pos,
                                  float scale, int32_t part, void* out, void* ws, size_t ws_bytes, void* stream) {
   if (part < 0) return fail(NOSA_ERR_ARG, "nosa_sparse_decode_attn_pool", "part must be 0 or 1");
-  return sparse_attn("nosa_sparse_decode_attn_pool", part, dims, q, pool, pool_slots, phys, n_sel, k_cap,
+  return sparse_attn("nosa_sparse_decode_attn_pool", part, 1, dims, q, pool, pool_slots, phys, n_sel, k_cap,
                      miss_list, n_miss, window_kv, window_head_stride, window_block_stride, pos, scale, out, ws,
                      ws_bytes, stream);
+}
+
+int nosa_sparse_chunk_attn(const nosa_dims* dims, const void* q, int32_t n_query, const void* kv,
+                           const int32_t* sel, const int32_t* n_sel, int32_t k_cap, const int32_t* pos, float scale,
+                           void* out, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "nosa_sparse_chunk_attn";
+  if (int rc = check_dims(dims, fn)) return rc;
+  // every row's window is a block of the cache itself
+  const int64_t blk = (int64_t)2 * 64 * dims->head_dim;
+  return sparse_attn(fn, -1, n_query, dims, q, kv, dims->max_blocks, sel, n_sel, k_cap,
+                     nullptr, nullptr, kv, dims->max_blocks * blk, blk, pos, scale, out, ws, ws_bytes, stream);
 }
 
 int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
@@ -316,8 +329,8 @@ size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, i
   if (op == NOSA_OP_SELECT)
     return nosa::select_ws_bytes(dims->batch, n_query, dims->n_kv_heads, dims->max_blocks);
   if (op == NOSA_OP_ATTN)
-    return nosa::attn_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
-                               kq + ke);
+    return nosa::attn_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, kq + ke,
+                               n_query);
   if (op == NOSA_OP_STEP)
     return nosa::step_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
                                dims->max_blocks, kq, ke);

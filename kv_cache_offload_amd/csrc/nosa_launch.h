@@ -74,6 +74,7 @@ struct LaunchAttn {
   float scale;
   void* out;
   void* ws;
+  int n_query;                 // query rows per batch entry (q, pos, phys, out per row)
   int part;                    // -1 whole step; 0 / 1 the two parts of a pool step
   const int32_t* miss_list;    // parts 0 and 1: the fetch's miss list and counts
   const int32_t* n_miss;
@@ -100,7 +101,7 @@ struct LaunchStep {
 
 // Workspace geometry (bytes), shared by the size query and the launchers.
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb);
-size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap);
+size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap, int n_query);
 size_t step_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq, int ke);
 // Dynamic LDS the selection kernel needs for nb candidate blocks.
 size_t select_lds_bytes(int nb);

@@ -176,6 +176,22 @@ def test_split_fetch_and_pool_attention_checks(lib):
     assert e.value.code == nb.ERR_WORKSPACE
 
 
+def test_chunk_attn_checks(lib):
+    d = _d()
+    need = nb.workspace_size(d, nb.OP_ATTN, 8, 64, 0)
+    assert need > nb.workspace_size(d, nb.OP_ATTN, 1, 64, 0)
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_chunk_attn(d, FAKE, 0, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, FAKE, ws_bytes=need, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_chunk_attn(d, FAKE, 8, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, FAKE, ws_bytes=need - 1, stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_chunk_attn(_d(batch=64), FAKE, 1024, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, FAKE,
+                             ws_bytes=1 << 40, stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+
+
 def test_step_checks(lib):
     d = _d()
     need = nb.workspace_size(d, nb.OP_STEP, 1, 16, 48)

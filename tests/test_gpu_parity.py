@@ -452,6 +452,74 @@ def test_select_many_rows_matches_oracle(name, over, n_q, kq, ke):
     assert ties <= 2
 
 
+def _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer):
+    """Select for the n_query rows, then attend each row over its own
+    selection and causal window; every row of every KV head against the
+    oracle's attention over the GPU's selection."""
+    B, n_q = pos_rows.shape
+    k_cap = w.kq + w.ke
+    qd = torch.from_numpy(q_rows).cuda().to(torch.bfloat16)          # [B, n_q, Hq, D]
+    posd = torch.from_numpy(pos_rows.astype(np.int32)).cuda()
+    sel = torch.full((B, n_q, w.n_kv_heads, k_cap), -1, dtype=torch.int32, device="cuda")
+    n_sel = torch.zeros((B, n_q, w.n_kv_heads), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, w.kq, w.ke), dtype=torch.uint8, device="cuda")
+    nb.select_blocks(layer.dims, qd, n_q, posd, layer.k_comp, layer.e_blk, w.kq, w.ke, sel, n_sel, ws)
+    out = torch.zeros((B, n_q, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    wsa = torch.zeros(nb.workspace_size(layer.dims, nb.OP_ATTN, n_q, k_cap, 0), dtype=torch.uint8, device="cuda")
+    nb.sparse_chunk_attn(layer.dims, qd, n_q, kv, sel, n_sel, k_cap, posd, None, out, wsa)
+    sel = sel.cpu().numpy()
+    n_sel = n_sel.cpu().numpy()
+    out = out.float().cpu().numpy()
+    G = w.group
+    err = 0.0
+    for b in range(B):
+        for r in range(n_q):
+            p = int(pos_rows[b, r])
+            for h in range(w.n_kv_heads):
+                S = list(sel[b, r, h, : n_sel[b, r, h]])
+                if not 0 <= p < 64 * w.n_blocks:
+                    assert np.all(out[b, r, h * G:(h + 1) * G] == 0.0)
+                    continue
+                ref = O.round_output(O.sparse_attention(q_rows[b, r, h * G:(h + 1) * G], K[b, h], V[b, h], S, p),
+                                     bf16=True)
+                e = float(np.max(np.abs(out[b, r, h * G:(h + 1) * G] - ref)))
+                assert e <= 2e-2, (b, r, h, e)
+                err = max(err, e)
+    return err
+
+
+def test_chunk_attention_small():
+    """Ragged prompt, two batch entries, 21 rows at scattered positions (one
+    out of range), G = 4, D = 64."""
+    _banner("chunk attention: B=2, 21 rows, D64 G4")
+    T = 64 * 90 + 13
+    w = _w("layer32k", batch=2, prompt_len=T, n_steps=1, head_dim=64, n_q_heads=8, kq=10, ke=14, prefill=True)
+    K, V, lam, _ = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
+    layer.pool_blocks(kv, logits, 0, T // 64)
+    rng = np.random.default_rng(17)
+    q_rows = NI.round_to_bf16(rng.standard_normal((w.batch, 21, w.n_q_heads, w.head_dim)).astype(np.float32))
+    pos_rows = rng.integers(0, T, size=(w.batch, 21))
+    pos_rows[1, 3] = -1
+    pos_rows[0, 5] = 63
+    _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer)
+
+
+def test_prefill128k_chunk_attention():
+    """The prefill128k workload at full size: 64 query rows at the end of the
+    131072-token prompt, each over its own selection and window."""
+    _banner("prefill128k: selection and attention for 64 query rows")
+    w = NI.WORKLOADS["prefill128k"]
+    K, V, lam, q = NI.layer_inputs(w)                                # q: [64, 1, 16, 128]
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, q)
+    layer = R.DecodeLayer(1, 16, 2, 128, w.n_blocks, "bf16", w.kq, w.ke)
+    layer.pool_blocks(kv, logits, 0, w.n_blocks)
+    q_rows = np.ascontiguousarray(q.transpose(1, 0, 2, 3))           # [B, n_query, Hq, D]
+    pos_rows = w.positions()[None, :].astype(np.int64)
+    _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer)
+
+
 # ---------------------------------------------------- one-launch decode step
 @pytest.mark.parametrize("wname,over", [
     ("tiny", {}),
