@@ -46,6 +46,9 @@ Readings taken where the pages leave a step open:
       with last_use = t - 1 under the same rule.
 * U14 gamma(t) counted in blocks, window of t-1 counted as held at t-1.
 * U16 several query rows: each row is a decode selection at its own position.
+* U19 eviction head (Eq. 4): per KV head, W1 is D x De and W2 has De
+      entries (the pages give no shapes; De is a parameter), tau = softplus
+      log(1 + e^x); weights fp32; computed here in float64.
 
 Pins: every function here is pinned by a test against something other than
 itself (a library routine, brute force, a closed form or a stated invariant);
@@ -158,6 +161,22 @@ def select_blocks(s_q: Sequence[float], E: Sequence[float], n_cand: int,
     g_q = top_blocks(list(s_q[:n_cand]), kq)
     g_e = top_blocks(list(E[:n_cand]), ke)
     return sorted(g_q), sorted(g_e), sorted(set(g_q) | set(g_e))
+
+
+# --------------------------------------------------------------------------
+# The eviction head of Eq. 4 (montaan summary, "Key Design Components" item 3:
+# s^e_j = tau(v_j W1) W2 with tau the softplus of DMA's design), one KV head;
+# its scores are the logits that O2 pools.
+# --------------------------------------------------------------------------
+def softplus(x: np.ndarray) -> np.ndarray:
+    """log(1 + e^x), without overflow."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def eviction_logits(V: np.ndarray, W1: np.ndarray, W2: np.ndarray) -> np.ndarray:
+    """V [T, D], W1 [D, De], W2 [De] -> s^e [T] (float64)."""
+    h = np.asarray(V, dtype=np.float64) @ np.asarray(W1, dtype=np.float64)
+    return softplus(h) @ np.asarray(W2, dtype=np.float64)
 
 
 # --------------------------------------------------------------------------

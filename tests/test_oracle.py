@@ -287,3 +287,47 @@ def test_pool_replay_invariants():
         assert [resident[b] for b in S] == tr.phys[t]
         assert len(set(resident.values())) == len(resident) <= P
     assert total_misses > 0
+
+
+# ---------------------------------------------------------------- eviction head
+def test_softplus_closed_forms():
+    # log 2 at 0; x + log1p(e^-x) and log1p(e^x) written out with the math module
+    assert O.softplus(0.0) == math.log(2.0)
+    for x in (-40.0, -3.5, -1e-3, 0.7, 5.0, 35.0, 800.0):
+        ref = x + math.log1p(math.exp(-x)) if x > 0 else math.log1p(math.exp(x))
+        assert abs(float(O.softplus(x)) - ref) <= 1e-15 * max(1.0, abs(ref))
+
+
+def test_eviction_head_brute_force():
+    """Eq. 4 term by term in plain Python on a tiny head."""
+    rng = np.random.default_rng(4)
+    T, D, De = 5, 6, 3
+    V = rng.standard_normal((T, D))
+    W1 = rng.standard_normal((D, De))
+    W2 = rng.standard_normal(De)
+    got = O.eviction_logits(V, W1, W2)
+    for t in range(T):
+        s = 0.0
+        for j in range(De):
+            h = sum(V[t, d] * W1[d, j] for d in range(D))
+            s += math.log1p(math.exp(h)) * W2[j] if h < 30 else (h + math.log1p(math.exp(-h))) * W2[j]
+        assert abs(got[t] - s) <= 1e-12 * max(1.0, abs(s))
+
+
+def test_eviction_head_special_weights():
+    rng = np.random.default_rng(5)
+    V = rng.standard_normal((7, 8))
+    W2 = rng.standard_normal(8)
+    # W1 = 0: every token scores log(2) * sum(W2)
+    assert np.allclose(O.eviction_logits(V, np.zeros((8, 8)), W2), math.log(2.0) * W2.sum(), rtol=0, atol=1e-14)
+    # W1 = I, W2 = e_i: the softplus of dimension i
+    for i in (0, 5):
+        e = np.zeros(8)
+        e[i] = 1.0
+        assert np.allclose(O.eviction_logits(V, np.eye(8), e), [math.log1p(math.exp(v)) for v in V[:, i]],
+                           rtol=1e-15, atol=0)
+    # linear in W2
+    Wa, Wb = rng.standard_normal(8), rng.standard_normal(8)
+    W1 = rng.standard_normal((8, 8))
+    assert np.allclose(O.eviction_logits(V, W1, Wa + Wb),
+                       O.eviction_logits(V, W1, Wa) + O.eviction_logits(V, W1, Wb), rtol=1e-12, atol=1e-12)
