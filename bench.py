@@ -275,6 +275,7 @@ def main():
         torch._C._host_emptyCache()          # hand the offload leg's pinned cache back
     if not args.no_prefill:
         result["prefill"] = _prefill_leg(torch, NI, R, nb)
+        result["split_qkv"] = _split_leg(torch, nb)
     if not args.no_stack:
         try:
             result["stack"] = _stack_leg(torch, NI, R)
@@ -604,6 +605,62 @@ def _prefill_leg(torch, NI, R, nb):
         "attn_bytes": int(attn_bytes), "attn_gbps": round(attn_bytes / attn_us / 1e3, 1),
         "attn_frac": round(attn_bytes / attn_us / 1e3 / HBM_PEAK_GBPS, 4),
         "attn_row_bytes": int(attn_row_bytes), "attn_distinct_blocks": distinct,
+    }
+
+
+def _split_leg(torch, nb):
+    """The QKV split with the fused eviction head (nosa_split_qkv), heads as
+    layer32k (16 query / 2 KV heads, D = 128, bf16, eviction hidden size 128):
+    one decode step (8 batch entries x 1 token, graph of 64 launches) and a
+    4096-token chunk of one sequence.  Synthetic rows and weights."""
+    Hq, Hkv, D, De, NB = 16, 2, 128, 128, 513
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    w1 = torch.randn((Hkv, D, De), device="cuda", generator=gen) / math.sqrt(D)
+    w2 = torch.randn((Hkv, De), device="cuda", generator=gen)
+    row = (Hq + 2 * Hkv) * D
+    per_tok = row * 2 + Hq * D * 2 + 2 * Hkv * D * 2 + Hkv * 4     # read the row, write q, k, v, logit
+
+    def run(B, n_tok, graph_reps):
+        d = nb.dims(B, Hq, Hkv, D, NB, "bf16")
+        qkv = torch.randn((B, n_tok, row), device="cuda", generator=gen).to(torch.bfloat16)
+        pos = (torch.arange(n_tok, device="cuda", dtype=torch.int32)[None, :] + 64 * 400).repeat(B, 1)
+        q_out = torch.empty((B, n_tok, Hq, D), dtype=torch.bfloat16, device="cuda")
+        kv = torch.zeros((B, Hkv, NB, 2 * 64 * D), dtype=torch.bfloat16, device="cuda")
+        lg = torch.zeros((B, Hkv, NB * 64), dtype=torch.float32, device="cuda")
+        call = lambda st=None: nb.split_qkv(d, qkv, n_tok, pos, w1, w2, De, q_out, kv, lg, stream=st)
+        call()
+        torch.cuda.synchronize()
+        st = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for _ in range(graph_reps):
+                    call(st)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(st):
+                a.record()
+                g.replay()
+                b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3 / graph_reps)
+        return float(np.median(ts))
+
+    dec_us = run(8, 1, 64)
+    n_chunk = 4096
+    chunk_us = run(1, n_chunk, 8)
+    chunk_bytes = n_chunk * per_tok + Hkv * D * De * 4 + Hkv * De * 4
+    log(f"split_qkv: decode step (8 tokens) {dec_us:.2f} us; {n_chunk}-token chunk {chunk_us:.1f} us "
+        f"({chunk_bytes / chunk_us / 1e3:.0f} GB/s)")
+    return {
+        "heads": [Hq, Hkv], "head_dim": D, "evict_hidden": De, "data": "synthetic rows and weights",
+        "decode_tokens": 8, "decode_us": round(dec_us, 2), "decode_bytes": 8 * per_tok + Hkv * D * De * 4,
+        "chunk_tokens": n_chunk, "chunk_us": round(chunk_us, 2), "chunk_bytes": int(chunk_bytes),
+        "chunk_gbps": round(chunk_bytes / chunk_us / 1e3, 1),
+        "chunk_evict_tflops": round(n_chunk * Hkv * D * De * 2 / chunk_us / 1e6, 3),
     }
 
 

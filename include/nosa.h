@@ -82,6 +82,35 @@ typedef struct nosa_dims {
 } nosa_dims;
 
 /*
+ * nosa_split_qkv -- split one fused QKV projection output per token into the
+ * path's inputs, with the eviction head fused in.
+ *
+ * NOSI fuses the eviction heads with the QKV split into one kernel (montaan
+ * summary, "System Optimization (NOSI)" item 1); the head is Eq. 4 of the
+ * same summary ("Key Design Components" item 3): s^e = softplus(v W1) W2,
+ * one score per KV pair from its value, used as the eviction logit that
+ * nosa_pool_keys averages.  For token t of batch entry b at p = pos[b][t]:
+ *   q_out[b][t] = the query heads;  the key and value rows of every KV head
+ *   h go to block p/64, token p%64, of the cache (fragment format);
+ *   evict_logits[b][h][p] = sum_j softplus(sum_d v[d] W1[h][d][j]) W2[h][j]
+ *   (fp32 products and sums; the order of the sums is the kernel's).
+ *
+ *   qkv           device [B][n_tok][(Hq + 2 Hkv) * D], cache dtype: the
+ *                 query heads, then the key heads, then the value heads
+ *   pos           device int32 [B][n_tok]; tokens outside [0, NB*64) only
+ *                 have their query copied
+ *   w1, w2        device fp32 [Hkv][D][d_e], [Hkv][d_e]  (1 <= d_e <= 512)
+ *   q_out         device [B][n_tok][Hq][D], cache dtype            (written)
+ *   kv            device cache [B][Hkv][NB][block]           (written rows)
+ *   evict_logits  device fp32 [B][Hkv][NB*64]                (written rows)
+ * Errors: -1 for NULL buffers or n_tok outside [1, 65535]; -2 for d_e
+ * outside [1, 512], batch above 65535 or more than 16 KV heads.
+ */
+int nosa_split_qkv(const nosa_dims* dims, const void* qkv, int32_t n_tok, const int32_t* pos,
+                   const float* w1, const float* w2, int32_t d_e, void* q_out, void* kv,
+                   float* evict_logits, void* stream);
+
+/*
  * nosa_pool_keys -- compressed keys and the block eviction score.
  *
  * Defined by the gist.science summary of NOSA ("1. Algorithme : NOSA",

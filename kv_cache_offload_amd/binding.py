@@ -24,7 +24,7 @@ OP_SELECT, OP_ATTN, OP_STEP = 1, 2, 3
 EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_sparse_decode_attn", "nosa_decode_step", "nosa_workspace_size",
            "nosa_status_str", "nosa_last_error", "nosa_update_pool", "nosa_gather_blocks",
-           "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn")
+           "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn", "nosa_split_qkv")
 
 
 class NosaError(RuntimeError):
@@ -62,6 +62,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_gather_blocks.argtypes = [D, P, P, I32, I32, P, P, P, P]
     lib.nosa_sparse_decode_attn_pool.argtypes = [D, P, P, I32, P, P, I32, P, P, P, I64, I64, P, F, I32, P, P, SZ, P]
     lib.nosa_sparse_chunk_attn.argtypes = [D, P, I32, P, P, P, I32, P, F, P, P, SZ, P]
+    lib.nosa_split_qkv.argtypes = [D, P, I32, P, P, P, I32, P, P, P, P]
     lib.nosa_workspace_size.restype = SZ
     lib.nosa_status_str.argtypes = [I32]
     lib.nosa_status_str.restype = ctypes.c_char_p
@@ -69,7 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_last_error.restype = ctypes.c_char_p
     for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
                  "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool",
-                 "nosa_sparse_chunk_attn"):
+                 "nosa_sparse_chunk_attn", "nosa_split_qkv"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -106,6 +107,12 @@ def _check(fn: str, rc: int) -> None:
 
 def workspace_size(d: Dims, op: int, n_query: int, kq: int, ke: int) -> int:
     return int(load().nosa_workspace_size(ctypes.byref(d), op, n_query, kq, ke))
+
+
+def split_qkv(d: Dims, qkv, n_tok: int, pos, w1, w2, d_e: int, q_out, kv, evict_logits, stream=None) -> None:
+    rc = load().nosa_split_qkv(ctypes.byref(d), _ptr(qkv), n_tok, _ptr(pos), _ptr(w1), _ptr(w2), d_e, _ptr(q_out),
+                               _ptr(kv), _ptr(evict_logits), _stream(stream))
+    _check("nosa_split_qkv", rc)
 
 
 def pool_keys(d: Dims, kv, kv_unit_stride: int, kv_block_stride: int, evict_logits,

@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnosa.so")
-SOURCES = ["nosa_api.hip", "pool_keys.hip", "select.hip", "fetch.hip", "attn.hip", "fused.hip"]
+SOURCES = ["nosa_api.hip", "pool_keys.hip", "select.hip", "fetch.hip", "attn.hip", "fused.hip", "qkv.hip"]
 ARCH = "gfx950"
 
 

@@ -280,6 +280,36 @@ int nosa_sparse_chunk_attn(const nosa_dims* dims, const void* q, int32_t n_query
                      nullptr, nullptr, kv, dims->max_blocks * blk, blk, pos, scale, out, ws, ws_bytes, stream);
 }
 
+int nosa_split_qkv(const nosa_dims* dims, const void* qkv, int32_t n_tok, const int32_t* pos, const float* w1,
+                   const float* w2, int32_t d_e, void* q_out, void* kv, float* evict_logits, void* stream) {
+  static const char* fn = "nosa_split_qkv";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (n_tok < 1 || n_tok > 65535) return fail(NOSA_ERR_ARG, fn, "n_tok must be in [1, 65535]");
+  if (dims->batch > 65535) return fail(NOSA_ERR_UNSUPPORTED, fn, "batch above 65535");
+  if (dims->n_kv_heads > 16) return fail(NOSA_ERR_UNSUPPORTED, fn, "more than 16 KV heads");
+  if (d_e < 1 || d_e > 512) return fail(NOSA_ERR_UNSUPPORTED, fn, "d_e must be in [1, 512]");
+  if (!qkv || !pos || !w1 || !w2 || !q_out || !kv || !evict_logits) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  nosa::LaunchQkv a{};
+  a.bf16 = dims->dtype == NOSA_BF16;
+  a.head_dim = dims->head_dim;
+  a.batch = dims->batch;
+  a.n_tok = n_tok;
+  a.n_q_heads = dims->n_q_heads;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.nb = dims->max_blocks;
+  a.d_e = d_e;
+  a.qkv = qkv;
+  a.pos = pos;
+  a.w1 = w1;
+  a.w2 = w2;
+  a.q_out = q_out;
+  a.kv = kv;
+  a.evict_logits = evict_logits;
+  a.stream = (hipStream_t)stream;
+  nosa::launch_qkv(a);
+  return check_launch(fn);
+}
+
 int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
                      const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,
                      int32_t* sel, int32_t* n_sel, void* out, void* ws, size_t ws_bytes, void* stream) {

@@ -81,6 +81,20 @@ struct LaunchAttn {
   hipStream_t stream;
 };
 
+struct LaunchQkv {
+  bool bf16;
+  int head_dim;
+  int batch, n_tok, n_q_heads, n_kv_heads, nb, d_e;
+  const void* qkv;
+  const int32_t* pos;
+  const float* w1;
+  const float* w2;
+  void* q_out;
+  void* kv;
+  float* evict_logits;
+  hipStream_t stream;
+};
+
 struct LaunchStep {
   bool bf16;
   int head_dim;
@@ -110,6 +124,7 @@ void launch_pool_keys(const LaunchPool& a);
 void launch_select(const LaunchSelect& a);
 void launch_fetch(const LaunchFetch& a);
 void launch_attn(const LaunchAttn& a);
+void launch_qkv(const LaunchQkv& a);
 void launch_step(const LaunchStep& a);
 
 }  // namespace nosa

@@ -192,6 +192,23 @@ def test_chunk_attn_checks(lib):
     assert e.value.code == nb.ERR_UNSUPPORTED
 
 
+def test_split_qkv_checks(lib):
+    d = _d()
+    args = lambda n_tok, d_e: (d, FAKE, n_tok, FAKE, FAKE, FAKE, d_e, FAKE, FAKE, FAKE)
+    for n_tok, d_e, code in ((0, 64, nb.ERR_ARG), (8, 0, nb.ERR_UNSUPPORTED), (8, 513, nb.ERR_UNSUPPORTED)):
+        with pytest.raises(nb.NosaError) as e:
+            nb.split_qkv(*args(n_tok, d_e), stream=0)
+        assert e.value.code == code
+    a = list(args(8, 64))
+    a[4] = None                                           # W1 is required
+    with pytest.raises(nb.NosaError) as e:
+        nb.split_qkv(*a, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.split_qkv(_d(n_q_heads=32, n_kv_heads=32), *args(8, 64)[1:], stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+
+
 def test_step_checks(lib):
     d = _d()
     need = nb.workspace_size(d, nb.OP_STEP, 1, 16, 48)

@@ -520,6 +520,66 @@ def test_prefill128k_chunk_attention():
     _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer)
 
 
+SPLIT_CASES = [
+    # name, dtype, D, Hq, Hkv, d_e, B, n_tok, contiguous positions
+    ("bf16 D128 G8 decode", "bf16", 128, 16, 2, 128, 8, 1, False),
+    ("bf16 D64 G4 chunk", "bf16", 64, 8, 2, 48, 2, 70, False),
+    ("f32 D64 G2", "f32", 64, 4, 2, 96, 3, 9, False),
+    ("f32 D128 G4 chunk", "f32", 128, 8, 2, 80, 2, 37, False),
+    ("bf16 D128 G8 prefill chunk", "bf16", 128, 16, 2, 128, 2, 300, True),
+]
+
+
+@pytest.mark.parametrize("name,dtype,D,Hq,Hkv,d_e,B,n_tok,contig", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_qkv_matches_oracle(name, dtype, D, Hq, Hkv, d_e, B, n_tok, contig):
+    """q copied, k and v written into the cache's block format at their
+    positions (bit-exact against packing the same rows), eviction logits
+    against the oracle's Eq. 4 in float64.  Chunks of 16 or more tokens take
+    the 16-tokens-per-workgroup path (ragged last group included)."""
+    _banner(f"split qkv {name}")
+    NB = 12
+    rng = np.random.default_rng(21)
+    row = (Hq + 2 * Hkv) * D
+    qkv = rng.standard_normal((B, n_tok, row)).astype(np.float32)
+    if dtype == "bf16":
+        qkv = NI.round_to_bf16(qkv)
+    if contig:      # a prefill chunk: consecutive positions from an unaligned start
+        pos = np.stack([np.arange(n_tok) + 5 + 64 * b for b in range(B)]).astype(np.int32)
+    else:
+        pos = np.stack([rng.permutation(NB * 64)[:n_tok] for _ in range(B)]).astype(np.int32)
+    if n_tok > 2:
+        pos[0, 1] = -1
+        pos[B - 1, 2] = NB * 64 + 3
+    w1 = (rng.standard_normal((Hkv, D, d_e)) / math.sqrt(D)).astype(np.float32)
+    w2 = rng.standard_normal((Hkv, d_e)).astype(np.float32)
+    tdt = R.torch_dtype(dtype)
+    d = nb.dims(B, Hq, Hkv, D, NB, dtype)
+    q_out = torch.zeros((B, n_tok, Hq, D), dtype=tdt, device="cuda")
+    kv = torch.zeros((B, Hkv, NB, 2 * 64 * D), dtype=tdt, device="cuda")
+    lg = torch.zeros((B, Hkv, NB * 64), dtype=torch.float32, device="cuda")
+    nb.split_qkv(d, torch.from_numpy(qkv).cuda().to(tdt), n_tok, torch.from_numpy(pos).cuda(),
+                 torch.from_numpy(w1).cuda(), torch.from_numpy(w2).cuda(), d_e, q_out, kv, lg)
+    torch.cuda.synchronize()
+    assert np.array_equal(q_out.float().cpu().numpy().reshape(B, n_tok, Hq * D), qkv[:, :, : Hq * D])
+    K = np.zeros((B, Hkv, NB * 64, D), np.float32)
+    V = np.zeros_like(K)
+    ref_lg = np.zeros((B, Hkv, NB * 64), np.float64)
+    for b in range(B):
+        for t in range(n_tok):
+            p = int(pos[b, t])
+            if not 0 <= p < NB * 64:
+                continue
+            for h in range(Hkv):
+                K[b, h, p] = qkv[b, t, (Hq + h) * D:(Hq + h + 1) * D]
+                V[b, h, p] = qkv[b, t, (Hq + Hkv + h) * D:(Hq + Hkv + h + 1) * D]
+                ref_lg[b, h, p] = O.eviction_logits(V[b, h, p][None, :], w1[h], w2[h])[0]
+    want = R.to_device_blocks(K, V, NB, dtype)
+    assert torch.equal(kv.view(torch.int16) if dtype == "bf16" else kv, want.view(torch.int16) if dtype == "bf16" else want)
+    got = lg.cpu().numpy()
+    scale = np.abs(w2).sum() * 4.0
+    assert np.max(np.abs(got - ref_lg)) <= 1e-5 * scale
+
+
 # ---------------------------------------------------- one-launch decode step
 @pytest.mark.parametrize("wname,over", [
     ("tiny", {}),
