@@ -49,6 +49,11 @@ Readings taken where the pages leave a step open:
 * U19 eviction head (Eq. 4): per KV head, W1 is D x De and W2 has De
       entries (the pages give no shapes; De is a parameter), tau = softplus
       log(1 + e^x); weights fp32; computed here in float64.
+* U20 chunk-shared selection (a variant of U16): one selection for all
+      rows of a prefill chunk, scored with the sum over the rows of their
+      summed query heads (U3 applied to the whole chunk); the candidates are
+      the complete blocks before the first row's block; every row attends the
+      shared set plus its own window.
 
 Pins: every function here is pinned by a test against something other than
 itself (a library routine, brute force, a closed form or a stated invariant);
@@ -161,6 +166,21 @@ def select_blocks(s_q: Sequence[float], E: Sequence[float], n_cand: int,
     g_q = top_blocks(list(s_q[:n_cand]), kq)
     g_e = top_blocks(list(E[:n_cand]), ke)
     return sorted(g_q), sorted(g_e), sorted(set(g_q) | set(g_e))
+
+
+def chunk_shared_selection(q_rows: np.ndarray, first_pos: int, kbar: np.ndarray, E: Sequence[float],
+                           kq: int, ke: int) -> Tuple[List[int], List[int], List[int]]:
+    """One Eq. 7 selection for all rows of a prefill chunk (reading U20).
+
+    q_rows: [n_query, G, D] the chunk's query heads of one KV head; first_pos:
+    the first row's position (its block bounds the candidates; a negative
+    position leaves none).  The chunk is one query group: its score is
+    query_block_scores over every row's heads together.
+    """
+    q_rows = np.asarray(q_rows)
+    n_cand = first_pos // BLOCK if first_pos >= 0 else 0
+    s_q = query_block_scores(q_rows.reshape(-1, q_rows.shape[-1]), kbar, n_cand)
+    return select_blocks(s_q, E, n_cand, kq, ke)
 
 
 # --------------------------------------------------------------------------

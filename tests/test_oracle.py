@@ -132,6 +132,64 @@ def test_selection_invariant_to_positive_query_scale():
     assert a == b
 
 
+# -------------------------------------------------- chunk-shared selection (U20)
+def _shared_case(seed, n_query=5, G=2, D=16, n_blk=12):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((64 * (n_blk + 1), D)).astype(np.float32)
+    kbar = O.subblock_key_means(K, False)
+    E = [float(v) for v in rng.standard_normal(n_blk + 1)]
+    q = rng.standard_normal((n_query, G, D)).astype(np.float32)
+    return kbar, E, q
+
+
+def test_shared_selection_of_one_row_is_the_decode_selection():
+    kbar, E, q = _shared_case(1, n_query=1)
+    pos = 64 * 12 + 9
+    want = O.select_blocks(O.query_block_scores(q[0], kbar, 12), E, 12, 3, 2)
+    assert O.chunk_shared_selection(q, pos, kbar, E, 3, 2) == want
+
+
+def test_shared_selection_brute_force():
+    """Scores by explicit loops over rows, heads, dimensions and sub-blocks;
+    the selected Gamma_q must out-rank every other candidate (ties by id)."""
+    kbar, E, q = _shared_case(2)
+    n_cand, kq, ke = 12, 4, 3
+    gq, ge, S = O.chunk_shared_selection(q, 64 * n_cand + 30, kbar, E, kq, ke)
+    score = []
+    for j in range(n_cand):
+        best = None
+        for i in range(4):
+            tot = 0.0
+            for r in range(q.shape[0]):
+                for g in range(q.shape[1]):
+                    for d in range(q.shape[2]):
+                        tot += float(q[r, g, d]) * float(kbar[4 * j + i, d])
+            best = tot if best is None else max(best, tot)
+        score.append(best)
+    assert len(gq) == kq and len(ge) == ke
+    for j in gq:
+        for o in range(n_cand):
+            if o not in gq:
+                assert score[j] > score[o] + 1e-9 or (abs(score[j] - score[o]) <= 1e-9 and j < o)
+    assert ge == sorted(O.top_blocks(E[:n_cand], ke))
+    assert S == sorted(set(gq) | set(ge))
+
+
+def test_shared_selection_ignores_row_order_and_duplication():
+    kbar, E, q = _shared_case(3, n_query=6)
+    pos = 64 * 12
+    base = O.chunk_shared_selection(q, pos, kbar, E, 5, 2)
+    assert O.chunk_shared_selection(q[::-1], pos, kbar, E, 5, 2) == base
+    assert O.chunk_shared_selection(np.concatenate([q, q]), pos, kbar, E, 5, 2) == base
+
+
+def test_shared_selection_candidates_from_the_first_row():
+    kbar, E, q = _shared_case(4, n_query=3)
+    gq, ge, S = O.chunk_shared_selection(q, 64 * 5 + 63, kbar, E, 4, 4)
+    assert max(S) < 5 and len(S) == 5                  # all 5 candidates, fewer than the budget
+    assert O.chunk_shared_selection(q, -1, kbar, E, 4, 4) == ([], [], [])
+
+
 # --------------------------------------------------------------- selection
 def test_selection_fixture():
     for case in _golden("selection_small.json")["cases"]:
