@@ -524,7 +524,8 @@ def _stack_leg(torch, NI, R):
 def _prefill_leg(torch, NI, R, nb):
     """The prefill128k workload: pool the compressed keys and eviction scores of
     a 131072-token prompt, then select for the 64 query rows at its end (each
-    row a decode selection at its own position).  Both timed cold: a 1 GiB
+    row a decode selection at its own position) and attend; then the same
+    with one selection shared by the 64 rows.  All timed cold: a 1 GiB
     scratch buffer is streamed before every timed launch, so neither the keys
     (64 MiB) nor the compressed keys (4 MiB) sit in the 256 MB Infinity Cache."""
     w = NI.WORKLOADS["prefill128k"]
@@ -594,6 +595,17 @@ def _prefill_leg(torch, NI, R, nb):
     log(f"prefill: pooling {pool_us:.1f} us ({pool_bytes / pool_us / 1e3:.0f} GB/s), "
         f"selection of {n_q} rows {sel_us:.1f} us, their attention {attn_us:.1f} us "
         f"({attn_bytes / attn_us / 1e3:.0f} GB/s of distinct blocks)")
+    # the chunk-shared variant: one selection for the 64 rows, each row then
+    # attends it plus its window
+    sh_us, sh_p10, sh_p90 = timed(lambda: nb.select_blocks_shared(layer.dims, qrows, n_q, posr, layer.k_comp,
+                                                                  layer.e_blk, w.kq, w.ke, sel, n_sel, ws))
+    sha_us, sha_p10, sha_p90 = timed(lambda: nb.sparse_chunk_attn(layer.dims, qrows, n_q, kv, sel, n_sel, k_cap,
+                                                                  posr, None, out, wsa))
+    torch.cuda.synchronize()
+    n_sh = n_sel.cpu().numpy()[:, 0, :]                       # one set per (b, h)
+    sha_bytes = int(n_sh.sum()) * blk_bytes + windows + qo
+    log(f"prefill, chunk-shared selection: selection {sh_us:.1f} us, attention {sha_us:.1f} us "
+        f"({sha_bytes / sha_us / 1e3:.0f} GB/s, {int(n_sh.sum())} blocks)")
     return {
         "workload": "prefill128k", "prompt": n_tok, "query_rows": n_q, "timing": "cold (1 GiB streamed first)",
         "pool_us": round(pool_us, 2), "pool_us_p10_p90": [round(pool_p10, 2), round(pool_p90, 2)],
@@ -605,6 +617,10 @@ def _prefill_leg(torch, NI, R, nb):
         "attn_bytes": int(attn_bytes), "attn_gbps": round(attn_bytes / attn_us / 1e3, 1),
         "attn_frac": round(attn_bytes / attn_us / 1e3 / HBM_PEAK_GBPS, 4),
         "attn_row_bytes": int(attn_row_bytes), "attn_distinct_blocks": distinct,
+        "shared": {"select_us": round(sh_us, 2), "select_us_p10_p90": [round(sh_p10, 2), round(sh_p90, 2)],
+                   "attn_us": round(sha_us, 2), "attn_us_p10_p90": [round(sha_p10, 2), round(sha_p90, 2)],
+                   "attn_bytes": sha_bytes, "attn_gbps": round(sha_bytes / sha_us / 1e3, 1),
+                   "blocks": int(n_sh.sum())},
     }
 
 

@@ -179,6 +179,29 @@ int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query,
                        size_t ws_bytes, void* stream);
 
 /*
+ * nosa_select_blocks_shared -- one selection for all n_query rows of a
+ * prefill chunk.
+ *
+ * The same Eq. 7 selection as nosa_select_blocks (same passages), with the
+ * chunk treated as one query group: the G query heads of every row are
+ * summed, as the G heads of one row are.  With c = pos[b][0] / 64 (the first
+ * row's window; the variant is meant for chunks inside one block, as the
+ * rows at the end of a prompt):
+ *   qsum      = sum over rows r and the G heads of KV head h (fp32);
+ *   sigma_s, score_j, Gamma_q, Gamma_e as in nosa_select_blocks over j < c;
+ *   sel[b][r][h][..] = Gamma_q U Gamma_e ascending for every row r, the rest
+ *   -1; n_sel[b][r][h] = its size.
+ * Each row still attends its own window block in nosa_sparse_chunk_attn.
+ * Arguments, layouts and workspace as nosa_select_blocks.
+ * Errors: as nosa_select_blocks, and -2 unless the dtype is bf16 and G is
+ * 1, 2, 4 or 8.
+ */
+int nosa_select_blocks_shared(const nosa_dims* dims, const void* q, int32_t n_query,
+                              const int32_t* pos, const void* k_comp, const float* e_blk,
+                              int32_t kq, int32_t ke, int32_t* sel, int32_t* n_sel, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
  * nosa_fetch_blocks -- keep the selected blocks in a fixed HBM block pool.
  *
  * Defined by the montaan summary ("System Optimization (NOSI)" item 2: KV in

@@ -24,7 +24,8 @@ OP_SELECT, OP_ATTN, OP_STEP = 1, 2, 3
 EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_sparse_decode_attn", "nosa_decode_step", "nosa_workspace_size",
            "nosa_status_str", "nosa_last_error", "nosa_update_pool", "nosa_gather_blocks",
-           "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn", "nosa_split_qkv")
+           "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn", "nosa_split_qkv",
+           "nosa_select_blocks_shared")
 
 
 class NosaError(RuntimeError):
@@ -54,6 +55,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     D = ctypes.POINTER(Dims)
     lib.nosa_pool_keys.argtypes = [D, P, I64, I64, P, I32, I32, P, P, P, P]
     lib.nosa_select_blocks.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
+    lib.nosa_select_blocks_shared.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
     lib.nosa_fetch_blocks.argtypes = [D, P, P, I32, P, P, P, I32, P, P, I32, P, P, P, P, P, P]
     lib.nosa_sparse_decode_attn.argtypes = [D, P, P, I32, P, P, I32, P, I64, I64, P, F, P, P, SZ, P]
     lib.nosa_decode_step.argtypes = [D, P, P, P, P, I32, I32, P, F, P, P, P, P, SZ, P]
@@ -70,7 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_last_error.restype = ctypes.c_char_p
     for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
                  "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool",
-                 "nosa_sparse_chunk_attn", "nosa_split_qkv"):
+                 "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -131,6 +133,16 @@ def select_blocks(d: Dims, q, n_query: int, pos, k_comp, e_blk, kq: int, ke: int
                                    _ptr(e_blk), kq, ke, _ptr(sel), _ptr(n_sel), _ptr(ws), ws_bytes,
                                    _stream(stream))
     _check("nosa_select_blocks", rc)
+
+
+def select_blocks_shared(d: Dims, q, n_query: int, pos, k_comp, e_blk, kq: int, ke: int, sel, n_sel,
+                         ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = load().nosa_select_blocks_shared(ctypes.byref(d), _ptr(q), n_query, _ptr(pos), _ptr(k_comp),
+                                          _ptr(e_blk), kq, ke, _ptr(sel), _ptr(n_sel), _ptr(ws), ws_bytes,
+                                          _stream(stream))
+    _check("nosa_select_blocks_shared", rc)
 
 
 def fetch_blocks(d: Dims, host_kv, pool, pool_slots: int, block_table, slot_block, slot_last_use,

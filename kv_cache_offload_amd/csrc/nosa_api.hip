@@ -128,6 +128,48 @@ int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query, co
   return check_launch(fn);
 }
 
+int nosa_select_blocks_shared(const nosa_dims* dims, const void* q, int32_t n_query, const int32_t* pos,
+                              const void* k_comp, const float* e_blk, int32_t kq, int32_t ke,
+                              int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "nosa_select_blocks_shared";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (n_query < 1) return fail(NOSA_ERR_ARG, fn, "n_query must be >= 1");
+  if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
+  if ((int64_t)kq + ke > 65535) return fail(NOSA_ERR_ARG, fn, "kq + ke above 65535");
+  if (!q || !pos || !k_comp || !e_blk || !n_sel || !ws || (kq + ke > 0 && !sel))
+    return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (dims->dtype != NOSA_BF16) return fail(NOSA_ERR_UNSUPPORTED, fn, "bf16 only");
+  const int G = dims->n_q_heads / dims->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "query heads per KV head must be 1, 2, 4 or 8");
+  if (dims->max_blocks > kMaxSelectBlocks)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "max_blocks above 4096 (256K tokens)");
+  if ((int64_t)dims->batch * n_query * dims->n_kv_heads > 65535)
+    return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_query * n_kv_heads above 65535");
+  const size_t need = nosa_workspace_size(dims, NOSA_OP_SELECT, n_query, kq, ke);
+  if (ws_bytes < need) return fail(NOSA_ERR_WORKSPACE, fn, "workspace too small");
+  nosa::LaunchSelect a{};
+  a.bf16 = true;
+  a.head_dim = dims->head_dim;
+  a.batch = dims->batch;
+  a.n_query = n_query;
+  a.n_q_heads = dims->n_q_heads;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.nb = dims->max_blocks;
+  a.kq = kq;
+  a.ke = ke;
+  a.q = q;
+  a.pos = pos;
+  a.k_comp = k_comp;
+  a.e_blk = e_blk;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.ws = ws;
+  a.stream = (hipStream_t)stream;
+  if (!nosa::launch_select_shared(a)) return fail(NOSA_ERR_UNSUPPORTED, fn, "unsupported shape");
+  return check_launch(fn);
+}
+
 // nosa_fetch_blocks and its two phases (1: tables, 2: gather)
 static int fetch_phases(const char* fn, int phases, const nosa_dims* dims, const void* host_kv, void* pool,
                         int32_t pool_slots, int32_t* block_table, int32_t* slot_block, int32_t* slot_last_use,

@@ -122,6 +122,8 @@ size_t select_lds_bytes(int nb);
 
 void launch_pool_keys(const LaunchPool& a);
 void launch_select(const LaunchSelect& a);
+// chunk-shared selection (bf16; G of 1, 2, 4 or 8); false when unsupported
+bool launch_select_shared(const LaunchSelect& a);
 void launch_fetch(const LaunchFetch& a);
 void launch_attn(const LaunchAttn& a);
 void launch_qkv(const LaunchQkv& a);

@@ -32,7 +32,10 @@ constexpr int kHalf = kSelThreads / 2;
 
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb) {
   const size_t rows = (size_t)batch * n_query * n_kv_heads;
-  return align256(rows * sizeof(int32_t)) + align256(rows * (size_t)nb * sizeof(float));
+  // tickets, scores per row and block, and (chunk-shared selection) 16
+  // partial sums of the query heads, up to 128 fp32 dimensions, per unit
+  return align256(rows * sizeof(int32_t)) + align256(rows * (size_t)nb * sizeof(float)) +
+         align256((size_t)16 * batch * n_kv_heads * 128 * sizeof(float));
 }
 
 size_t select_lds_bytes(int nb) {
@@ -293,6 +296,191 @@ static bool launch_multi(const LaunchSelect& a) {
   }
   hipLaunchKernelGGL((mtopk_kernel<Bf16>), dim3(rows), dim3(kMThreads), select_lds_bytes(a.nb), a.stream, a.pos,
                      a.e_blk, score, a.n_query, a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-shared selection: one selection for all n_query rows of a unit,
+// scored with the sum of every row's G query heads.
+//   qsum_kernel         grid (kQsumParts, units): part z sums, in fp32, its
+//                       share of the unit's n_query*G query heads (each
+//                       thread 8 dimensions of every 32nd head of the share,
+//                       in head order, then the thread sums added in order);
+//   shared_scan_kernel  grid (splits, units): adds the kQsumParts partial
+//                       sums in order, then each 16-lane group (8 for D = 64)
+//                       dots one sub-block row of K-bar with the summed query
+//                       (fp32 FMAs, DPP sum); a block's score is the max of
+//                       its four rows;
+//   mtopk_shared_kernel one workgroup per unit: top-kq / top-ke over the
+//                       first row's candidates, the union written to every row.
+constexpr int kQsumThreads = 512;
+constexpr int kQsumParts = 16;                     // workgroups per unit summing the chunk's query heads
+static_assert(kMThreads == 512, "the shared kernels use 512-thread workgroups");
+
+template <int D>
+__global__ void __launch_bounds__(kQsumThreads) qsum_kernel(const uint16_t* __restrict__ q, int n_query, int n_q_heads,
+                                                            int n_kv_heads, float* __restrict__ qsum) {
+  constexpr int CPR = D / 8;                       // 16-byte chunks per head
+  constexpr int SLOTS = kQsumThreads / CPR;        // heads summed side by side
+  __shared__ float s_part[SLOTS][D];
+  const int z = blockIdx.x, unit = blockIdx.y, b = unit / n_kv_heads, h = unit % n_kv_heads;
+  const int G = n_q_heads / n_kv_heads, n_heads = n_query * G;
+  const int per = (n_heads + kQsumParts - 1) / kQsumParts;
+  const int i_lo = z * per, i_hi = min(n_heads, i_lo + per);
+  const int ch = threadIdx.x % CPR, slot = threadIdx.x / CPR;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int i = i_lo + slot; i < i_hi; i += SLOTS) {   // head i: row i / G, head h*G + i % G
+    const int r = i / G, g = i % G;
+    float v[8];
+    unpack16(ld16(q + (((size_t)b * n_query + r) * n_q_heads + h * G + g) * D + 8 * ch), v, Bf16{});
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_part[slot][8 * ch + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.f;
+    for (int k = 0; k < SLOTS; ++k) t += s_part[k][threadIdx.x];
+    qsum[((size_t)z * gridDim.y + unit) * D + threadIdx.x] = t;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kMThreads) shared_scan_kernel(const int32_t* __restrict__ pos,
+                                                                const uint16_t* __restrict__ k_comp,
+                                                                const float* __restrict__ qsum, int n_query,
+                                                                int n_kv_heads, int nb, float* __restrict__ score) {
+  constexpr int LPR = D / 8;                       // lanes per sub-block row, 8 dimensions each
+  constexpr int BPW = 64 / (LPR * kSubsPerBlock);  // blocks per wavefront load (1 or 2)
+  constexpr int WAVES = kMThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int unit = blockIdx.y, b = unit / n_kv_heads;
+  const int p = pos[(size_t)b * n_query];          // the first row's window bounds the candidates
+  const int c = (p >= 0 && p < nb * kBlock) ? p / kBlock : 0;
+  const int bps = (nb + gridDim.x - 1) / gridDim.x;
+  const int blk_lo = min(c, (int)blockIdx.x * bps), blk_hi = min(c, blk_lo + bps);
+  if (blk_lo >= blk_hi) return;
+  const int ch = lane % LPR, rw = lane / LPR;      // dimensions 8ch.. of row rw of a load
+  float qv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  {
+    float4 x[kQsumParts][2];
+#pragma unroll
+    for (int z = 0; z < kQsumParts; ++z) {
+      const float* src = qsum + ((size_t)z * gridDim.y + unit) * D + 8 * ch;
+      x[z][0] = *reinterpret_cast<const float4*>(src);
+      x[z][1] = *reinterpret_cast<const float4*>(src + 4);
+    }
+#pragma unroll
+    for (int z = 0; z < kQsumParts; ++z) {         // the parts in order
+      qv[0] += x[z][0].x; qv[1] += x[z][0].y; qv[2] += x[z][0].z; qv[3] += x[z][0].w;
+      qv[4] += x[z][1].x; qv[5] += x[z][1].y; qv[6] += x[z][1].z; qv[7] += x[z][1].w;
+    }
+  }
+  const uint16_t* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D;
+  constexpr int U = 4;                             // loads in flight per lane
+  constexpr int STEP = WAVES * BPW;
+  for (int jb = blk_lo + wave * BPW; jb < blk_hi; jb += STEP * U) {      // uniform over the wavefront
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {                  // rows clamped, results past blk_hi dropped
+      const int row = min(kSubsPerBlock * (jb + u * STEP) + rw, kSubsPerBlock * blk_hi - 1);
+      raw[u] = ld16(kc + (size_t)row * D + 8 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j0 = jb + u * STEP;
+      float v[8];
+      unpack16(raw[u], v, Bf16{});
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qv[e], v[e], d);
+      d = group_sum<LPR>(d);                       // the row's score in every lane of its group
+#pragma unroll
+      for (int bi = 0; bi < BPW; ++bi) {
+        float m = lane_value(d, 4 * bi * LPR);
+#pragma unroll
+        for (int i = 1; i < kSubsPerBlock; ++i) m = fmaxf(m, lane_value(d, (4 * bi + i) * LPR));
+        if (lane == 0 && j0 + bi < blk_hi) score[(size_t)unit * nb + j0 + bi] = m;
+      }
+    }
+  }
+}
+
+// One workgroup per unit (b, h): the shared selection of all n_query rows.
+__global__ void __launch_bounds__(kMThreads) mtopk_shared_kernel(const int32_t* __restrict__ pos,
+                                                                 const float* __restrict__ e_blk,
+                                                                 const float* __restrict__ score, int n_query,
+                                                                 int n_kv_heads, int nb, int kq, int ke,
+                                                                 int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
+  constexpr int kH = kMThreads / 2;
+  const int unit = blockIdx.x;              // b * Hkv + h
+  const int b = unit / n_kv_heads, h = unit % n_kv_heads;
+  const int tid = threadIdx.x;
+  const int k_cap = kq + ke;
+  const int p = pos[(size_t)b * n_query];
+  const int c = (p >= 0 && p < nb * kBlock) ? p / kBlock : 0;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const size_t kb = align256((size_t)nb * 4), lb = align256((size_t)nb * 2);
+  uint32_t* key_q = reinterpret_cast<uint32_t*>(lds);
+  uint32_t* key_e = reinterpret_cast<uint32_t*>(lds + kb);
+  uint16_t* blist_q = reinterpret_cast<uint16_t*>(lds + 2 * kb);
+  uint16_t* blist_e = reinterpret_cast<uint16_t*>(lds + 2 * kb + lb);
+  uint8_t* flag_q = lds + 2 * kb + 2 * lb;
+  uint8_t* flag_e = flag_q + align256((size_t)nb);
+  __shared__ int s_hist[2][kBins];
+  __shared__ int s_small[2][32];
+  __shared__ int s_wsum[kMThreads / 64];
+  const float* sc = score + (size_t)unit * nb;
+  const float* eb = e_blk + (size_t)unit * nb;
+  for (int j = tid; j < c; j += kMThreads) {
+    key_q[j] = orderable(sc[j]);
+    key_e[j] = orderable(eb[j]);
+    flag_q[j] = 0;
+    flag_e[j] = 0;
+  }
+  __syncthreads();
+  const int half = tid / kH;
+  select_top<kH>(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, s_hist[half], s_small[half],
+                 half ? blist_e : blist_q, tid % kH);
+  // the union goes to LDS first, over the dead score keys (write_union
+  // writes only after its own barrier, when every top-k pass is done; it has
+  // at most min(k_cap, c) <= nb members)
+  int32_t* s_list = reinterpret_cast<int32_t*>(key_q);
+  const int total = write_union<kMThreads>(flag_q, flag_e, c, s_list, min(k_cap, nb), s_wsum, tid);
+  __syncthreads();
+  for (int i = tid; i < n_query * k_cap; i += kMThreads) {
+    const int r = i / k_cap, k = i % k_cap;
+    sel[(((size_t)b * n_query + r) * n_kv_heads + h) * k_cap + k] = k < total ? s_list[k] : -1;
+  }
+  for (int r = tid; r < n_query; r += kMThreads) n_sel[((size_t)b * n_query + r) * n_kv_heads + h] = total;
+}
+
+template <int D>
+static void launch_shared(const LaunchSelect& a) {
+  const int units = a.batch * a.n_kv_heads;
+  const size_t rows = (size_t)a.batch * a.n_query * a.n_kv_heads;
+  char* ws = (char*)a.ws;
+  float* score = (float*)(ws + align256(rows * sizeof(int32_t)));
+  float* qs = (float*)(ws + align256(rows * sizeof(int32_t)) + align256(rows * (size_t)a.nb * sizeof(float)));
+  const uint16_t* q = (const uint16_t*)a.q;
+  hipLaunchKernelGGL((qsum_kernel<D>), dim3(kQsumParts, units), dim3(kQsumThreads), 0, a.stream, q, a.n_query,
+                     a.n_q_heads, a.n_kv_heads, qs);
+  // about 4 blocks per wavefront, at most 512 workgroups in all
+  int splits = (a.nb + 31) / 32;
+  const int cap = 512 / units > 1 ? 512 / units : 1;
+  splits = splits < 1 ? 1 : (splits > cap ? cap : splits);
+  hipLaunchKernelGGL((shared_scan_kernel<D>), dim3(splits, units), dim3(kMThreads), 0, a.stream, a.pos,
+                     (const uint16_t*)a.k_comp, qs, a.n_query, a.n_kv_heads, a.nb, score);
+  hipLaunchKernelGGL(mtopk_shared_kernel, dim3(units), dim3(kMThreads), select_lds_bytes(a.nb), a.stream, a.pos,
+                     a.e_blk, score, a.n_query, a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel);
+}
+
+bool launch_select_shared(const LaunchSelect& a) {
+  const int G = a.n_q_heads / a.n_kv_heads;
+  if (!a.bf16 || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
+  if (a.head_dim == 128) launch_shared<128>(a); else launch_shared<64>(a);
   return true;
 }
 

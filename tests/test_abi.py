@@ -107,6 +107,38 @@ def test_select_checks(lib):
     assert e.value.code == nb.ERR_UNSUPPORTED
 
 
+def test_select_shared_checks(lib):
+    """The chunk-shared selection validates like nosa_select_blocks, and
+    rejects fp32 caches and query groups other than 1, 2, 4 or 8 heads."""
+    d = _d()
+    need = nb.workspace_size(d, nb.OP_SELECT, 1, 4, 4)
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks_shared(d, FAKE, 1, FAKE, FAKE, FAKE, 4, 4, FAKE, FAKE, FAKE, need - 1, stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks_shared(d, FAKE, 0, FAKE, FAKE, FAKE, 4, 4, FAKE, FAKE, FAKE, need, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks_shared(_d(dtype=nb.F32), FAKE, 8, FAKE, FAKE, FAKE, 4, 4, FAKE, FAKE, FAKE, 1 << 40,
+                                stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks_shared(_d(n_q_heads=24, n_kv_heads=2), FAKE, 8, FAKE, FAKE, FAKE, 4, 4, FAKE, FAKE,
+                                FAKE, 1 << 40, stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+
+
+def test_select_workspace_covers_shared_selection(lib):
+    """The selection workspace also holds what the chunk-shared selection
+    keeps there: one score per (unit, block) and 16 partial query sums of up
+    to 128 fp32 dimensions per unit, after the per-row tickets."""
+    for n_query in (1, 2, 9, 64):
+        d = _d(max_blocks=2048)
+        need = nb.workspace_size(d, nb.OP_SELECT, n_query, 16, 48)
+        units = d.batch * d.n_kv_heads
+        assert need >= units * n_query * 4 + units * 2048 * 4 + 16 * units * 128 * 4
+
+
 def test_fetch_checks(lib):
     d = _d()
     args = lambda P, k: (d, FAKE, FAKE, P, FAKE, FAKE, FAKE, 0, FAKE, FAKE, k, None, None, FAKE, FAKE, FAKE)

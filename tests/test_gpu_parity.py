@@ -452,6 +452,66 @@ def test_select_many_rows_matches_oracle(name, over, n_q, kq, ke):
     assert ties <= 2
 
 
+SHARED_CASES = [
+    # name, workload overrides, n_query, kq, ke, first row's position in batch entry 0 / 1
+    ("D128 G8 64 rows", dict(), 64, 16, 48, (64 * 639, 64 * 500)),
+    ("D64 G4 13 rows", dict(head_dim=64, n_q_heads=8), 13, 12, 20, (64 * 600 + 40, 64 * 3 + 1)),
+    ("D128 G1 3 rows", dict(n_q_heads=2), 3, 8, 8, (64 * 100 + 7, 64 * 639 + 61)),
+    ("D64 G2 1 row kq only", dict(head_dim=64, n_q_heads=4), 1, 30, 0, (64 * 200, 64 * 10)),
+]
+
+
+@pytest.mark.parametrize("name,over,n_q,kq,ke,starts", SHARED_CASES, ids=[c[0] for c in SHARED_CASES])
+def test_select_shared_matches_oracle(name, over, n_q, kq, ke, starts):
+    """One selection per (b, h) for all rows of a chunk (reading U20), written
+    to every row, against the oracle; then each row's exact attention over it
+    plus the row's own window."""
+    _banner(f"chunk-shared selection {name}")
+    T = 64 * 640 + 11
+    w = _w("layer32k", batch=2, prompt_len=T, n_steps=1, kq=kq, ke=ke, prefill=True, **over)
+    K, V, lam, _ = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, kq, ke)
+    layer.pool_blocks(kv, logits, 0, T // 64)
+    rng = np.random.default_rng(23)
+    qn = NI.round_to_bf16(rng.standard_normal((w.batch, n_q, w.n_q_heads, w.head_dim)).astype(np.float32))
+    posn = np.stack([np.arange(n_q) + s for s in starts]).astype(np.int32)   # rows inside one block
+    assert np.all(posn // 64 == posn[:, :1] // 64) and posn.max() < T
+    qd = torch.from_numpy(qn).cuda().to(torch.bfloat16)
+    posd = torch.from_numpy(posn).cuda()
+    k_cap = kq + ke
+    sel = torch.full((w.batch, n_q, w.n_kv_heads, k_cap), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((w.batch, n_q, w.n_kv_heads), -7, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, kq, ke), dtype=torch.uint8, device="cuda")
+    nb.select_blocks_shared(layer.dims, qd, n_q, posd, layer.k_comp, layer.e_blk, kq, ke, sel, n_sel, ws)
+    out = torch.zeros((w.batch, n_q, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    wsa = torch.zeros(nb.workspace_size(layer.dims, nb.OP_ATTN, n_q, k_cap, 0), dtype=torch.uint8, device="cuda")
+    nb.sparse_chunk_attn(layer.dims, qd, n_q, kv, sel, n_sel, k_cap, posd, None, out, wsa)
+    sel = sel.cpu().numpy()
+    n_sel = n_sel.cpu().numpy()
+    out = out.float().cpu().numpy()
+    G, D = w.group, w.head_dim
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            kbar = O.subblock_key_means(K[b, h], bf16=True)
+            E = O.block_eviction_scores(O.subblock_logit_means(lam[b, h]))
+            q_chunk = qn[b, :, h * G:(h + 1) * G]
+            c = int(posn[b, 0]) // 64
+            _, _, S = O.chunk_shared_selection(q_chunk, int(posn[b, 0]), kbar, E, kq, ke)
+            got = list(sel[b, 0, h, : n_sel[b, 0, h]])
+            for r in range(n_q):                        # the same set in every row, -1 after it
+                assert n_sel[b, r, h] == len(got) and list(sel[b, r, h, : len(got)]) == got, (b, r, h)
+                assert np.all(sel[b, r, h, len(got):] == -1), (b, r, h)
+            if got != S:
+                s_q = O.query_block_scores(q_chunk.reshape(-1, D), kbar, c)
+                assert H.selection_ok(got, s_q, E, c, kq, ke), (b, h, got, S)
+            for r in range(n_q):
+                ref = O.round_output(O.sparse_attention(q_chunk[r], K[b, h], V[b, h], got, int(posn[b, r])),
+                                     bf16=True)
+                e = float(np.max(np.abs(out[b, r, h * G:(h + 1) * G] - ref)))
+                assert e <= 2e-2, (b, r, h, e)
+
+
 def _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer):
     """Select for the n_query rows, then attend each row over its own
     selection and causal window; every row of every KV head against the
@@ -518,6 +578,48 @@ def test_prefill128k_chunk_attention():
     q_rows = np.ascontiguousarray(q.transpose(1, 0, 2, 3))           # [B, n_query, Hq, D]
     pos_rows = w.positions()[None, :].astype(np.int64)
     _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer)
+
+
+def test_prefill128k_shared_selection():
+    """prefill128k at full size: one shared selection for the 64 rows at the
+    end of the 131072-token prompt (block 2047), and their attention over it;
+    every selection and a sample of rows against the oracle."""
+    _banner("prefill128k: chunk-shared selection and attention, 64 rows")
+    w = NI.WORKLOADS["prefill128k"]
+    K, V, lam, q = NI.layer_inputs(w)                                # q: [64, 1, 16, 128]
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, q)
+    layer = R.DecodeLayer(1, 16, 2, 128, w.n_blocks, "bf16", w.kq, w.ke)
+    layer.pool_blocks(kv, logits, 0, w.n_blocks)
+    q_rows = np.ascontiguousarray(q.transpose(1, 0, 2, 3))           # [1, 64, 16, 128]
+    pos_rows = w.positions()[None, :].astype(np.int32)
+    n_q, k_cap = pos_rows.shape[1], w.kq + w.ke
+    qd = torch.from_numpy(q_rows).cuda().to(torch.bfloat16)
+    posd = torch.from_numpy(pos_rows).cuda()
+    sel = torch.full((1, n_q, 2, k_cap), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.zeros((1, n_q, 2), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, w.kq, w.ke), dtype=torch.uint8, device="cuda")
+    nb.select_blocks_shared(layer.dims, qd, n_q, posd, layer.k_comp, layer.e_blk, w.kq, w.ke, sel, n_sel, ws)
+    out = torch.zeros((1, n_q, 16, 128), dtype=torch.bfloat16, device="cuda")
+    wsa = torch.zeros(nb.workspace_size(layer.dims, nb.OP_ATTN, n_q, k_cap, 0), dtype=torch.uint8, device="cuda")
+    nb.sparse_chunk_attn(layer.dims, qd, n_q, kv, sel, n_sel, k_cap, posd, None, out, wsa)
+    sel = sel.cpu().numpy()
+    n_sel = n_sel.cpu().numpy()
+    out = out.float().cpu().numpy()
+    c = int(pos_rows[0, 0]) // 64
+    for h in range(2):
+        kbar = O.subblock_key_means(K[0, h], bf16=True)
+        E = O.block_eviction_scores(O.subblock_logit_means(lam[0, h]))
+        q_chunk = q_rows[0, :, h * 8:(h + 1) * 8]
+        _, _, S = O.chunk_shared_selection(q_chunk, int(pos_rows[0, 0]), kbar, E, w.kq, w.ke)
+        got = list(sel[0, 0, h, : n_sel[0, 0, h]])
+        assert all(list(sel[0, r, h, : n_sel[0, r, h]]) == got for r in range(n_q))
+        if got != S:
+            s_q = O.query_block_scores(q_chunk.reshape(-1, 128), kbar, c)
+            assert H.selection_ok(got, s_q, E, c, w.kq, w.ke), (h, got, S)
+        for r in (0, 1, 31, 62, 63):
+            ref = O.round_output(O.sparse_attention(q_chunk[r], K[0, h], V[0, h], got, int(pos_rows[0, r])),
+                                 bf16=True)
+            assert float(np.max(np.abs(out[0, r, h * 8:(h + 1) * 8] - ref))) <= 2e-2, (h, r)
 
 
 SPLIT_CASES = [
