@@ -689,7 +689,8 @@ def test_split_qkv_matches_oracle(name, dtype, D, Hq, Hkv, d_e, B, n_tok, contig
     ("layer32k", dict(batch=2, prompt_len=64 * 200 + 7, n_steps=70, kq=5, ke=0)),
     ("layer32k", dict(batch=2, prompt_len=64 * 30 + 60, n_steps=10, kq=0, ke=9, head_dim=64, n_q_heads=4)),
     ("layer32k", dict(batch=2, prompt_len=64 * 10 + 5, n_steps=70)),          # fewer candidates than kq
-], ids=["tiny", "boundaries", "kq-only", "ke-only-D64", "short-context"])
+    ("layer32k", dict(batch=2, prompt_len=5, n_steps=70)),                    # no candidates, then one
+], ids=["tiny", "boundaries", "kq-only", "ke-only-D64", "short-context", "first-block"])
 def test_fused_step_matches_oracle(wname, over):
     _banner(f"fused step {wname} {over}")
     w = NI.scaled(NI.WORKLOADS[wname], **over) if over else NI.WORKLOADS[wname]
@@ -715,6 +716,27 @@ def test_fused_step_layer32k_full():
     for b in range(w.batch):
         for h in range(w.n_kv_heads):
             H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
+
+
+def test_max_size_context_and_budget():
+    """The largest configuration the calls accept: 4096 blocks (a 256K-token
+    context) and k = 256 blocks (kq 64 + ke 192), the last steps of the
+    cache; the one-launch step against the separate calls (identical sets)
+    and against the oracle for every unit and step."""
+    _banner("max size: 4096 blocks, k = 256")
+    w = NI.scaled(NI.WORKLOADS["layer32k"], batch=1, prompt_len=64 * 4096 - 10, n_steps=5, kq=64, ke=192)
+    assert w.n_blocks == 4096
+    K, V, lam, q = NI.layer_inputs(w)
+    s1, n1, o1, layer = H.run_resident(w, K, V, lam, q, fused=True)
+    assert layer.step_timeouts() == 0
+    s2, n2, o2, _ = H.run_resident(w, K, V, lam, q, fused=False)
+    for a, b in zip(n1, n2):
+        assert np.array_equal(a, b)
+    for a, b in zip(s1, s2):
+        assert np.array_equal(a, b)
+    assert all(int(n.max()) > 200 for n in n1)        # kq + ke minus the overlap of the two top-k sets
+    for h in range(w.n_kv_heads):
+        H.compare_unit(w, K, V, lam, q, 0, h, H.unit_selections(s1, n1, 0, h), gpu_out=o1)
 
 
 @pytest.mark.parametrize("batch", [32, 64], ids=["64-units", "128-units"])
