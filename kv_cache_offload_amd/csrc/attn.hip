@@ -35,12 +35,40 @@ namespace nosa {
 static inline int attn_waves(int G) { return G <= 8 ? 8 : 4; }
 static inline int attn_splits(int k_cap, int G) { return (k_cap + 1 + attn_waves(G) - 1) / attn_waves(G); }
 
-size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap, int n_query) {
+// Packed prefill-chunk attention (see chunk_attn_kernel): NR = 16 / G rows
+// per unit for G = 4 or 8 (bf16), 0 when the rows are not packed.
+constexpr int kChunkWaves = 8;
+static inline int chunk_rows(int G) { return (G == 4 || G == 8) ? 16 / G : 0; }
+constexpr int kChunkMaxShare = 2048;                        // union entries per workgroup (nb <= 4096, >= 2 splits)
+struct ChunkGeometry {
+  size_t units, splits, off_ml, off_o, total;
+};
+static ChunkGeometry chunk_geometry(int batch, int n_kv_heads, int head_dim, int n_query, int NR) {
+  ChunkGeometry g{};
+  g.units = (size_t)batch * ((n_query + NR - 1) / NR) * n_kv_heads;
+  // splits per unit: about one workgroup per CU in all, at least 2, at most 8
+  const size_t s = (256 + g.units - 1) / g.units;
+  g.splits = s < 2 ? 2 : (s > 8 ? 8 : s);
+  size_t o = align256(g.units * sizeof(int32_t));           // tickets
+  g.off_ml = o; o += align256(g.units * g.splits * 16 * 2 * sizeof(float));
+  g.off_o = o; o += align256(g.units * g.splits * 16 * (size_t)head_dim * sizeof(float));
+  g.total = o;
+  return g;
+}
+
+size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int k_cap, int n_query) {
+  (void)nb;
   const size_t units = (size_t)batch * n_query * n_kv_heads;
   const size_t G = n_q_heads / n_kv_heads;
   const size_t splits = 2 * attn_splits(k_cap, (int)G);   // both parts of a pool step
-  return align256(units * sizeof(int32_t)) + align256(units * splits * G * 2 * sizeof(float)) +
-         align256(units * splits * G * head_dim * sizeof(float));
+  size_t need = align256(units * sizeof(int32_t)) + align256(units * splits * G * 2 * sizeof(float)) +
+                align256(units * splits * G * head_dim * sizeof(float));
+  const int NR = chunk_rows((int)G);
+  if (n_query > 1 && NR > 0) {
+    const size_t packed = chunk_geometry(batch, n_kv_heads, head_dim, n_query, NR).total;
+    need = need > packed ? need : packed;
+  }
+  return need;
 }
 
 // Whether a pool slot is being filled by this step's fetch (a miss, or the
@@ -146,6 +174,210 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   merge_splits<T, D, WAVES, GMAX>(L, G, tid, n_split, po, pml, out_g);
 }
 
+// ---------------------------------------------------------------------------
+// Prefill-chunk attention with the rows packed into the MFMA columns (bf16,
+// G = 4 or 8): the NR = 16 / G consecutive rows of a unit fill the 16
+// columns of the tiles (column = rr * G + head).  The rows of a chunk select
+// mostly the same blocks (the same Gamma_e whenever they share a window
+// block), so a unit attends the union of its rows' blocks once, every column
+// masked to what its own row attends: its selected blocks whole, its window
+// block up to its position, nothing else.
+//
+// Grid (units, S): every workgroup builds the unit's union in LDS (bit rr of
+// a block: selected by row rr; bit NR + rr: the window of row rr; the marked
+// blocks ranked in ascending order) and takes the S-th share of it; its
+// wavefronts walk their entries, folding each block into a running
+// partial; the wavefronts merge in LDS, the S workgroups through partials,
+// and the last one (ticket) stores every row's heads.
+template <int D>
+__device__ __forceinline__ void load_q_rows(Frags<Bf16, D>& f, const uint16_t* q, int b, int r0, int n_query,
+                                            int n_q_heads, int h, int G, int lane) {
+  const int col = lane & 15, grp = lane >> 4, r = r0 + col / G;
+  const uint16_t* src = q + (((size_t)b * n_query + r) * n_q_heads + (size_t)h * G + col % G) * D;
+#pragma unroll
+  for (int s = 0; s < Frags<Bf16, D>::NK; ++s)
+    f.q[s] = as_bf16x8(r < n_query ? ld16(src + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0));
+}
+
+template <int D, int NR>
+__global__ void __launch_bounds__(64 * kChunkWaves) chunk_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ n_sel, int k_cap, const int32_t* __restrict__ pos, float scale_log2, int n_q_heads,
+    int n_kv_heads, int nb, int n_query, uint16_t* __restrict__ out, int32_t* __restrict__ ticket,
+    float* __restrict__ part_ml, float* __restrict__ part_o) {
+  constexpr int ND = D / 16, WAVES = kChunkWaves, G = 16 / NR, NT = 64 * WAVES;
+  const int u = blockIdx.x, split = blockIdx.y, n_split = gridDim.y;
+  const int n_groups = (n_query + NR - 1) / NR;
+  const int h = u % n_kv_heads, brg = u / n_kv_heads, b = brg / n_groups, r0 = (brg % n_groups) * NR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ AttnLds<D, WAVES, 16> L;
+  __shared__ int s_ent[kChunkMaxShare];
+  __shared__ int s_wsum[WAVES];
+  __shared__ int s_share[2];
+
+  // ---- the union (the block marks live in the merge buffer until the merge)
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(&L.o[0][0][0]);
+  int rp[NR], rn[NR];                              // each row's position and selection count
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    const int r = r0 + rr;
+    rp[rr] = r < n_query ? pos[(size_t)b * n_query + r] : -1;
+    rn[rr] = r < n_query ? n_sel[((size_t)b * n_query + r) * n_kv_heads + h] : 0;
+  }
+  for (int j = tid; j < nb; j += NT) s_mask[j] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    const int p = rp[rr];
+    if (p < 0 || p >= nb * kBlock) continue;       // a row out of range attends nothing
+    const size_t row = ((size_t)b * n_query + r0 + rr) * n_kv_heads + h;
+    const int ns = rn[rr] < 0 ? 0 : (rn[rr] > k_cap ? k_cap : rn[rr]);
+    for (int e = tid; e < ns; e += NT) {
+      const int blk = sel[row * k_cap + e];
+      if (blk >= 0 && blk < nb) atomicOr(&s_mask[blk], 1u << rr);
+    }
+    if (tid == 0) atomicOr(&s_mask[p / kBlock], 1u << (NR + rr));
+  }
+  __syncthreads();
+  {
+    // rank the marked blocks (each thread a run of blocks, a wavefront scan
+    // and the wavefront totals) and keep this workgroup's share
+    const int per = (nb + NT - 1) / NT;
+    const int lo = min(nb, tid * per), hi = min(nb, lo + per);
+    int cnt = 0;
+    for (int j = lo; j < hi; ++j) cnt += s_mask[j] != 0u;
+    const int incl = wave_incl_sum(cnt, lane);
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int off = incl - cnt, total = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      if (w < wave) off += s_wsum[w];
+      total += s_wsum[w];
+    }
+    const int sh_lo = (int)((int64_t)total * split / n_split), sh_hi = (int)((int64_t)total * (split + 1) / n_split);
+    for (int j = lo; j < hi; ++j) {
+      if (s_mask[j] == 0u) continue;
+      if (off >= sh_lo && off < sh_hi) s_ent[off - sh_lo] = j | (int)(s_mask[j] << 16);
+      ++off;
+    }
+    if (tid == 0) s_share[0] = sh_hi - sh_lo;
+  }
+  __syncthreads();
+  const int n_share = min(s_share[0], kChunkMaxShare);
+
+  // ---- the share's blocks, one wavefront each in turn
+  const int rr = (lane & 15) / G;
+  int p = rp[0];                                   // this lane's row's position
+#pragma unroll
+  for (int k = 1; k < NR; ++k)
+    if (rr == k) p = rp[k];
+  const bool valid = p >= 0 && p < nb * kBlock;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Frags<Bf16, D> f;
+  load_q_rows<D>(f, q, b, r0, n_query, n_q_heads, h, G, lane);
+  const uint16_t* unit_kv = kv + (size_t)(b * n_kv_heads + h) * nb * ((size_t)2 * kBlock * D);
+  for (int i = wave; i < n_share; i += WAVES) {
+    const int ent = s_ent[i];
+    const int blk = ent & 0xffff;
+    const uint32_t mask = (uint32_t)ent >> 16;
+    int len = 0;                                   // this lane's column: its row's token count
+    if (valid) {
+      if ((mask >> rr) & 1u) len = kBlock;
+      else if ((mask >> (NR + rr)) & 1u) len = p - blk * kBlock + 1;
+    }
+    load_tiles<Bf16, D, 4>(f, unit_kv + (size_t)blk * ((size_t)2 * kBlock * D), 0, lane);
+    float mb, lb;
+    f32x4 ob[ND];
+    attend_frags<Bf16, D, 4>(f, 0, len, scale_log2, lane, mb, lb, ob);
+    combine_partial<ND>(m_run, l_run, o, mb, lb, ob);
+  }
+  __syncthreads();                                 // the marks are dead: L is the merge buffer again
+  float* pml = part_ml + (size_t)u * n_split * 16 * 2;
+  float* po = part_o + (size_t)u * n_split * 16 * D;
+  merge_waves<Bf16, D, WAVES, 16>(L, m_run, l_run, o, 16, tid, split, n_split, nullptr, po, pml);
+
+  // ---- the last workgroup of the unit merges the S partials
+  __shared__ int s_last;
+  wait_stores_done();
+  __syncthreads();
+  if (tid == 0) {
+    const int t = ticket_take(&ticket[u]);
+    s_last = (t == n_split - 1);
+    if (s_last) ticket_reset(&ticket[u]);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  constexpr int PER = 16 * D / NT;                 // outputs per thread
+  constexpr int kRegSplits = 8;                    // the most splits a launch uses
+  float v[PER][kRegSplits];
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+#pragma unroll
+    for (int sp = 0; sp < kRegSplits; ++sp)
+      v[k][sp] = sp < n_split ? load_coherent(&po[((size_t)sp * 16 + (tid + k * NT) / D) * D + (tid + k * NT) % D])
+                              : 0.f;
+  float* fw = &L.o[0][0][0];                       // split weights [split][column]
+  float* fl = fw + n_split * 16;
+  for (int i = tid; i < n_split * 16; i += NT) {
+    fw[i] = load_coherent(&pml[2 * i]);
+    fl[i] = load_coherent(&pml[2 * i + 1]);
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, fw[sp * 16 + tid]);
+    float den = 0.f;
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float ms = fw[sp * 16 + tid];
+      const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      fw[sp * 16 + tid] = wt;
+      den += wt * fl[sp * 16 + tid];
+    }
+    L.den[tid] = den;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = tid + k * NT, col = idx / D, d = idx % D, rw = r0 + col / G;
+    float num = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kRegSplits; ++sp) num += (sp < n_split ? fw[sp * 16 + col] : 0.f) * v[k][sp];
+    if (rw >= n_query) continue;
+    const float den = L.den[col];
+    store_out(&out[(((size_t)b * n_query + rw) * n_q_heads + (size_t)h * G + col % G) * D + d],
+              den > 0.f ? num / den : 0.f);
+  }
+}
+
+template <int D, int NR>
+static void launch_chunk(const LaunchAttn& a) {
+  const ChunkGeometry g = chunk_geometry(a.batch, a.n_kv_heads, D, a.n_query, NR);
+  char* ws = (char*)a.ws;
+  int32_t* ticket = (int32_t*)ws;
+  float* part_ml = (float*)(ws + g.off_ml);
+  float* part_o = (float*)(ws + g.off_o);
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((chunk_attn_kernel<D, NR>), dim3((unsigned)g.units, (unsigned)g.splits), dim3(64 * kChunkWaves), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.blocks, a.phys, a.n_sel, a.k_cap, a.pos,
+                     scale_log2, a.n_q_heads, a.n_kv_heads, a.nb, a.n_query, (uint16_t*)a.out, ticket, part_ml,
+                     part_o);
+}
+
+// The packed path needs the chunk layout: bf16, G of 4 or 8, several rows,
+// one call over the whole attention, every block (windows included) in one
+// resident cache.
+static bool chunk_packed(const LaunchAttn& a) {
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const size_t blk_elems = (size_t)2 * kBlock * a.head_dim;
+  return a.bf16 && chunk_rows(G) > 0 && a.n_query > 1 && a.part < 0 && a.blocks == a.window_kv &&
+         a.blocks_per_head == a.nb && a.window_block_stride == (int64_t)blk_elems &&
+         a.window_head_stride == (int64_t)a.nb * (int64_t)blk_elems;
+}
+
 template <class T, int D, int WAVES, int GMAX>
 static void launch_w(const LaunchAttn& a) {
   const int units = a.batch * a.n_query * a.n_kv_heads;
@@ -180,6 +412,15 @@ static void launch(const LaunchAttn& a) {
 }
 
 void launch_attn(const LaunchAttn& a) {
+  if (chunk_packed(a)) {
+    const int NR = chunk_rows(a.n_q_heads / a.n_kv_heads);
+    if (a.head_dim == 128) {
+      if (NR == 2) launch_chunk<128, 2>(a); else launch_chunk<128, 4>(a);
+    } else {
+      if (NR == 2) launch_chunk<64, 2>(a); else launch_chunk<64, 4>(a);
+    }
+    return;
+  }
   if (a.bf16) {
     if (a.head_dim == 128) launch<Bf16, 128>(a); else launch<Bf16, 64>(a);
   } else {

@@ -524,7 +524,8 @@ def _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer):
     n_sel = torch.zeros((B, n_q, w.n_kv_heads), dtype=torch.int32, device="cuda")
     ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, w.kq, w.ke), dtype=torch.uint8, device="cuda")
     nb.select_blocks(layer.dims, qd, n_q, posd, layer.k_comp, layer.e_blk, w.kq, w.ke, sel, n_sel, ws)
-    out = torch.zeros((B, n_q, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    # a sentinel, so rows the call fails to write (zeros for rows out of range) show
+    out = torch.full((B, n_q, w.n_q_heads, w.head_dim), 3.0, dtype=torch.bfloat16, device="cuda")
     wsa = torch.zeros(nb.workspace_size(layer.dims, nb.OP_ATTN, n_q, k_cap, 0), dtype=torch.uint8, device="cuda")
     nb.sparse_chunk_attn(layer.dims, qd, n_q, kv, sel, n_sel, k_cap, posd, None, out, wsa)
     sel = sel.cpu().numpy()
@@ -549,8 +550,8 @@ def _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer):
 
 
 def test_chunk_attention_small():
-    """Ragged prompt, two batch entries, 21 rows at scattered positions (one
-    out of range), G = 4, D = 64."""
+    """Ragged prompt, two batch entries, 21 rows at scattered positions (five
+    out of range, four of them a whole packed group), G = 4, D = 64."""
     _banner("chunk attention: B=2, 21 rows, D64 G4")
     T = 64 * 90 + 13
     w = _w("layer32k", batch=2, prompt_len=T, n_steps=1, head_dim=64, n_q_heads=8, kq=10, ke=14, prefill=True)
@@ -562,6 +563,7 @@ def test_chunk_attention_small():
     q_rows = NI.round_to_bf16(rng.standard_normal((w.batch, 21, w.n_q_heads, w.head_dim)).astype(np.float32))
     pos_rows = rng.integers(0, T, size=(w.batch, 21))
     pos_rows[1, 3] = -1
+    pos_rows[1, 4:8] = -1          # a whole group of four rows (G = 4 packs four rows per MFMA tile)
     pos_rows[0, 5] = 63
     _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer)
 
