@@ -37,7 +37,7 @@ N_REPLICAS = 4
 # Byte counters of step_kernel on this workload (rocprofv3 --pmc, KiB per dispatch),
 # valid for the kernel sources whose digest is recorded here.  FETCH_SIZE reads half
 # of a plain 256 MiB copy's bytes (factor 2.0); WRITE_SIZE reads all of them (1.0).
-STEP_PMC = {"src_sha256": "a2df8798ab5f38633826ca927d5ab09cd3af674cc2614fbf157eb5e1aed08e2e", "fetch_kib": 21924.4, "write_kib": 2219.5}
+STEP_PMC = {"src_sha256": "2e9a3a93e28fb59f9caa8573ee0e324de52c7e85dfd10527a8f9e75f51f1f39d", "fetch_kib": 21913.0, "write_kib": 2219.5}
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 STEP_SOURCES = ("fused.hip", "attn_dev.h", "select_dev.h", "nosa_common.h")
 

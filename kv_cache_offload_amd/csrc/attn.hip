@@ -56,8 +56,7 @@ static ChunkGeometry chunk_geometry(int batch, int n_kv_heads, int head_dim, int
   return g;
 }
 
-size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int k_cap, int n_query) {
-  (void)nb;
+size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap, int n_query) {
   const size_t units = (size_t)batch * n_query * n_kv_heads;
   const size_t G = n_q_heads / n_kv_heads;
   const size_t splits = 2 * attn_splits(k_cap, (int)G);   // both parts of a pool step

@@ -464,15 +464,13 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
                         l_run, o);
   }
 
-  // ---------------- partials: publish, or (last workgroup) merge
+  // ---------------- the workgroup's partial: wavefronts merged in LDS, published as flagged words
   auto& L = *reinterpret_cast<MergeLds<D, kStepWaves, kStepGMax>*>(lds);
   uint64_t* recs = reinterpret_cast<uint64_t*>(ws + off_part) + (size_t)unit * W * REC;
-  typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
   __syncthreads();   // the selection arrays in LDS are dead; L reuses the space
   float own[2];
   merge_waves_keep<D, kStepWaves, kStepGMax>(L, m_run, l_run, o, G, tid, own);
   publish_part_ll<D, kStepWaves, kStepGMax>(L, G, tid, own, recs + (size_t)j * REC, flag);
-  (void)out_g;
 }
 
 template <class T, int D>

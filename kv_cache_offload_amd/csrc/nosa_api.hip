@@ -401,8 +401,7 @@ size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, i
   if (op == NOSA_OP_SELECT)
     return nosa::select_ws_bytes(dims->batch, n_query, dims->n_kv_heads, dims->max_blocks);
   if (op == NOSA_OP_ATTN)
-    return nosa::attn_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, dims->max_blocks, kq + ke,
-                               n_query);
+    return nosa::attn_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, kq + ke, n_query);
   if (op == NOSA_OP_STEP)
     return nosa::step_ws_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
                                dims->max_blocks, kq, ke);

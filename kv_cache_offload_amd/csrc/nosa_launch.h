@@ -115,7 +115,7 @@ struct LaunchStep {
 
 // Workspace geometry (bytes), shared by the size query and the launchers.
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb);
-size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int k_cap, int n_query);
+size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap, int n_query);
 size_t step_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq, int ke);
 // Dynamic LDS the selection kernel needs for nb candidate blocks.
 size_t select_lds_bytes(int nb);
