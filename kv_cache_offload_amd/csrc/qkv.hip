@@ -121,6 +121,22 @@ __global__ void __launch_bounds__(kQkvThreads) qkv_kernel(const typename T::stor
     }
   };
 
+  // key and value rows, 16-byte chunks, each with its token's position
+  // (read from global memory, so nothing waits on it first), requested
+  // before anything else: nothing they feed depends on the query copy
+  constexpr int KV_CHUNKS = 2 * TT * CPR, KVN = (KV_CHUNKS + kQkvThreads - 1) / kQkvThreads;
+  const int32_t* pos_t = pos + (size_t)b * n_tok + t0;
+  auto valid = [&](int i, int p) { return i < nt && p >= 0 && p < cap; };
+  uint4 kvr[KVN];
+  int kvp[KVN];
+  const int p_own = pos_t[min(tid, nt - 1)];
+#pragma unroll
+  for (int u = 0; u < KVN; ++u) {                  // unconditional loads (token clamped), zero if skipped
+    const int e = min(tid + u * kQkvThreads, KV_CHUNKS - 1);
+    const int isv = e >= TT * CPR, f = isv ? e - TT * CPR : e, i = f / CPR, ch = f % CPR;
+    kvr[u] = reinterpret_cast<const uint4*>(rows + min(i, nt - 1) * row_elems + (size_t)(n_q_heads + isv * n_kv_heads + h) * D)[ch];
+    kvp[u] = pos_t[min(i, nt - 1)];
+  }
   // the query heads of this KV head, 16-byte copies.  No branch: indexes
   // past the end are clamped to the last chunk, which those lanes then
   // store again with the same value (a guarded store would pull its load
@@ -143,28 +159,19 @@ __global__ void __launch_bounds__(kQkvThreads) qkv_kernel(const typename T::stor
   }
   load_b(0);                                         // in flight until the eviction head
   S* unit_kv = kv + ((size_t)b * n_kv_heads + h) * nb * ((size_t)2 * kBlock * D);
-  // key and value rows, 16-byte chunks, each with its token's position
-  // (read here from global memory, so nothing before this phase waits on
-  // it): keys straight to their block, values staged as fp32 [token][d]
-  // (zero for skipped tokens).  The positions reach LDS for the phases
-  // after the barrier.
+  // keys straight to their block, values staged as fp32 [token][d] (zero
+  // for skipped tokens); the positions reach LDS for the phases after the
+  // barrier
   {
-    constexpr int KV_CHUNKS = 2 * TT * CPR, KVN = (KV_CHUNKS + kQkvThreads - 1) / kQkvThreads;
-    const int32_t* pos_t = pos + (size_t)b * n_tok + t0;
-    auto valid = [&](int i, int p) { return i < nt && p >= 0 && p < cap; };
     uint4 r[KVN];
     int pr[KVN];
-    const int p_own = pos_t[min(tid, nt - 1)];
 #pragma unroll
-    for (int u = 0; u < KVN; ++u) {                // unconditional loads (token clamped), zero if skipped
+    for (int u = 0; u < KVN; ++u) {
       const int e = min(tid + u * kQkvThreads, KV_CHUNKS - 1);
-      const int isv = e >= TT * CPR, f = isv ? e - TT * CPR : e, i = f / CPR, ch = f % CPR;
-      const uint4 x =
-          reinterpret_cast<const uint4*>(rows + min(i, nt - 1) * row_elems + (size_t)(n_q_heads + isv * n_kv_heads + h) * D)[ch];
-      const int p = pos_t[min(i, nt - 1)];
-      const uint32_t keep = valid(i, p) ? ~0u : 0u;  // a mask, not a branch on the load
-      r[u] = make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep);
-      pr[u] = valid(i, p) ? p : -1;
+      const int i = (e >= TT * CPR ? e - TT * CPR : e) / CPR;
+      const uint32_t keep = valid(i, kvp[u]) ? ~0u : 0u;   // a mask, not a branch on the load
+      r[u] = make_uint4(kvr[u].x & keep, kvr[u].y & keep, kvr[u].z & keep, kvr[u].w & keep);
+      pr[u] = valid(i, kvp[u]) ? kvp[u] : -1;
     }
     if (tid < TT) s_pos[tid] = valid(tid, p_own) ? p_own : -1;
 #pragma unroll
