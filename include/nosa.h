@@ -347,7 +347,10 @@ int nosa_sparse_decode_attn_pool(const nosa_dims* dims, const void* q, const voi
  *   q        device [B][n_query][Hq][D], cache dtype
  *   kv       device cache [B][Hkv][NB][block]
  *   sel, n_sel  device int32 [B][n_query][Hkv][k_cap], [B][n_query][Hkv]
- *            (k_cap <= 512); entries outside [0, NB) are skipped
+ *            (k_cap <= 512); entries outside [0, NB) are skipped.  A row's
+ *            entries are distinct blocks before its window block, as
+ *            nosa_select_blocks writes them (a repeated entry, or the
+ *            window block itself, is not defined).
  *   pos      device int32 [B][n_query]; rows outside [0, NB*64) give zeros
  *   out      device [B][n_query][Hq][D], cache dtype                (written)
  *   ws       device workspace of at least
