@@ -2,8 +2,11 @@
 //
 // Exact attention over the selected 64-token blocks plus the current window
 // block (the second stage of NOSA's two-stage attention, NOSA-1B release
-// post, "工程实现亮点").  Grid = (splits, B*Hkv); each workgroup has WAVES
-// wavefronts and each wavefront attends whole 64-token blocks.
+// post, "工程实现亮点").  Grid = (units, splits), a unit being one query row
+// of one KV head; each workgroup has WAVES wavefronts and each wavefront
+// attends whole 64-token blocks.  Prefill chunks in bf16 with 4 or 8 query
+// heads per KV head use chunk_attn_kernel below instead, which packs 16/G
+// rows into the MFMA columns.
 //
 // Per block and wavefront, the G query heads of the KV head form the 16
 // columns of a 16x16 MFMA tile (G <= 16, spare columns hold zeros):

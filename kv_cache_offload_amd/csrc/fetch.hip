@@ -10,10 +10,11 @@
 // Kernel 1 (one wavefront per (b, h)): the selected set S arrives sorted, one
 // entry per lane.  Membership is a table lookup (block_table), the misses are
 // compacted with a ballot, the free slots are listed in ascending order, and
-// the evictable slots (resident, not in S) are ranked by (last_use, block
-// id) in LDS.  Miss i takes the i-th free slot, then the LRU victims in
-// order -- the same outcome as assigning the misses one at a time.  Every
-// table entry is written at most once per call.
+// the LRU victims among the evictable slots (resident, not in S) are found
+// one at a time by a wavefront minimum of (last_use, block id) keys held in
+// registers.  Miss i takes the i-th free slot, then the victims in order --
+// the same outcome as assigning the misses one at a time.  Every table entry
+// is written at most once per call.
 //
 // Kernel 2 (one workgroup per miss): copies the 64-token block from the
 // pinned host cache into its pool slot with 16-byte loads through the GPU's

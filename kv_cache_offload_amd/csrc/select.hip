@@ -11,11 +11,10 @@
 //    each publishes its block scores with coherent stores and the workgroup
 //    that draws the last ticket selects.  With a single split the scores
 //    never leave LDS.
-//  * Scan: groups of D*esize/16 lanes read one 16-byte chunk each of a row
-//    (a wavefront load is 1 KiB of contiguous rows), two rounds of 8 loads
-//    per thread in flight; the partial dot products are summed across lanes
-//    with DPP and the max over a block's 4 rows is taken on wavefront-uniform
-//    lane reads.
+//  * Scan (select_dev.h): bf16 takes 16-row tiles of the compressed keys as
+//    the A operand of v_mfma_f32_16x16x32_bf16 with the G query heads as B,
+//    sums the heads by DPP and takes a block's max over its four rows in one
+//    lane group; fp32 dots each row with the summed query (FMAs, DPP sums).
 //  * Selection: each half of the workgroup (one per budget) bins its scores
 //    into 256 equal value bins between their min and max, finds the bin
 //    holding the k-th best, takes every block above it and ranks the few

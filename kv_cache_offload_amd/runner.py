@@ -1,5 +1,5 @@
 """Decode-step driver: device buffers of one attention layer and the order of
-the four libnosa calls per step.
+the libnosa calls per step.
 
 Two modes:
 
@@ -8,13 +8,19 @@ Two modes:
   window straight from the cache;
 * offload  -- the KV cache sits in pinned host memory; a fixed HBM pool of
   `pool_slots` blocks per KV head holds the selected blocks, refilled each
-  step by nosa_fetch_blocks on a side stream (NOSI's design: only the window
-  and the Top-K blocks stay on the GPU, the rest is offloaded).
+  step (NOSI's design: only the window and the Top-K blocks stay on the GPU,
+  the rest is offloaded).
 
-Per step: select (compute stream) -> [fetch (side stream)] -> attention
-(compute stream).  The compressed keys of a block are built once, when the
+Per step, resident: select, then attention (or both in one launch,
+nosa_decode_step).  Offload, on one stream: select, fetch, attention over the
+pool; or overlapped, with a side stream: select and the pool update on the
+compute stream, then the gather of the misses on the side stream while the
+first part of the pool attention (the resident hits and the window) runs on
+the compute stream, then the second part (the fetched blocks and the merge)
+once both are done.  The compressed keys of a block are built once, when the
 block is complete.  All buffers are torch tensors; torch provides device
-memory, pinned host memory and streams, and nothing else.
+memory, pinned host memory and streams, and nothing else.  `OffloadStack`
+runs several offload layers one after another per decode step.
 """
 from __future__ import annotations
 
