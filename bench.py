@@ -109,7 +109,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the path runs on a single GPU (no sharding is implemented); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
