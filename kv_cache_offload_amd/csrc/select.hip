@@ -155,6 +155,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
 //                 over its candidates, union ascending (as select_kernel).
 constexpr int kMRows = 8;          // query rows per scan workgroup (at least one MFMA column block)
 constexpr int kMThreads = 512;
+constexpr int kTopkThreads = 1024;  // top-k workgroups, as select_kernel (512: +1.2 us per call at prefill128k)
 __host__ __device__ constexpr int mrows_per_chunk(int G) { return 16 / G > kMRows ? 16 / G : kMRows; }
 
 template <int G>
@@ -231,11 +232,11 @@ __global__ void __launch_bounds__(kMThreads) mscan_kernel(const uint16_t* __rest
 }
 
 template <class T>
-__global__ void __launch_bounds__(kMThreads) mtopk_kernel(const int32_t* __restrict__ pos, const float* __restrict__ e_blk,
+__global__ void __launch_bounds__(kTopkThreads) mtopk_kernel(const int32_t* __restrict__ pos, const float* __restrict__ e_blk,
                                                           const float* __restrict__ score, int n_query, int n_kv_heads,
                                                           int nb, int kq, int ke, int32_t* __restrict__ sel,
                                                           int32_t* __restrict__ n_sel) {
-  constexpr int kH = kMThreads / 2;
+  constexpr int kH = kTopkThreads / 2;
   const int row = blockIdx.x;               // (b * n_query + r) * Hkv + h
   const int h = row % n_kv_heads;
   const int br = row / n_kv_heads;
@@ -255,10 +256,10 @@ __global__ void __launch_bounds__(kMThreads) mtopk_kernel(const int32_t* __restr
   uint8_t* flag_e = flag_q + align256((size_t)nb);
   __shared__ int s_hist[2][kBins];
   __shared__ int s_small[2][32];
-  __shared__ int s_wsum[kMThreads / 64];
+  __shared__ int s_wsum[kTopkThreads / 64];
   const float* sc = score + (size_t)row * nb;
   const float* eb = e_blk + (size_t)unit * nb;
-  for (int j = tid; j < c; j += kMThreads) {
+  for (int j = tid; j < c; j += kTopkThreads) {
     key_q[j] = orderable(sc[j]);
     key_e[j] = orderable(eb[j]);
     flag_q[j] = 0;
@@ -268,7 +269,7 @@ __global__ void __launch_bounds__(kMThreads) mtopk_kernel(const int32_t* __restr
   const int half = tid / kH;
   select_top<kH>(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, s_hist[half], s_small[half],
                  half ? blist_e : blist_q, tid % kH);
-  const int total = write_union<kMThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
+  const int total = write_union<kTopkThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
   if (tid == 0) n_sel[row] = total;
 }
 
@@ -293,7 +294,7 @@ static bool launch_multi(const LaunchSelect& a) {
     case 8: hipLaunchKernelGGL((mscan_kernel<D, 8>), grid, dim3(kMThreads), 0, a.stream, q, a.pos, kc, a.n_query, a.n_q_heads, a.n_kv_heads, a.nb, score); break;
     default: return false;
   }
-  hipLaunchKernelGGL((mtopk_kernel<Bf16>), dim3(rows), dim3(kMThreads), select_lds_bytes(a.nb), a.stream, a.pos,
+  hipLaunchKernelGGL((mtopk_kernel<Bf16>), dim3(rows), dim3(kTopkThreads), select_lds_bytes(a.nb), a.stream, a.pos,
                      a.e_blk, score, a.n_query, a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel);
   return true;
 }
@@ -314,7 +315,6 @@ static bool launch_multi(const LaunchSelect& a) {
 //                       first row's candidates, the union written to every row.
 constexpr int kQsumThreads = 512;
 constexpr int kQsumParts = 16;                     // workgroups per unit summing the chunk's query heads
-static_assert(kMThreads == 512, "the shared kernels use 512-thread workgroups");
 
 template <int D>
 __global__ void __launch_bounds__(kQsumThreads) qsum_kernel(const uint16_t* __restrict__ q, int n_query, int n_q_heads,
@@ -408,12 +408,12 @@ __global__ void __launch_bounds__(kMThreads) shared_scan_kernel(const int32_t* _
 }
 
 // One workgroup per unit (b, h): the shared selection of all n_query rows.
-__global__ void __launch_bounds__(kMThreads) mtopk_shared_kernel(const int32_t* __restrict__ pos,
+__global__ void __launch_bounds__(kTopkThreads) mtopk_shared_kernel(const int32_t* __restrict__ pos,
                                                                  const float* __restrict__ e_blk,
                                                                  const float* __restrict__ score, int n_query,
                                                                  int n_kv_heads, int nb, int kq, int ke,
                                                                  int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
-  constexpr int kH = kMThreads / 2;
+  constexpr int kH = kTopkThreads / 2;
   const int unit = blockIdx.x;              // b * Hkv + h
   const int b = unit / n_kv_heads, h = unit % n_kv_heads;
   const int tid = threadIdx.x;
@@ -430,10 +430,10 @@ __global__ void __launch_bounds__(kMThreads) mtopk_shared_kernel(const int32_t* 
   uint8_t* flag_e = flag_q + align256((size_t)nb);
   __shared__ int s_hist[2][kBins];
   __shared__ int s_small[2][32];
-  __shared__ int s_wsum[kMThreads / 64];
+  __shared__ int s_wsum[kTopkThreads / 64];
   const float* sc = score + (size_t)unit * nb;
   const float* eb = e_blk + (size_t)unit * nb;
-  for (int j = tid; j < c; j += kMThreads) {
+  for (int j = tid; j < c; j += kTopkThreads) {
     key_q[j] = orderable(sc[j]);
     key_e[j] = orderable(eb[j]);
     flag_q[j] = 0;
@@ -447,13 +447,13 @@ __global__ void __launch_bounds__(kMThreads) mtopk_shared_kernel(const int32_t* 
   // writes only after its own barrier, when every top-k pass is done; it has
   // at most min(k_cap, c) <= nb members)
   int32_t* s_list = reinterpret_cast<int32_t*>(key_q);
-  const int total = write_union<kMThreads>(flag_q, flag_e, c, s_list, min(k_cap, nb), s_wsum, tid);
+  const int total = write_union<kTopkThreads>(flag_q, flag_e, c, s_list, min(k_cap, nb), s_wsum, tid);
   __syncthreads();
-  for (int i = tid; i < n_query * k_cap; i += kMThreads) {
+  for (int i = tid; i < n_query * k_cap; i += kTopkThreads) {
     const int r = i / k_cap, k = i % k_cap;
     sel[(((size_t)b * n_query + r) * n_kv_heads + h) * k_cap + k] = k < total ? s_list[k] : -1;
   }
-  for (int r = tid; r < n_query; r += kMThreads) n_sel[((size_t)b * n_query + r) * n_kv_heads + h] = total;
+  for (int r = tid; r < n_query; r += kTopkThreads) n_sel[((size_t)b * n_query + r) * n_kv_heads + h] = total;
 }
 
 template <int D>
@@ -472,7 +472,7 @@ static void launch_shared(const LaunchSelect& a) {
   splits = splits < 1 ? 1 : (splits > cap ? cap : splits);
   hipLaunchKernelGGL((shared_scan_kernel<D>), dim3(splits, units), dim3(kMThreads), 0, a.stream, a.pos,
                      (const uint16_t*)a.k_comp, qs, a.n_query, a.n_kv_heads, a.nb, score);
-  hipLaunchKernelGGL(mtopk_shared_kernel, dim3(units), dim3(kMThreads), select_lds_bytes(a.nb), a.stream, a.pos,
+  hipLaunchKernelGGL(mtopk_shared_kernel, dim3(units), dim3(kTopkThreads), select_lds_bytes(a.nb), a.stream, a.pos,
                      a.e_blk, score, a.n_query, a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel);
 }
 
