@@ -512,6 +512,61 @@ def test_select_shared_matches_oracle(name, over, n_q, kq, ke, starts):
                 assert e <= 2e-2, (b, r, h, e)
 
 
+def test_chunk_selections_exact_ties():
+    """Prefill-chunk selection (per-row MFMA scan, and the chunk-shared
+    selection) on keys and eviction logits that repeat one of three block
+    patterns: every score is shared by a third of the blocks, the budgets
+    are filled by the lowest ids of a group of equal scores, and the sets
+    must equal the oracle's exactly."""
+    _banner("chunk selections with exact ties")
+    T = 64 * 640 + 11
+    w = _w("layer32k", batch=2, prompt_len=T, n_steps=1, prefill=True)
+    K, V, lam, _ = NI.layer_inputs(w)
+    rng = np.random.default_rng(31)
+    pat = NI.round_to_bf16(rng.standard_normal((3, w.head_dim)).astype(np.float32))
+    blk = np.arange(K.shape[2]) // 64
+    K[:] = pat[blk % 3][None, None]
+    lam[:] = np.float32([0.5, -1.0, 2.0])[(blk * 7 // 3) % 3][None, None]
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
+    layer.pool_blocks(kv, logits, 0, T // 64)
+    n_q, k_cap, G = 13, w.kq + w.ke, w.group
+    qn = NI.round_to_bf16(rng.standard_normal((w.batch, n_q, w.n_q_heads, w.head_dim)).astype(np.float32))
+    qd = torch.from_numpy(qn).cuda().to(torch.bfloat16)
+    kbar = [[O.subblock_key_means(K[b, h], bf16=True) for h in range(w.n_kv_heads)] for b in range(w.batch)]
+    E = [[O.block_eviction_scores(O.subblock_logit_means(lam[b, h])) for h in range(w.n_kv_heads)]
+         for b in range(w.batch)]
+
+    def run(call, posn):
+        sel = torch.full((w.batch, n_q, w.n_kv_heads, k_cap), -7, dtype=torch.int32, device="cuda")
+        n_sel = torch.full((w.batch, n_q, w.n_kv_heads), -7, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, w.kq, w.ke), dtype=torch.uint8,
+                         device="cuda")
+        call(layer.dims, qd, n_q, torch.from_numpy(posn).cuda(), layer.k_comp, layer.e_blk, w.kq, w.ke, sel,
+             n_sel, ws)
+        return sel.cpu().numpy(), n_sel.cpu().numpy()
+
+    posn = rng.integers(64 * 100, T, size=(w.batch, n_q)).astype(np.int32)
+    sel, n_sel = run(nb.select_blocks, posn)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            for r in range(n_q):
+                c = int(posn[b, r]) // 64
+                s_q = O.query_block_scores(qn[b, r, h * G:(h + 1) * G], kbar[b][h], c)
+                assert len(set(np.round(s_q[:c], 9))) == 3
+                _, _, S = O.select_blocks(s_q, E[b][h], c, w.kq, w.ke)
+                assert [int(x) for x in sel[b, r, h, : n_sel[b, r, h]]] == S, ("per-row", b, r, h)
+
+    posn = np.stack([np.arange(n_q) + 64 * 600 + 3, np.arange(n_q) + 64 * 150 + 40]).astype(np.int32)
+    sel, n_sel = run(nb.select_blocks_shared, posn)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            _, _, S = O.chunk_shared_selection(qn[b, :, h * G:(h + 1) * G], int(posn[b, 0]), kbar[b][h], E[b][h],
+                                               w.kq, w.ke)
+            for r in range(n_q):
+                assert [int(x) for x in sel[b, r, h, : n_sel[b, r, h]]] == S, ("shared", b, r, h)
+
+
 def _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer):
     """Select for the n_query rows, then attend each row over its own
     selection and causal window; every row of every KV head against the
@@ -707,6 +762,38 @@ def test_fused_step_matches_oracle(wname, over):
     for b in range(w.batch):
         for h in range(w.n_kv_heads):
             H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["one-launch", "separate-calls"])
+def test_exact_ties_break_by_block_id(fused):
+    """Blocks whose keys and eviction logits repeat one of three patterns
+    score exactly alike (the same arithmetic on the same values), so each
+    budget is filled from a group of equal scores; Eq. 7's top-k then
+    keeps the lowest ids of that group (score desc, id asc) on both sides,
+    and the sets must equal the oracle's exactly, with no tie allowance."""
+    _banner(f"exact ties, fused={fused}")
+    w = NI.scaled(NI.WORKLOADS["layer32k"], batch=2, prompt_len=64 * 60 + 40, n_steps=40)
+    K, V, lam, q = NI.layer_inputs(w)
+    rng = np.random.default_rng(7)
+    pat = torch.from_numpy(rng.standard_normal((3, w.head_dim)).astype(np.float32))
+    pat = pat.to(torch.bfloat16).float().numpy()
+    blk = np.arange(K.shape[2]) // 64
+    K[:] = pat[blk % 3][None, None]
+    lam[:] = np.float32([0.5, -1.0, 2.0])[(blk * 7 // 3) % 3][None, None]
+    s1, n1, o1, layer = H.run_resident(w, K, V, lam, q, fused=fused)
+    if fused:
+        assert layer.step_timeouts() == 0
+    positions = w.positions()
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            sel = H.unit_selections(s1, n1, b, h)
+            tr, _ = H.oracle_scores(w, K, V, lam, q, b, h)
+            for t, S in enumerate(sel):
+                c = int(positions[t]) // 64
+                assert len(set(np.round(tr.s_q[t][:c], 12))) == 3      # three distinct scores, many blocks each
+                assert [int(x) for x in S] == tr.sel[t], f"unit ({b},{h}) step {t}"
+            st = H.compare_unit(w, K, V, lam, q, b, h, sel, gpu_out=o1)
+            assert st["ties"] == 0
 
 
 def test_fused_step_layer32k_full():
