@@ -57,17 +57,22 @@ __global__ void __launch_bounds__(64) pool_update_kernel(
   int32_t* lu = slot_last_use + (size_t)unit * P;
   int32_t* ml = miss_list + (size_t)unit * (k_cap + 1) * 2;
 
+  // every load that depends on nothing here goes out first (the selection,
+  // its size and the inserted block, then the slot tables), and the two
+  // block-table lookups that depend on them go out together: two memory
+  // round trips before the first decision
+  const int n_raw = n_sel[unit];
+  const int sel_raw = k_cap > 0 ? sel[(size_t)unit * k_cap + min(lane, k_cap - 1)] : -1;
+  int ins = insert_block ? insert_block[b] : -1;
   for (int s = lane; s < P; s += 64) {
     s_blk[s] = sb[s];
     s_lu[s] = lu[s];
     s_prot[s] = 0;
   }
-  __syncthreads();
 
   // this lane's selected block (S arrives ascending; anything else is skipped)
-  int n = n_sel[unit];
-  n = n < 0 ? 0 : (n > k_cap ? k_cap : n);
-  int blk = (lane < n) ? sel[(size_t)unit * k_cap + lane] : -1;
+  const int n = n_raw < 0 ? 0 : (n_raw > k_cap ? k_cap : n_raw);
+  int blk = (lane < n) ? sel_raw : -1;
   if (blk >= nb) blk = -1;
   int prev_max = blk;
 #pragma unroll
@@ -78,21 +83,17 @@ __global__ void __launch_bounds__(64) pool_update_kernel(
   int before_max = __shfl_up(prev_max, 1);
   if (lane == 0) before_max = -1;
   if (blk <= before_max) blk = -1;  // not strictly ascending: duplicate or out of order
+  if (ins >= nb) ins = -1;
+  const int bt_blk = blk >= 0 ? bt[blk] : -1;
+  const int bt_ins = ins >= 0 ? bt[ins] : -1;
+  __syncthreads();                  // the slot tables are in LDS
   int slot = -1;
-  if (blk >= 0) {
-    const int s = bt[blk];
-    if (s >= 0 && s < P && s_blk[s] == blk) slot = s;
-  }
+  if (blk >= 0 && bt_blk >= 0 && bt_blk < P && s_blk[bt_blk] == blk) slot = bt_blk;
   if (slot >= 0) s_prot[slot] = 1;
   __syncthreads();
 
   // insertion of the block the window just completed
-  int ins = insert_block ? insert_block[b] : -1;
-  if (ins >= nb) ins = -1;
-  if (ins >= 0) {
-    const int s = bt[ins];
-    if (s >= 0 && s < P && s_blk[s] == ins) ins = -1;  // already resident
-  }
+  if (ins >= 0 && bt_ins >= 0 && bt_ins < P && s_blk[bt_ins] == ins) ins = -1;  // already resident
   int ins_slot = -1, ins_old = -1;
   if (ins >= 0) {
     int fs = kMaxSlots;
