@@ -26,3 +26,18 @@ def test_locality_matches_oracle_definition():
                                       list(sels[t, u, : nsel[t, u]])))
     got = bench._locality(list(sels), list(nsel), blocks)
     assert abs(got - float(np.mean(ref))) < 1e-12
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    """The path runs on one GPU: --gpus above 1 ends with status 2 and one
+    JSON line saying so, without touching a GPU (this runs on the CPU)."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120, cwd=root)
+    assert res.returncode == 2
+    line = json.loads(res.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "single GPU" in line["error"]
