@@ -214,6 +214,8 @@ __global__ void __launch_bounds__(64) pool_update_kernel(
 }
 
 // One workgroup per (miss entry, unit); entry k_cap is the inserted block.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // a native vector stays in registers
+
 __global__ void __launch_bounds__(kGatherThreads) gather_kernel(
     const uint4* __restrict__ host_kv, uint4* __restrict__ pool, const uint4* __restrict__ insert_src,
     int nb, int P, int k_cap, int blk16, const int32_t* __restrict__ miss_list,
@@ -235,20 +237,23 @@ __global__ void __launch_bounds__(kGatherThreads) gather_kernel(
     if (insert_src == nullptr || blk < 0 || slot < 0 || slot >= P) return;
     src = insert_src + (size_t)unit * blk16;
   }
-  uint4* dst = pool + ((size_t)unit * P + slot) * blk16;
-  constexpr int U = 8;
+  const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+  u32x4* dst4 = reinterpret_cast<u32x4*>(pool + ((size_t)unit * P + slot) * blk16);
+  // U loads in flight per thread (2: with 4 or 8 the overlapped attention
+  // and the link slow each other).  Loads and stores are unguarded, with the
+  // same index clamped into the block: an index past the end rewrites the
+  // block's last chunk with its own value.  (A guarded store lets the
+  // compiler sink each load into its guard, which serialises the loads; the
+  // scheduling barrier keeps the scheduler from pairing each store with its
+  // load, which does the same.)
+  constexpr int U = 2;
   for (int base = 0; base < blk16; base += kGatherThreads * U) {
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * kGatherThreads + threadIdx.x;
-      if (i < blk16) v[u] = src[i];
-    }
+    for (int u = 0; u < U; ++u) v[u] = src4[min(base + u * kGatherThreads + (int)threadIdx.x, blk16 - 1)];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * kGatherThreads + threadIdx.x;
-      if (i < blk16) dst[i] = v[u];
-    }
+    for (int u = 0; u < U; ++u) dst4[min(base + u * kGatherThreads + (int)threadIdx.x, blk16 - 1)] = v[u];
   }
 }
 
