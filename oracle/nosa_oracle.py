@@ -43,7 +43,10 @@ Readings taken where the pages leave a step open:
 * U13 pool: each miss (ascending id) takes the lowest free slot, else evicts
       the resident block not needed this step with the smallest
       (last_use, block id); a block completed by the window is inserted first
-      with last_use = t - 1 under the same rule.
+      with last_use = t - 1 under the same rule (nothing happens when it is
+      already resident).  If a miss of the same step evicts the inserted
+      block again, no insertion is reported (insert_slot = -1): the window
+      block must not be copied over the slot the miss now owns.
 * U14 gamma(t) counted in blocks, window of t-1 counted as held at t-1.
 * U16 several query rows: each row is a decode selection at its own position.
 * U19 eviction head (Eq. 4): per KV head, W1 is D x De and W2 has De

@@ -310,13 +310,43 @@ def test_locality_counts_previous_window_as_held():
 
 
 # ---------------------------------------------------------------- the pool
-def test_pool_fixture():
+def _pool_sequences():
     g = _golden("pool_lru.json")
-    pool = O.BlockPool(g["n_slots"])
-    for st in g["steps"]:
+    yield "first", g["n_slots"], g["steps"]
+    for i, seq in enumerate(g["sequences"]):
+        yield f"seq{i}", seq["n_slots"], seq["steps"]
+
+
+@pytest.mark.parametrize("name,n_slots,steps", list(_pool_sequences()), ids=[s[0] for s in _pool_sequences()])
+def test_pool_fixture(name, n_slots, steps):
+    pool = O.BlockPool(n_slots)
+    for st in steps:
         misses, ins, phys = pool.step(st["t"], st["S"], st["insert"])
         assert [list(m) for m in misses] == st["misses"], st
         assert ins == st["insert_slot"] and phys == st["phys"], st
+        # the pool holds every block of S, each in the slot phys names
+        assert [pool.slot_of(b) for b in sorted(st["S"])] == st["phys"]
+        if ins >= 0:
+            assert pool.slot_block[ins] == st["insert"]
+
+
+def test_pool_fixture_covers_the_insert_cases():
+    """The hand-worked sequences include an insert evicted by a miss of the same
+    step, an insert of a block already resident and an insert selected in the
+    same step."""
+    seqs = list(_pool_sequences())
+    evicted = resident = selected = False
+    for _, n_slots, steps in seqs:
+        pool = O.BlockPool(n_slots)
+        for st in steps:
+            before = pool.resident()
+            pool.step(st["t"], st["S"], st["insert"])
+            if st["insert"] is None:
+                continue
+            resident |= st["insert"] in before
+            evicted |= st["insert"] not in before and st["insert_slot"] < 0
+            selected |= st["insert"] in st["S"] and st["insert_slot"] >= 0
+    assert evicted and resident and selected
 
 
 def test_pool_replay_invariants():
@@ -326,15 +356,16 @@ def test_pool_replay_invariants():
     P = 14
     tr = O.decode_unit(K, V, lam, q, w.positions(), 5, 6, bf16=False, pool_slots=P, attend=False)
     resident = {}
-    total_misses = 0
+    total_misses = inserts = 0
     for t, S in enumerate(tr.sel):
         before = set(resident)
         c = int(w.positions()[t]) // 64
-        if t > 0 and c > int(w.positions()[t - 1]) // 64:
-            if tr.insert_slot[t] >= 0:
-                slot = tr.insert_slot[t]
-                resident = {b: s for b, s in resident.items() if s != slot}
-                resident[c - 1] = slot
+        completed = t > 0 and c > int(w.positions()[t - 1]) // 64
+        if completed and tr.insert_slot[t] >= 0:
+            slot = tr.insert_slot[t]
+            resident = {b: s for b, s in resident.items() if s != slot}
+            resident[c - 1] = slot
+            inserts += 1
         misses = tr.misses[t]
         assert [b for b, _ in misses] == sorted(set(S) - set(resident))
         for b, s in misses:
@@ -344,7 +375,18 @@ def test_pool_replay_invariants():
         assert all(b in resident for b in S)
         assert [resident[b] for b in S] == tr.phys[t]
         assert len(set(resident.values())) == len(resident) <= P
-    assert total_misses > 0
+        if completed:
+            # the completed block enters the pool unless it was resident already
+            # or a miss of the same step took its slot again (reading U13); the
+            # pool is larger than k, so in a decode run that last case cannot
+            # happen: the block is always resident after the step
+            assert tr.insert_slot[t] >= 0 or (c - 1) in before
+            assert resident.get(c - 1, -1) >= 0
+            if tr.insert_slot[t] >= 0:
+                assert resident[c - 1] == tr.insert_slot[t]
+        else:
+            assert tr.insert_slot[t] == -1
+    assert total_misses > 0 and inserts > 0
 
 
 # ---------------------------------------------------------------- eviction head
