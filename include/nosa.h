@@ -387,21 +387,39 @@ int nosa_sparse_chunk_attn(const nosa_dims* dims, const void* q, int32_t n_query
  *   ws       device workspace of nosa_workspace_size(dims, NOSA_OP_STEP,
  *            1, kq, ke) bytes, zero-filled once before its first use (and
  *            again before it is used with other dims, kq or ke).  It keeps
- *            a launch counter per (b, h) and Gamma_e per (b, h) between
- *            calls, keyed by the window block: the eviction scores of blocks
- *            before the window must not change between calls with the same
- *            window block (they never do in decoding; zero-fill the
- *            workspace again after changing them).  Calls sharing a
- *            workspace must not overlap.  The int32 at byte offset
- *            256 * ceil(4 * B * Hkv / 256) counts hand-off waits between the
- *            kernel's workgroups that hit their bound (about 0.3 s); it
- *            stays 0 unless the device failed to run them concurrently, in
- *            which case the outputs of that call are wrong.
+ *            an arrival counter per (b, h) and Gamma_e per (b, h) between
+ *            calls, keyed by the e_blk address and the window block: the
+ *            eviction scores at that address must not change for blocks
+ *            before the window between calls with the same window block
+ *            (they never do in decoding, where a block's score is fixed once
+ *            it is complete; zero-fill the workspace again after changing
+ *            them).  Calls sharing a workspace must not overlap.
+ * The kernel's workgroups hand partial results to each other through the
+ * workspace; every such wait is bounded (about 0.3 s).  A wait that hits its
+ * bound -- only possible if the device did not run the workgroups of one
+ * launch concurrently -- is counted in the workspace and turns the outputs
+ * it feeds into NaN; nosa_step_timeouts reads the count.
  */
 int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
                      const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,
                      int32_t* sel, int32_t* n_sel, void* out, void* ws, size_t ws_bytes,
                      void* stream);
+
+/*
+ * nosa_step_timeouts -- the number of bounded hand-off waits of
+ * nosa_decode_step that hit their bound so far in workspace ws (0 when every
+ * launch ran as it should).
+ *
+ *   dims, kq, ke  as given to nosa_decode_step with this workspace
+ *   ws            the step workspace (device)
+ *   out           device memory, or pinned host memory the device can write
+ *                 (hipHostMalloc), receiving one int32            (written)
+ * Enqueued on `stream` after the steps to be checked; the caller reads out
+ * once the stream has reached it.  Errors: -1 for NULL buffers or negative
+ * budgets.
+ */
+int nosa_step_timeouts(const nosa_dims* dims, int32_t kq, int32_t ke, const void* ws, int32_t* out,
+                       void* stream);
 
 /* Workspace bytes needed by op (NOSA_OP_SELECT, NOSA_OP_ATTN or NOSA_OP_STEP); 0 on bad input. */
 size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, int32_t kq,

@@ -25,7 +25,7 @@ EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_sparse_decode_attn", "nosa_decode_step", "nosa_workspace_size",
            "nosa_status_str", "nosa_last_error", "nosa_update_pool", "nosa_gather_blocks",
            "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn", "nosa_split_qkv",
-           "nosa_select_blocks_shared")
+           "nosa_select_blocks_shared", "nosa_step_timeouts")
 
 
 class NosaError(RuntimeError):
@@ -65,6 +65,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_sparse_decode_attn_pool.argtypes = [D, P, P, I32, P, P, I32, P, P, P, I64, I64, P, F, I32, P, P, SZ, P]
     lib.nosa_sparse_chunk_attn.argtypes = [D, P, I32, P, P, P, I32, P, F, P, P, SZ, P]
     lib.nosa_split_qkv.argtypes = [D, P, I32, P, P, P, I32, P, P, P, P]
+    lib.nosa_step_timeouts.argtypes = [D, I32, I32, P, P, P]
     lib.nosa_workspace_size.restype = SZ
     lib.nosa_status_str.argtypes = [I32]
     lib.nosa_status_str.restype = ctypes.c_char_p
@@ -72,7 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_last_error.restype = ctypes.c_char_p
     for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
                  "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool",
-                 "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared"):
+                 "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared", "nosa_step_timeouts"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -223,3 +224,10 @@ def decode_step(d: Dims, q, pos, k_comp, e_blk, kq: int, ke: int, kv, scale: Opt
                                  _ptr(kv), float(scale), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(ws),
                                  ws_bytes, _stream(stream))
     _check("nosa_decode_step", rc)
+
+
+def step_timeouts(d: Dims, kq: int, ke: int, ws, out, stream=None) -> None:
+    """Enqueue the copy of workspace ws's hand-off timeout count into out
+    (an int32 device or pinned host tensor)."""
+    rc = load().nosa_step_timeouts(ctypes.byref(d), kq, ke, _ptr(ws), _ptr(out), _stream(stream))
+    _check("nosa_step_timeouts", rc)

@@ -359,18 +359,19 @@ __device__ void merge_waves_keep(MergeLds<D, WAVES, GMAX>& L, float m_run, float
 }
 
 // Publish a workgroup's partial (from merge_waves_keep) as flagged words;
-// no wait: the merging workgroup polls the words themselves.
+// no wait: the merging workgroup polls the words themselves.  A poisoned
+// partial carries NaN maxima and sums, which make the merged outputs NaN.
 template <int D, int WAVES, int GMAX>
 __device__ void publish_part_ll(const MergeLds<D, WAVES, GMAX>& L, int G, int tid, const float (&own)[2],
-                                uint64_t* rec, uint32_t flag) {
+                                uint64_t* rec, uint32_t flag, bool poison = false) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int idx = tid + r * 64 * WAVES;
     if (idx < G * D) ll_store(&rec[idx], own[r], flag);
   }
   if (tid < G) {
-    ll_store(&rec[GMAX * D + 2 * tid], L.M[tid], flag);
-    ll_store(&rec[GMAX * D + 2 * tid + 1], L.den[tid], flag);
+    ll_store(&rec[GMAX * D + 2 * tid], poison ? __builtin_nanf("") : L.M[tid], flag);
+    ll_store(&rec[GMAX * D + 2 * tid + 1], poison ? __builtin_nanf("") : L.den[tid], flag);
   }
 }
 
@@ -398,6 +399,7 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
   const uint64_t* pm = recs + (size_t)sp_ml * REC + GMAX * D + 2 * g_ml;
   uint64_t wm = has_ml ? ll_load(pm) : ll_word(-INFINITY, flag);
   uint64_t wl = has_ml ? ll_load(pm + 1) : ll_word(0.f, flag);
+  bool late = false;   // a wait hit its bound: this workgroup's outputs are NaN
   {
     // one loop for every word this thread waits on, so a record that lands
     // late costs one reload round, not one per word kind
@@ -407,7 +409,10 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
 #pragma unroll
       for (int sp = 0; sp < MAXP; ++sp) ok = ok && ll_ok(w[sp], flag);
       if (ok || it >= spin_limit) {
-        if (!ok) atomicAdd(err, 1);
+        if (!ok) {
+          atomicAdd(err, 1);
+          late = true;
+        }
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -425,15 +430,16 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
     const float M = group_max<16>(m);
     const float a = m == -INFINITY ? 0.f : exp2f(m - M);
     const float den = group_sum<16>(a * l);
-    L.a[g_ml][sp_ml] = den > 0.f ? a / den : 0.f;
+    // a NaN sum (a poisoned record) keeps the weights NaN
+    L.a[g_ml][sp_ml] = (den > 0.f || den != den) ? a / den : 0.f;
   }
-  __syncthreads();
+  const bool any_late = __syncthreads_or(late ? 1 : 0) != 0;
   if (has) {
     const int g = idx / D;
     float n = 0.f;
 #pragma unroll
     for (int sp = 0; sp < MAXP; ++sp) n = fmaf(L.a[g][sp], ll_float(w[sp]), n);
-    store_out(&out_g[idx], n);
+    store_out(&out_g[idx], any_late ? __builtin_nanf("") : n);
   }
 }
 

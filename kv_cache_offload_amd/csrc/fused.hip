@@ -24,18 +24,21 @@
 //
 // Every hand-off between workgroups goes through flagged 8-byte words
 // (payload + launch flag; see nosa_common.h): producers store and move on,
-// consumers poll the words.  The flag is a per-unit launch counter; the last
-// merge workgroup advances it once every merge workgroup has read it (each
-// posts a start word), by which point every other workgroup of the unit has
-// read it too, since the merges depend on all of them.  The workspace never
-// needs resetting between launches.
+// consumers poll the words.  The flag comes from a per-unit arrival ticket:
+// every workgroup of a unit draws one ticket (an atomic add) per launch, the
+// launches of one stream draw theirs in order, so ticket / (workgroups per
+// unit) is the launch's index whatever the timing -- even a workgroup that
+// starts after a merge gave up waiting for it tags its words with its own
+// launch's flag.  The workspace never needs resetting between launches.
 //
 // Workgroup j of unit u has index j * U + u, and every wait is on a
 // workgroup of lower index (Q workers wait on E workers, merge workgroups on
 // all the others), which the dispatcher has started earlier, so each wait
-// ends; the waits are bounded as well (a timeout is counted in the workspace
-// and leaves a wrong result, never a hang).  The merge workgroups come last
-// in the grid, so they occupy CUs only once E workers have finished.
+// ends; the waits are bounded as well.  A wait that hits its bound is
+// counted in the workspace (nosa_step_timeouts reads the count) and the
+// outputs it feeds are written as NaN, never a hang.  The merge workgroups
+// come last in the grid, so they occupy CUs only once E workers have
+// finished.
 #include "nosa_common.h"
 #include "nosa_launch.h"
 #include "attn_dev.h"
@@ -53,8 +56,11 @@ constexpr int kStepWgsTarget = 256;   // workgroups per launch to aim for: one p
 
 struct StepGeometry {
   int units, W, nQ, nE, nM;
-  size_t off_epoch, off_err, off_ge, off_score, off_part, off_mstart, total;
+  size_t off_arrive, off_err, off_ge, off_score, off_part, total;
 };
+// Gamma_e cache words per unit: the count, the e_blk address (two words),
+// then up to kStepMaxK ids
+constexpr int kGeHead = 3;
 
 static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq,
                                   int ke) {
@@ -75,18 +81,29 @@ static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int 
   const size_t U = g.units;
   const size_t rec = (size_t)kStepGMax * head_dim + 2 * kStepGMax;
   size_t o = 0;
-  g.off_epoch = o; o += align256(U * 4);
+  g.off_arrive = o; o += align256(U * 8);
   g.off_err = o; o += 256;
-  g.off_ge = o; o += align256(U * (kStepMaxK + 1) * 8);
+  g.off_ge = o; o += align256(U * (kStepMaxK + kGeHead) * 8);
   g.off_score = o; o += align256(U * (size_t)nb * 8);
   g.off_part = o; o += align256(U * (size_t)W * rec * 8);
-  g.off_mstart = o; o += align256(U * 4 * 8);
   g.total = o;
   return g;
 }
 
 size_t step_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq, int ke) {
   return step_geometry(batch, n_q_heads, n_kv_heads, head_dim, nb, kq, ke).total;
+}
+
+size_t step_err_offset(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq, int ke) {
+  return step_geometry(batch, n_q_heads, n_kv_heads, head_dim, nb, kq, ke).off_err;
+}
+
+// This launch's flag from one arrival ticket of the unit (thread 0 draws it;
+// the caller broadcasts it): launch index + 1, never 0, which is what a word
+// nobody has written holds.
+__device__ __forceinline__ uint32_t draw_flag(uint64_t* arrive, int wgs_per_unit) {
+  const uint64_t t = __hip_atomic_fetch_add(arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (uint32_t)((t / (uint64_t)wgs_per_unit) % 0xFFFFFFFFull) + 1u;
 }
 
 template <int D>
@@ -123,10 +140,10 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     const typename T::storage* __restrict__ kv, int n_q_heads, int n_kv_heads, int nb, int kq,
     int ke, float scale_log2, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
     typename T::storage* __restrict__ out, unsigned char* __restrict__ ws, int W, int nQ, int nM,
-    size_t off_err, size_t off_ge, size_t off_score, size_t off_part, size_t off_mstart) {
+    size_t off_err, size_t off_ge, size_t off_score, size_t off_part) {
   constexpr int ND = D / 16;
   constexpr int REC = part_record_words<D, kStepGMax>();
-  constexpr int GER = (kStepMaxK + 1 + kStepThreads - 1) / kStepThreads;   // cache words per thread
+  constexpr int GER = (kStepMaxK + kGeHead + kStepThreads - 1) / kStepThreads;   // cache words per thread
   const int G = n_q_heads / n_kv_heads;
   const int U = gridDim.x / (W + nM);
   const int nE = W - nQ;
@@ -136,39 +153,35 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   const int unit = blockIdx.x % U, j = blockIdx.x / U;
   const bool is_q = j >= nE;
   const int b = unit / n_kv_heads, h = unit % n_kv_heads;
-  int* epoch = reinterpret_cast<int*>(ws);
+  uint64_t* arrive = reinterpret_cast<uint64_t*>(ws) + unit;
   int* err = reinterpret_cast<int*>(ws + off_err);
+  __shared__ uint32_t s_flag;
   const uint64_t* recs_all = reinterpret_cast<const uint64_t*>(ws + off_part);
   constexpr int REC_ = part_record_words<D, kStepGMax>();
 
   if (j >= W) {
     // ---------------- merge workgroup m of the unit: a slice of the output
     // from all W records.  Every other workgroup of the unit precedes it in
-    // index order.  The last merge workgroup advances the unit's launch
-    // counter once every merge workgroup has read it (a start word each).
+    // index order.
     extern __shared__ __align__(16) unsigned char lds_m[];
     auto& L = *reinterpret_cast<MergeLds<D, kStepWaves, kStepGMax>*>(lds_m);
     const int m = j - W;
-    const uint32_t flag = (uint32_t)__builtin_amdgcn_readfirstlane(load_coherent_i(&epoch[unit])) + 1u;
-    uint64_t* mstart = reinterpret_cast<uint64_t*>(ws + off_mstart) + (size_t)unit * 4;
-    if (tid == 0) ll_store(&mstart[m], 0u, flag);
+    if (tid == 0) s_flag = draw_flag(arrive, W + nM);
+    __syncthreads();
+    const uint32_t flag = s_flag;
     const int GD = G * D, per = (GD + nM - 1) / nM;
     const int lo = min(GD, m * per), n_out = min(per, GD - lo);
     typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
     merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs_all + (size_t)unit * W * REC_, flag,
                                                     kSpinLimit, err, out_g);
-    if (m == nM - 1) {
-      if (tid < m) ll_wait(&mstart[tid], ll_load(&mstart[tid]), flag, kSpinLimit, err);
-      __syncthreads();
-      if (tid == 0) store_coherent_i(&epoch[unit], (int)(flag == 0xFFFFFFFFu ? 0u : flag));
-    }
     return;
   }
 
   uint64_t* score_ll = reinterpret_cast<uint64_t*>(ws + off_score) + (size_t)unit * nb;
-  // Gamma_e cache: word 0 = count, words 1.. = ids, each tagged with the
-  // window block + 1 it was computed for
-  uint64_t* ge = reinterpret_cast<uint64_t*>(ws + off_ge) + (size_t)unit * (kStepMaxK + 1);
+  // Gamma_e cache: word 0 = count, words 1, 2 = the e_blk address it was
+  // computed from, words 3.. = ids, each tagged with the window block + 1 it
+  // was computed for
+  uint64_t* ge = reinterpret_cast<uint64_t*>(ws + off_ge) + (size_t)unit * (kStepMaxK + kGeHead);
   const typename T::storage* q_group = q + ((size_t)b * n_q_heads + (size_t)h * G) * D;
   const typename T::storage* unit_kv = kv + (size_t)unit * nb * ((size_t)2 * kBlock * D);
   const float* eb = e_blk + (size_t)unit * nb;
@@ -189,12 +202,12 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   // (Q workers) the unit's block scores are requested together; nothing waits
   // for them before the scan's own loads are out
   const int p_raw = pos[b];
-  const int e_raw = load_coherent_i(&epoch[unit]);
+  if (tid == 0) s_flag = draw_flag(arrive, W + nM);
   uint64_t gw[GER];
 #pragma unroll
   for (int r = 0; r < GER; ++r) {
     const int i = tid + r * kStepThreads;
-    gw[r] = i <= ke ? ll_load(&ge[i]) : 0;
+    gw[r] = i < ke + kGeHead ? ll_load(&ge[i]) : 0;
   }
   uint64_t w_sc[kScoreRegs];
   if (is_q) {
@@ -226,27 +239,31 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   const bool valid_pos = (p_raw >= 0 && p_raw < nb * kBlock);
   const int c = valid_pos ? p_raw / kBlock : 0;
   const int win_len = valid_pos ? p_raw - c * kBlock + 1 : 0;
-  // this launch's flag: the unit's launch counter + 1 (never 0, which is
-  // what a never-written word holds)
-  const uint32_t flag = (uint32_t)__builtin_amdgcn_readfirstlane(e_raw) + 1u;
   const uint32_t ge_tag = (uint32_t)c + 1u;
   const int ge_cap = min(ke, c);
-  // the cache is current when its count and every listed id carry this
-  // window block's tag
+  const uint64_t eb_addr = (uint64_t)(uintptr_t)e_blk;
+  // the cache is current when its count, the e_blk address and every listed
+  // id carry this window block's tag
   bool mine = true;
 #pragma unroll
   for (int r = 0; r < GER; ++r) {
     const int i = tid + r * kStepThreads;
-    if (i >= 1 && i <= ge_cap) mine = mine && ll_ok(gw[r], ge_tag);
+    if (i >= kGeHead && i < kGeHead + ge_cap) mine = mine && ll_ok(gw[r], ge_tag);
     if (i == 0) mine = mine && ll_ok(gw[r], ge_tag) && (int)(uint32_t)gw[r] == ge_cap;
+    if (i == 1) mine = mine && ll_ok(gw[r], ge_tag) && (uint32_t)gw[r] == (uint32_t)eb_addr;
+    if (i == 2) mine = mine && ll_ok(gw[r], ge_tag) && (uint32_t)gw[r] == (uint32_t)(eb_addr >> 32);
   }
   if (!is_q && kq > 0) {
     // publish this slice's scores of blocks before the window
     __syncthreads();
+    const uint32_t flag = s_flag;
     const int pub_hi = min(slice_hi, c);
     for (int i = tid; i < pub_hi - slice_lo; i += kStepThreads) ll_store(&score_ll[slice_lo + i], s_sc[i], flag);
   }
   const bool cache_ok = __syncthreads_or(mine ? 0 : 1) == 0;   // also: s_sc dead
+  // this launch's flag (drawn by thread 0 in the prologue)
+  const uint32_t flag = s_flag;
+  bool timed_out = false;
 
   if (!is_q) {
     // ---------------- E worker: Gamma_e
@@ -256,7 +273,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
 #pragma unroll
       for (int r = 0; r < GER; ++r) {
         const int i = tid + r * kStepThreads;
-        if (i >= 1 && i <= ge_cap) s_list[i - 1] = (int)(uint32_t)gw[r];
+        if (i >= kGeHead && i < kGeHead + ge_cap) s_list[i - kGeHead] = (int)(uint32_t)gw[r];
       }
     } else {
       for (int jj = tid; jj < c; jj += kStepThreads) {
@@ -269,8 +286,12 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
       if (j == 0) {
         // refresh the cache (every word tagged, so no ordering is needed)
         __syncthreads();
-        for (int i = tid; i < nge; i += kStepThreads) ll_store(&ge[1 + i], (uint32_t)s_list[i], ge_tag);
-        if (tid == 0) ll_store(&ge[0], (uint32_t)nge, ge_tag);
+        for (int i = tid; i < nge; i += kStepThreads) ll_store(&ge[kGeHead + i], (uint32_t)s_list[i], ge_tag);
+        if (tid == 0) {
+          ll_store(&ge[0], (uint32_t)nge, ge_tag);
+          ll_store(&ge[1], (uint32_t)eb_addr, ge_tag);
+          ll_store(&ge[2], (uint32_t)(eb_addr >> 32), ge_tag);
+        }
       }
     }
     __syncthreads();
@@ -302,7 +323,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
       for (int r = 0; r < GER; ++r) {
         const int i = tid + r * kStepThreads;
         const int id = (int)(uint32_t)gw[r];
-        if (i >= 1 && i <= ge_cap && id >= 0 && id < c) flag_e[id] = 1;
+        if (i >= kGeHead && i < kGeHead + ge_cap && id >= 0 && id < c) flag_e[id] = 1;
       }
     } else {
       select_top<kStepThreads>(key_e, c, ke, flag_e, s_hist, s_small, blist, tid);
@@ -322,7 +343,10 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
 #pragma unroll
         for (int i = 0; i < kScoreRegs; ++i) ok = ok && (tid + i * kStepThreads >= c || ll_ok(w_sc[i], flag));
         if (ok || it >= kSpinLimit) {
-          if (!ok) atomicAdd(err, 1);
+          if (!ok) {
+            atomicAdd(err, 1);
+            timed_out = true;
+          }
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -467,10 +491,13 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   // ---------------- the workgroup's partial: wavefronts merged in LDS, published as flagged words
   auto& L = *reinterpret_cast<MergeLds<D, kStepWaves, kStepGMax>*>(lds);
   uint64_t* recs = reinterpret_cast<uint64_t*>(ws + off_part) + (size_t)unit * W * REC;
-  __syncthreads();   // the selection arrays in LDS are dead; L reuses the space
   float own[2];
+  // the selection arrays in LDS are dead past this barrier (L reuses the
+  // space); a worker whose score wait timed out poisons its partial, so the
+  // unit's outputs come out NaN
+  const bool poison = __syncthreads_or(timed_out ? 1 : 0) != 0;
   merge_waves_keep<D, kStepWaves, kStepGMax>(L, m_run, l_run, o, G, tid, own);
-  publish_part_ll<D, kStepWaves, kStepGMax>(L, G, tid, own, recs + (size_t)j * REC, flag);
+  publish_part_ll<D, kStepWaves, kStepGMax>(L, G, tid, own, recs + (size_t)j * REC, flag, poison);
 }
 
 template <class T, int D>
@@ -482,8 +509,7 @@ static void launch(const LaunchStep& a) {
                      (const typename T::storage*)a.q, a.pos, (const typename T::storage*)a.k_comp,
                      a.e_blk, (const typename T::storage*)a.kv, a.n_q_heads, a.n_kv_heads, a.nb,
                      a.kq, a.ke, scale_log2, a.sel, a.n_sel, (typename T::storage*)a.out,
-                     (unsigned char*)a.ws, g.W, g.nQ, g.nM, g.off_err, g.off_ge, g.off_score, g.off_part,
-                     g.off_mstart);
+                     (unsigned char*)a.ws, g.W, g.nQ, g.nM, g.off_err, g.off_ge, g.off_score, g.off_part);
 }
 
 void launch_step(const LaunchStep& a) {
@@ -492,6 +518,17 @@ void launch_step(const LaunchStep& a) {
   } else {
     if (a.head_dim == 128) launch<F32, 128>(a); else launch<F32, 64>(a);
   }
+}
+
+// ---------------------------------------------------------------------------
+// The timeout counter of a step workspace, copied out by one thread.
+__global__ void copy_counter_kernel(const int* __restrict__ src, int32_t* __restrict__ dst) {
+  if (threadIdx.x == 0) *dst = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+void launch_step_timeouts(const void* ws, size_t off_err, int32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_counter_kernel, dim3(1), dim3(64), 0, stream,
+                     reinterpret_cast<const int*>(static_cast<const unsigned char*>(ws) + off_err), out);
 }
 
 }  // namespace nosa

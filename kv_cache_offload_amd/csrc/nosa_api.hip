@@ -352,10 +352,15 @@ int nosa_split_qkv(const nosa_dims* dims, const void* qkv, int32_t n_tok, const 
   return check_launch(fn);
 }
 
-int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
-                     const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,
-                     int32_t* sel, int32_t* n_sel, void* out, void* ws, size_t ws_bytes, void* stream) {
-  static const char* fn = "nosa_decode_step";
+}  // extern "C"
+
+namespace nosa {
+
+// Checks every host-side argument of the one-launch step except the
+// workspace and fills its launch descriptor (ws left NULL); 0 or a status.
+int prepare_step(const char* fn, const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
+                 const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale, int32_t* sel,
+                 int32_t* n_sel, void* out, void* stream, LaunchStep* a) {
   if (int rc = check_dims(dims, fn)) return rc;
   if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
   if (kq + ke > kMaxStepK) return fail(NOSA_ERR_UNSUPPORTED, fn, "kq + ke above 256");
@@ -363,34 +368,62 @@ int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, c
     return fail(NOSA_ERR_UNSUPPORTED, fn, "more than 8 query heads per KV head");
   if (dims->max_blocks > kMaxSelectBlocks)
     return fail(NOSA_ERR_UNSUPPORTED, fn, "max_blocks above 4096 (256K tokens)");
-  if (!q || !pos || !k_comp || !e_blk || !kv || !n_sel || !out || !ws || (kq + ke > 0 && !sel))
+  if (!q || !pos || !k_comp || !e_blk || !kv || !n_sel || !out || (kq + ke > 0 && !sel))
     return fail(NOSA_ERR_ARG, fn, "NULL buffer");
   if (!(scale == scale)) return fail(NOSA_ERR_ARG, fn, "scale is NaN");
   if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
     return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_kv_heads above 65535");
+  *a = LaunchStep{};
+  a->bf16 = dims->dtype == NOSA_BF16;
+  a->head_dim = dims->head_dim;
+  a->batch = dims->batch;
+  a->n_q_heads = dims->n_q_heads;
+  a->n_kv_heads = dims->n_kv_heads;
+  a->nb = dims->max_blocks;
+  a->kq = kq;
+  a->ke = ke;
+  a->q = q;
+  a->pos = pos;
+  a->k_comp = k_comp;
+  a->e_blk = e_blk;
+  a->kv = kv;
+  a->scale = scale;
+  a->sel = sel;
+  a->n_sel = n_sel;
+  a->out = out;
+  a->ws = nullptr;
+  a->stream = (hipStream_t)stream;
+  return NOSA_OK;
+}
+
+}  // namespace nosa
+
+extern "C" {
+
+int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
+                     const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,
+                     int32_t* sel, int32_t* n_sel, void* out, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "nosa_decode_step";
+  nosa::LaunchStep a;
+  if (int rc = nosa::prepare_step(fn, dims, q, pos, k_comp, e_blk, kq, ke, kv, scale, sel, n_sel, out, stream, &a))
+    return rc;
+  if (!ws) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
   const size_t need = nosa_workspace_size(dims, NOSA_OP_STEP, 1, kq, ke);
   if (ws_bytes < need) return fail(NOSA_ERR_WORKSPACE, fn, "workspace too small");
-  nosa::LaunchStep a{};
-  a.bf16 = dims->dtype == NOSA_BF16;
-  a.head_dim = dims->head_dim;
-  a.batch = dims->batch;
-  a.n_q_heads = dims->n_q_heads;
-  a.n_kv_heads = dims->n_kv_heads;
-  a.nb = dims->max_blocks;
-  a.kq = kq;
-  a.ke = ke;
-  a.q = q;
-  a.pos = pos;
-  a.k_comp = k_comp;
-  a.e_blk = e_blk;
-  a.kv = kv;
-  a.scale = scale;
-  a.sel = sel;
-  a.n_sel = n_sel;
-  a.out = out;
   a.ws = ws;
-  a.stream = (hipStream_t)stream;
   nosa::launch_step(a);
+  return check_launch(fn);
+}
+
+int nosa_step_timeouts(const nosa_dims* dims, int32_t kq, int32_t ke, const void* ws, int32_t* out,
+                       void* stream) {
+  static const char* fn = "nosa_step_timeouts";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
+  if (!ws || !out) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  const size_t off = nosa::step_err_offset(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                                           dims->max_blocks, kq, ke);
+  nosa::launch_step_timeouts(ws, off, out, (hipStream_t)stream);
   return check_launch(fn);
 }
 

@@ -117,6 +117,9 @@ struct LaunchStep {
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb);
 size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap, int n_query);
 size_t step_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq, int ke);
+// Byte offset of the timeout counter inside a step workspace.
+size_t step_err_offset(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq, int ke);
+void launch_step_timeouts(const void* ws, size_t off_err, int32_t* out, hipStream_t stream);
 // Dynamic LDS the selection kernel needs for nb candidate blocks.
 size_t select_lds_bytes(int nb);
 

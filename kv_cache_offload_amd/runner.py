@@ -185,12 +185,13 @@ class DecodeLayer:
 
     def step_timeouts(self) -> int:
         """Waits of the one-launch step that hit their bound so far (0 when
-        every hand-off completed); reads the workspace counter (synchronises)."""
+        every hand-off completed), read through nosa_step_timeouts on the
+        current stream (synchronises)."""
         if self.ws_step is None:
             return 0
-        units = self.dims.batch * self.dims.n_kv_heads
-        off = (units * 4 + 255) // 256 * 256
-        return int(self.ws_step[off:off + 4].view(torch.int32).item())
+        out = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        nb.step_timeouts(self.dims, self.kq, self.ke, self.ws_step, out)
+        return int(out.item())
 
     def step_offload(self, q, host_kv, window, pos, step: int, insert_block=None, insert_src=None,
                      side: Optional[torch.cuda.Stream] = None) -> None:

@@ -257,3 +257,14 @@ def test_step_checks(lib):
     with pytest.raises(nb.NosaError) as e:
         nb.decode_step(_d(n_q_heads=32), *args[1:], ws_bytes=1 << 30, stream=0)
     assert e.value.code == nb.ERR_UNSUPPORTED
+
+
+def test_step_timeouts_checks(lib):
+    d = _d()
+    for ws, out in ((None, FAKE), (FAKE, None)):
+        with pytest.raises(nb.NosaError) as e:
+            nb.step_timeouts(d, 16, 48, ws, out, stream=0)
+        assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.step_timeouts(d, -1, 48, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_ARG
