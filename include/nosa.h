@@ -406,17 +406,39 @@ int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, c
                      void* stream);
 
 /*
+ * nosa_decode_step_static -- nosa_decode_step with no workspace argument and
+ * no allocation: for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments (minus ws, ws_bytes), results and errors as
+ * nosa_decode_step.  The workspace is the library's own: one 16 MiB device
+ * array per device, held until the process ends, zero-filled on the first
+ * call on a device and whenever the geometry (dims, kq, ke) differs from the
+ * previous call's on that device.  Every call on a device shares it and it
+ * keeps the last call's contents, so calls that overlap on one device (other
+ * streams, other threads) race; calls in stream order do not.  Gamma_e is
+ * cached in it keyed by the e_blk address and the window block, as in
+ * nosa_decode_step.  A geometry whose workspace (nosa_workspace_size with
+ * NOSA_OP_STEP) exceeds 16 MiB is rejected with -4.  The call allocates and
+ * frees nothing; the first call on a device looks up the array's address.
+ */
+int nosa_decode_step_static(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
+                            const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,
+                            int32_t* sel, int32_t* n_sel, void* out, void* stream);
+
+/*
  * nosa_step_timeouts -- the number of bounded hand-off waits of
  * nosa_decode_step that hit their bound so far in workspace ws (0 when every
  * launch ran as it should).
  *
  *   dims, kq, ke  as given to nosa_decode_step with this workspace
- *   ws            the step workspace (device)
+ *   ws            the step workspace (device); NULL: this device's static
+ *                 workspace of nosa_decode_step_static
  *   out           device memory, or pinned host memory the device can write
  *                 (hipHostMalloc), receiving one int32            (written)
  * Enqueued on `stream` after the steps to be checked; the caller reads out
- * once the stream has reached it.  Errors: -1 for NULL buffers or negative
- * budgets.
+ * once the stream has reached it.  Errors: -1 for a NULL out, negative
+ * budgets, or ws = NULL before nosa_decode_step_static ran on this device.
  */
 int nosa_step_timeouts(const nosa_dims* dims, int32_t kq, int32_t ke, const void* ws, int32_t* out,
                        void* stream);

@@ -25,7 +25,7 @@ EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_sparse_decode_attn", "nosa_decode_step", "nosa_workspace_size",
            "nosa_status_str", "nosa_last_error", "nosa_update_pool", "nosa_gather_blocks",
            "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn", "nosa_split_qkv",
-           "nosa_select_blocks_shared", "nosa_step_timeouts")
+           "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static")
 
 
 class NosaError(RuntimeError):
@@ -66,6 +66,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_sparse_chunk_attn.argtypes = [D, P, I32, P, P, P, I32, P, F, P, P, SZ, P]
     lib.nosa_split_qkv.argtypes = [D, P, I32, P, P, P, I32, P, P, P, P]
     lib.nosa_step_timeouts.argtypes = [D, I32, I32, P, P, P]
+    lib.nosa_decode_step_static.argtypes = [D, P, P, P, P, I32, I32, P, F, P, P, P, P]
     lib.nosa_workspace_size.restype = SZ
     lib.nosa_status_str.argtypes = [I32]
     lib.nosa_status_str.restype = ctypes.c_char_p
@@ -73,7 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_last_error.restype = ctypes.c_char_p
     for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
                  "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool",
-                 "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared", "nosa_step_timeouts"):
+                 "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -231,3 +232,13 @@ def step_timeouts(d: Dims, kq: int, ke: int, ws, out, stream=None) -> None:
     (an int32 device or pinned host tensor)."""
     rc = load().nosa_step_timeouts(ctypes.byref(d), kq, ke, _ptr(ws), _ptr(out), _stream(stream))
     _check("nosa_step_timeouts", rc)
+
+
+def decode_step_static(d: Dims, q, pos, k_comp, e_blk, kq: int, ke: int, kv, scale: Optional[float], sel, n_sel,
+                       out, stream=None) -> None:
+    """nosa_decode_step on the library's own per-device workspace (no allocation)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(d.head_dim)
+    rc = load().nosa_decode_step_static(ctypes.byref(d), _ptr(q), _ptr(pos), _ptr(k_comp), _ptr(e_blk), kq, ke,
+                                        _ptr(kv), float(scale), _ptr(sel), _ptr(n_sel), _ptr(out), _stream(stream))
+    _check("nosa_decode_step_static", rc)

@@ -10,7 +10,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnosa.so")
-SOURCES = ["nosa_api.hip", "pool_keys.hip", "select.hip", "fetch.hip", "attn.hip", "fused.hip", "qkv.hip"]
+SOURCES = ["nosa_api.hip", "pool_keys.hip", "select.hip", "fetch.hip", "attn.hip", "fused.hip", "qkv.hip",
+           "step_static.hip"]
 ARCH = "gfx950"
 
 

@@ -396,6 +396,9 @@ int prepare_step(const char* fn, const nosa_dims* dims, const void* q, const int
   return NOSA_OK;
 }
 
+int report(int code, const char* fn, const char* what) { return fail(code, fn, what); }
+int launched(const char* fn) { return check_launch(fn); }
+
 }  // namespace nosa
 
 extern "C" {
@@ -420,7 +423,12 @@ int nosa_step_timeouts(const nosa_dims* dims, int32_t kq, int32_t ke, const void
   static const char* fn = "nosa_step_timeouts";
   if (int rc = check_dims(dims, fn)) return rc;
   if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
-  if (!ws || !out) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (!out) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  if (!ws) {
+    // the static workspace of nosa_decode_step_static on this device
+    ws = nosa::static_step_address();
+    if (!ws) return fail(NOSA_ERR_ARG, fn, "ws is NULL and nosa_decode_step_static has not run on this device");
+  }
   const size_t off = nosa::step_err_offset(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
                                            dims->max_blocks, kq, ke);
   nosa::launch_step_timeouts(ws, off, out, (hipStream_t)stream);

@@ -113,6 +113,12 @@ struct LaunchStep {
   hipStream_t stream;
 };
 
+// Geometry of a one-launch step, the key of the library's static workspace.
+struct StepKey {
+  int batch, n_q_heads, n_kv_heads, head_dim, nb, dtype, kq, ke;
+};
+constexpr size_t kStaticStepBytes = (size_t)16 << 20;   // the static step workspace per device
+
 // Workspace geometry (bytes), shared by the size query and the launchers.
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb);
 size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int k_cap, int n_query);
@@ -120,8 +126,28 @@ size_t step_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int
 // Byte offset of the timeout counter inside a step workspace.
 size_t step_err_offset(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq, int ke);
 void launch_step_timeouts(const void* ws, size_t off_err, int32_t* out, hipStream_t stream);
+// This device's static step workspace, zero-filled on `stream` when first used
+// and when the geometry changes; returns 0, or a status with *why set.
+int static_step_workspace(const StepKey& key, size_t need, hipStream_t stream, void** ws_out, const char** why);
+// Device address of this device's static step workspace (NULL before its first use).
+void* static_step_address();
 // Dynamic LDS the selection kernel needs for nb candidate blocks.
 size_t select_lds_bytes(int nb);
+
+}  // namespace nosa
+
+struct nosa_dims;
+
+namespace nosa {
+
+// The one-launch step's host-side checks (everything but the workspace) and
+// its launch descriptor; 0 or a status, with the error text recorded.
+int prepare_step(const char* fn, const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
+                 const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale, int32_t* sel,
+                 int32_t* n_sel, void* out, void* stream, LaunchStep* a);
+// Record a failure of `fn` (returns code); the status of a call's launches.
+int report(int code, const char* fn, const char* what);
+int launched(const char* fn);
 
 void launch_pool_keys(const LaunchPool& a);
 void launch_select(const LaunchSelect& a);

@@ -268,3 +268,14 @@ def test_step_timeouts_checks(lib):
     with pytest.raises(nb.NosaError) as e:
         nb.step_timeouts(d, -1, 48, FAKE, FAKE, stream=0)
     assert e.value.code == nb.ERR_ARG
+
+
+def test_static_step_rejects_a_workspace_above_its_size(lib):
+    # 2048 units x 4096 blocks of scores alone need 64 MiB: more than the
+    # static workspace holds; rejected before anything touches a device
+    d = _d(batch=1024, max_blocks=4096)
+    assert nb.workspace_size(d, nb.OP_STEP, 1, 16, 48) > (16 << 20)
+    with pytest.raises(nb.NosaError) as e:
+        nb.decode_step_static(d, FAKE, FAKE, FAKE, FAKE, 16, 48, FAKE, None, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
+    assert "16 MiB" in lib.nosa_last_error().decode()
