@@ -377,12 +377,14 @@ __device__ void publish_part_ll(const MergeLds<D, WAVES, GMAX>& L, int G, int ti
 
 // A merge workgroup of a unit: outputs [out_lo, out_lo + n_out) (n_out <=
 // 64*WAVES, one per thread) from the unit's n_part flagged records, polled
-// until they carry `flag`; per-head weights from one 16-lane group per head
-// (lane = record); normalised and stored.  Splitting a unit's outputs over
-// several such workgroups divides the record bytes each one reads.
-template <class T, int D, int WAVES, int GMAX, int MAXP>
+// until they carry the launch's flag; per-head weights from one 16-lane
+// group per head (lane = record); normalised and stored.  Splitting a unit's
+// outputs over several such workgroups divides the record bytes each one
+// reads.  The first loads of every word go out before get_flag() (which may
+// itself wait on memory) is called, so its wait overlaps theirs.
+template <class T, int D, int WAVES, int GMAX, int MAXP, class GetFlag>
 __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int n_part, int out_lo, int n_out,
-                               const uint64_t* recs, uint32_t flag, int spin_limit, int* err,
+                               const uint64_t* recs, GetFlag get_flag, int spin_limit, int* err,
                                typename T::storage* out_g) {
   constexpr int REC = part_record_words<D, GMAX>();
   static_assert(MAXP <= 16, "one 16-lane group per head");
@@ -390,24 +392,24 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
   const bool has = tid < n_out;
   uint64_t w[MAXP];
 #pragma unroll
-  for (int sp = 0; sp < MAXP; ++sp)
-    w[sp] = (sp < n_part && has) ? ll_load(recs + (size_t)sp * REC + idx) : ll_word(0.f, flag);
+  for (int sp = 0; sp < MAXP; ++sp) w[sp] = (sp < n_part && has) ? ll_load(recs + (size_t)sp * REC + idx) : 0;
   // lanes of the first 16 * GMAX threads also own the (max, sum) words of
   // record sp = tid % 16 for head g = tid / 16
   const int g_ml = tid >> 4, sp_ml = tid & 15;
   const bool has_ml = tid < 16 * GMAX && g_ml < G && sp_ml < n_part;
   const uint64_t* pm = recs + (size_t)sp_ml * REC + GMAX * D + 2 * g_ml;
-  uint64_t wm = has_ml ? ll_load(pm) : ll_word(-INFINITY, flag);
-  uint64_t wl = has_ml ? ll_load(pm + 1) : ll_word(0.f, flag);
+  uint64_t wm = has_ml ? ll_load(pm) : 0;
+  uint64_t wl = has_ml ? ll_load(pm + 1) : 0;
+  const uint32_t flag = get_flag();
   bool late = false;   // a wait hit its bound: this workgroup's outputs are NaN
   {
     // one loop for every word this thread waits on, so a record that lands
     // late costs one reload round, not one per word kind
     int it = 0;
     while (true) {
-      bool ok = ll_ok(wm, flag) && ll_ok(wl, flag);
+      bool ok = !has_ml || (ll_ok(wm, flag) && ll_ok(wl, flag));
 #pragma unroll
-      for (int sp = 0; sp < MAXP; ++sp) ok = ok && ll_ok(w[sp], flag);
+      for (int sp = 0; sp < MAXP; ++sp) ok = ok && (!(sp < n_part && has) || ll_ok(w[sp], flag));
       if (ok || it >= spin_limit) {
         if (!ok) {
           atomicAdd(err, 1);
@@ -416,11 +418,11 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-      if (!ll_ok(wm, flag)) wm = ll_load(pm);
-      if (!ll_ok(wl, flag)) wl = ll_load(pm + 1);
+      if (has_ml && !ll_ok(wm, flag)) wm = ll_load(pm);
+      if (has_ml && !ll_ok(wl, flag)) wl = ll_load(pm + 1);
 #pragma unroll
       for (int sp = 0; sp < MAXP; ++sp)
-        if (!ll_ok(w[sp], flag)) w[sp] = ll_load(recs + (size_t)sp * REC + idx);
+        if (sp < n_part && has && !ll_ok(w[sp], flag)) w[sp] = ll_load(recs + (size_t)sp * REC + idx);
       ++it;
     }
   }
@@ -438,7 +440,8 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
     const int g = idx / D;
     float n = 0.f;
 #pragma unroll
-    for (int sp = 0; sp < MAXP; ++sp) n = fmaf(L.a[g][sp], ll_float(w[sp]), n);
+    for (int sp = 0; sp < MAXP; ++sp)
+      if (sp < n_part) n = fmaf(L.a[g][sp], ll_float(w[sp]), n);
     store_out(&out_g[idx], any_late ? __builtin_nanf("") : n);
   }
 }

@@ -113,6 +113,15 @@ static size_t step_lds_bytes(int nb) {
   return a > s ? a : s;
 }
 
+// A workgroup barrier that orders LDS only.  __syncthreads() also releases
+// global memory, so every wavefront would first wait for its outstanding
+// global stores (the published scores); nothing after the publish needs that.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Attend half blocks first, first + stride, ... < n_half of the list
 // (entry e: half e & 1 of block blk_of(e >> 1), len_of(e >> 1) valid tokens),
 // folding them into the wavefront's running partial.
@@ -172,8 +181,8 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     const int GD = G * D, per = (GD + nM - 1) / nM;
     const int lo = min(GD, m * per), n_out = min(per, GD - lo);
     typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
-    merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs_all + (size_t)unit * W * REC_, flag,
-                                                    kSpinLimit, err, out_g);
+    merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs_all + (size_t)unit * W * REC_,
+                                                    [&]() { return flag; }, kSpinLimit, err, out_g);
     return;
   }
 
@@ -198,26 +207,31 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   uint8_t* flag_q = lds + 2 * kb + 2 * lb;
   uint8_t* flag_e = flag_q + align256((size_t)nb);
 
-  // ---- prologue: the position, the launch counter, the Gamma_e cache and
-  // (Q workers) the unit's block scores are requested together; nothing waits
-  // for them before the scan's own loads are out
-  const int p_raw = pos[b];
-  if (tid == 0) s_flag = draw_flag(arrive, W + nM);
+  // ---- prologue: the position, the arrival ticket, the Gamma_e cache and
+  // (Q workers) the unit's block scores are requested together.  An E worker
+  // issues its scan's loads first and these behind them: a wavefront's memory
+  // counter is in order, so the wait for the scan's data then never waits
+  // for the coherent loads and the ticket, which are used only afterwards.
+  int p_raw = 0;
+  uint64_t ticket = 0;
   uint64_t gw[GER];
-#pragma unroll
-  for (int r = 0; r < GER; ++r) {
-    const int i = tid + r * kStepThreads;
-    gw[r] = i < ke + kGeHead ? ll_load(&ge[i]) : 0;
-  }
   uint64_t w_sc[kScoreRegs];
-  if (is_q) {
+  auto prologue = [&]() {
+    p_raw = pos[b];
+    if (tid == 0) ticket = __hip_atomic_fetch_add(arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-    for (int i = 0; i < kScoreRegs; ++i) {
-      const int jj = tid + i * kStepThreads;
-      w_sc[i] = jj < nb ? ll_load(&score_ll[jj]) : 0;
+    for (int r = 0; r < GER; ++r) {
+      const int i = tid + r * kStepThreads;
+      gw[r] = i < ke + kGeHead ? ll_load(&ge[i]) : 0;
     }
-  }
-
+    if (is_q) {
+#pragma unroll
+      for (int i = 0; i < kScoreRegs; ++i) {
+        const int jj = tid + i * kStepThreads;
+        w_sc[i] = jj < nb ? ll_load(&score_ll[jj]) : 0;
+      }
+    }
+  };
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[ND];
 #pragma unroll
@@ -231,8 +245,22 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   float* s_sc = reinterpret_cast<float*>(lds);
   if (!is_q && kq > 0 && slice_lo < slice_hi) {
     const typename T::storage* kc = k_comp + (size_t)unit * nb * kSubsPerBlock * D;
-    scan_block_scores<T, D, kStepThreads>(q_group, G, kc, kSubsPerBlock * slice_lo, kSubsPerBlock * slice_hi, tid,
-                                          [&](int blk, float sc) { s_sc[blk - slice_lo] = sc; });
+    auto put = [&](int blk, float sc) { s_sc[blk - slice_lo] = sc; };
+    if constexpr (sizeof(typename T::storage) == 2) {
+      MfmaScan<D, kStepThreads> scan(q_group, G, kc, kSubsPerBlock * slice_lo, kSubsPerBlock * slice_hi, tid);
+      prologue();
+      scan.finish(put);
+    } else {
+      prologue();
+      scan_block_scores_fma<T, D, kStepThreads>(q_group, G, kc, kSubsPerBlock * slice_lo, kSubsPerBlock * slice_hi, tid, put);
+    }
+  } else {
+    prologue();
+  }
+  __shared__ int s_stale;                             // a thread found the Gamma_e cache stale
+  if (tid == 0) {
+    s_flag = (uint32_t)((ticket / (uint64_t)(W + nM)) % 0xFFFFFFFFull) + 1u;
+    s_stale = 0;
   }
 
   // ---- now the prologue values
@@ -259,8 +287,12 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     const uint32_t flag = s_flag;
     const int pub_hi = min(slice_hi, c);
     for (int i = tid; i < pub_hi - slice_lo; i += kStepThreads) ll_store(&score_ll[slice_lo + i], s_sc[i], flag);
+  } else {
+    __syncthreads();                                  // s_stale cleared
   }
-  const bool cache_ok = __syncthreads_or(mine ? 0 : 1) == 0;   // also: s_sc dead
+  if (!mine) s_stale = 1;
+  lds_barrier();                                      // also: s_sc dead
+  const bool cache_ok = s_stale == 0;
   // this launch's flag (drawn by thread 0 in the prologue)
   const uint32_t flag = s_flag;
   bool timed_out = false;
