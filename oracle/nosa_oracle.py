@@ -58,6 +58,20 @@ Readings taken where the pages leave a step open:
       the complete blocks before the first row's block; every row attends the
       shared set plus its own window.
 
+Alternative readings, each behind a flag and off by default (the library's
+own path follows U1 and U6):
+
+* U21 Eq. 7 read as "fill the remainder from the candidates left": the
+      query-agnostic part is the top-ke of E over the candidates outside
+      Gamma_q, so the union holds exactly min(kq + ke, c) blocks.  A block can
+      then leave the query-agnostic part and come back later, which the
+      eviction rule forbids (montaan "Key Design Components" items 1, 4).
+* U22 ED-DMA's deferred exponential read as an additive logit: the eviction
+      score of each attended token (its pre-exponential logit, U5) is added to
+      that token's attention logit, softmax(q K^T / sqrt(D) + lambda)
+      (gist.science "1. Algorithme : NOSA", the ED-DMA item: the exponential
+      is applied at the attention step).
+
 Pins: every function here is pinned by a test against something other than
 itself (a library routine, brute force, a closed form or a stated invariant);
 none is "parity unpinned".
@@ -171,6 +185,18 @@ def select_blocks(s_q: Sequence[float], E: Sequence[float], n_cand: int,
     return sorted(g_q), sorted(g_e), sorted(set(g_q) | set(g_e))
 
 
+def select_blocks_fill(s_q: Sequence[float], E: Sequence[float], n_cand: int,
+                       kq: int, ke: int) -> Tuple[List[int], List[int], List[int]]:
+    """Eq. 7 read as U21: Gamma_q as in select_blocks, then the query-agnostic
+    part is the top-ke of E over the candidates not in Gamma_q.  Returns
+    (Gamma_q, the query-agnostic part, their union), each ascending."""
+    g_q = top_blocks(list(s_q[:n_cand]), kq)
+    in_q = set(g_q)
+    rest = [j for j in range(n_cand) if j not in in_q]
+    g_e = [rest[i] for i in top_blocks([E[j] for j in rest], ke)]
+    return sorted(g_q), sorted(g_e), sorted(in_q | set(g_e))
+
+
 def chunk_shared_selection(q_rows: np.ndarray, first_pos: int, kbar: np.ndarray, E: Sequence[float],
                            kq: int, ke: int) -> Tuple[List[int], List[int], List[int]]:
     """One Eq. 7 selection for all rows of a prefill chunk (reading U20).
@@ -214,16 +240,20 @@ def attended_tokens(S: Sequence[int], pos: int) -> np.ndarray:
 
 
 def sparse_attention(q_group: np.ndarray, K: np.ndarray, V: np.ndarray,
-                     S: Sequence[int], pos: int) -> np.ndarray:
-    """o_g = softmax(q_g K_T^T / sqrt(D)) V_T for T = selected blocks + window.
+                     S: Sequence[int], pos: int, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """o_g = softmax(q_g K_T^T / sqrt(D) [+ bias_T]) V_T for T = selected blocks + window.
 
-    float64 throughout; returns [G, D] float64 (the caller rounds).
+    bias (reading U22): per-token additive logits [>= pos + 1], natural-log
+    units, the same for every query head.  float64 throughout; returns [G, D]
+    float64 (the caller rounds).
     """
     idx = attended_tokens(S, pos)
     q = np.asarray(q_group, dtype=np.float64)
     k = np.asarray(K[idx], dtype=np.float64)
     v = np.asarray(V[idx], dtype=np.float64)
     logits = (q @ k.T) / math.sqrt(q.shape[1])
+    if bias is not None:
+        logits = logits + np.asarray(bias, dtype=np.float64)[idx][None, :]
     logits = logits - logits.max(axis=1, keepdims=True)
     w = np.exp(logits)
     w = w / w.sum(axis=1, keepdims=True)
@@ -306,6 +336,20 @@ class BlockPool:
 # O9: locality (montaan "How it works", Eq. 3; gist.science "Garantie de
 # localité": gamma(t) >= ke/k)
 # --------------------------------------------------------------------------
+def readmissions(gamma_e: Sequence[Sequence[int]]) -> int:
+    """Blocks that re-enter the query-agnostic part after leaving it, summed
+    over the steps: the eviction rule (montaan "Key Design Components"
+    item 1) says this is 0."""
+    dropped, count = set(), 0
+    for t in range(len(gamma_e)):
+        cur = set(gamma_e[t])
+        count += len(cur & dropped)
+        if t > 0:
+            dropped |= set(gamma_e[t - 1]) - cur
+        dropped -= cur
+    return count
+
+
 def locality(S_prev: Sequence[int], window_prev: int, S: Sequence[int]) -> float:
     if len(S) == 0:
         return 1.0
@@ -332,12 +376,15 @@ class UnitTrace:
 def decode_unit(K: np.ndarray, V: np.ndarray, lam: np.ndarray, q_rows: np.ndarray,
                 positions: Sequence[int], kq: int, ke: int, bf16: bool,
                 pool_slots: Optional[int] = None, attend: bool = True,
-                forced_sel: Optional[Dict[int, List[int]]] = None) -> UnitTrace:
+                forced_sel: Optional[Dict[int, List[int]]] = None,
+                fill_remaining: bool = False, evict_bias: bool = False) -> UnitTrace:
     """Run the path for one (batch, KV head) over consecutive decode positions.
 
     K, V: [T, D]; lam: [T]; q_rows: [n, G, D]; positions: the n positions.
     `forced_sel` maps a step to a selection to use in place of the oracle's
     own (used to keep lock-step when a score tie is accepted).
+    `fill_remaining` selects with reading U21 (gamma_e then holds the
+    query-agnostic part), `evict_bias` attends with reading U22.
     """
     kbar = subblock_key_means(K, bf16)
     E = block_eviction_scores(subblock_logit_means(lam))
@@ -348,7 +395,8 @@ def decode_unit(K: np.ndarray, V: np.ndarray, lam: np.ndarray, q_rows: np.ndarra
     for t, p in enumerate(positions):
         c = int(p) // BLOCK
         s_q = query_block_scores(q_rows[t], kbar, c)
-        g_q, g_e, S = select_blocks(s_q, E, c, kq, ke)
+        pick = select_blocks_fill if fill_remaining else select_blocks
+        g_q, g_e, S = pick(s_q, E, c, kq, ke)
         if forced_sel is not None and t in forced_sel:
             S = sorted(forced_sel[t])
         tr.s_q.append(s_q)
@@ -362,7 +410,8 @@ def decode_unit(K: np.ndarray, V: np.ndarray, lam: np.ndarray, q_rows: np.ndarra
             tr.insert_slot.append(ins_slot)
             tr.phys.append(phys)
         if attend:
-            tr.out.append(round_output(sparse_attention(q_rows[t], K, V, S, int(p)), bf16))
+            tr.out.append(round_output(sparse_attention(q_rows[t], K, V, S, int(p), lam if evict_bias else None),
+                                       bf16))
         tr.locality.append(locality(prev_S, prev_c, S) if prev_S is not None else float("nan"))
         prev_S, prev_c = S, c
     return tr

@@ -431,3 +431,126 @@ def test_eviction_head_special_weights():
     W1 = rng.standard_normal((8, 8))
     assert np.allclose(O.eviction_logits(V, W1, Wa + Wb),
                        O.eviction_logits(V, W1, Wa) + O.eviction_logits(V, W1, Wb), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------- alternative readings (U21, U22)
+def _rank_order(E, ids):
+    """ids ordered by (E desc, id asc), the order of Eq. 7's top-k."""
+    return sorted(ids, key=lambda j: (-float(E[j]), j))
+
+
+def test_fill_remaining_brute_force():
+    """U21 on tiny inputs: Gamma_q is the default one, the query-agnostic part
+    is the unique subset of the candidates outside Gamma_q that precedes all
+    the others in (E desc, id asc) order (found by enumerating every subset),
+    and the union holds exactly min(kq + ke, c) blocks."""
+    rng = np.random.default_rng(21)
+    for trial in range(300):
+        c = int(rng.integers(0, 11))
+        s_q = rng.integers(-3, 4, size=c).astype(np.float64)       # many ties
+        E = rng.integers(-2, 3, size=c).astype(np.float32)
+        kq, ke = int(rng.integers(0, 6)), int(rng.integers(0, 6))
+        g_q, g_f, S = O.select_blocks_fill(s_q, E, c, kq, ke)
+        assert g_q == O.select_blocks(s_q, E, c, kq, ke)[0]
+        rest = [j for j in range(c) if j not in set(g_q)]
+        n_e = min(ke, len(rest))
+        assert len(g_f) == n_e and not set(g_f) & set(g_q)
+        assert len(S) == min(kq + ke, c) and S == sorted(set(g_q) | set(g_f))
+        pos = {j: i for i, j in enumerate(_rank_order(E, rest))}
+        winners = [set(R) for R in itertools.combinations(rest, n_e)
+                   if all(pos[a] < pos[b] for a in R for b in rest if b not in R)]
+        assert winners == [set(g_f)], (trial, c, kq, ke)
+
+
+def test_fill_remaining_reduces_to_one_budget():
+    rng = np.random.default_rng(22)
+    for _ in range(50):
+        c = int(rng.integers(1, 40))
+        s_q, E = rng.standard_normal(c), rng.standard_normal(c).astype(np.float32)
+        k = int(rng.integers(0, 12))
+        assert O.select_blocks_fill(s_q, E, c, 0, k)[2] == O.select_blocks(s_q, E, c, 0, k)[2]
+        assert O.select_blocks_fill(s_q, E, c, k, 0)[2] == O.select_blocks(s_q, E, c, k, 0)[2]
+
+
+def test_readmissions_counts_returns_to_the_query_agnostic_part():
+    # worked by hand: block 2 leaves at step 1 and returns at step 2; block 5
+    # leaves at step 2 and returns at step 4 after one step away, then leaves
+    # and returns again at step 6
+    seq = [[1, 2, 5], [0, 1, 5], [1, 2], [1, 3], [1, 5], [1, 6], [1, 5]]
+    assert O.readmissions(seq) == 3
+    assert O.readmissions([[1, 2], [1, 2], [2, 3], [3, 4]]) == 0
+    assert O.readmissions([]) == 0
+
+
+def test_fill_remaining_can_break_the_eviction_rule():
+    """Hand-worked: E = [10, 9, 8, 7] over four fixed candidates, kq = 1,
+    ke = 2.  The query picks block 0, then block 3, then block 0 again.
+    Under U21 the query-agnostic part is {1, 2}, {0, 1}, {1, 2}: block 2 is
+    dropped at step 1 and re-admitted at step 2.  Under U1 it is {0, 1}
+    every step."""
+    E = np.float32([10, 9, 8, 7])
+    picks = [0, 3, 0]
+    parts_fill, parts_union = [], []
+    for p in picks:
+        s_q = np.zeros(4)
+        s_q[p] = 1.0
+        parts_fill.append(O.select_blocks_fill(s_q, E, 4, 1, 2)[1])
+        parts_union.append(O.select_blocks(s_q, E, 4, 1, 2)[1])
+    assert parts_fill == [[1, 2], [0, 1], [1, 2]]
+    assert parts_union == [[0, 1]] * 3
+    assert O.readmissions(parts_fill) == 1 and O.readmissions(parts_union) == 0
+
+
+def test_fill_remaining_readmits_in_decode_runs_and_union_never_does():
+    w = NI.scaled(NI.WORKLOADS["tiny"], prompt_len=64 * 20 + 5, n_steps=200, kq=4, ke=4, head_dim=16, rho=0.9)
+    K, V, lam = NI.unit_kv(w, 0, 0)
+    q = NI.queries(w)[:, 0]
+    union = O.decode_unit(K, V, lam, q, w.positions(), 4, 4, bf16=False, attend=False)
+    fill = O.decode_unit(K, V, lam, q, w.positions(), 4, 4, bf16=False, attend=False, fill_remaining=True)
+    assert O.readmissions(union.gamma_e) == 0
+    assert O.readmissions(fill.gamma_e) > 0
+    for t, p in enumerate(w.positions()):
+        c = int(p) // 64
+        assert len(fill.sel[t]) == min(8, c) and len(union.sel[t]) <= min(8, c)
+
+
+def test_evict_bias_zero_and_constant_change_nothing():
+    rng = np.random.default_rng(23)
+    T, D, pos = 64 * 5 + 9, 16, 64 * 5 + 8
+    K, V = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    q = rng.standard_normal((3, D))
+    S = [0, 2, 3]
+    ref = O.sparse_attention(q, K, V, S, pos)
+    assert np.array_equal(O.sparse_attention(q, K, V, S, pos, np.zeros(T)), ref)
+    # softmax is invariant to adding one constant to every logit
+    np.testing.assert_allclose(O.sparse_attention(q, K, V, S, pos, np.full(T, -7.25)), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_evict_bias_brute_force():
+    """U22 term by term in plain Python on a tiny case."""
+    rng = np.random.default_rng(24)
+    T, D, pos = 64 * 2 + 3, 4, 64 * 2 + 2
+    K, V = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    lam = rng.standard_normal(T) * 2
+    q = rng.standard_normal((2, D))
+    S = [1]
+    got = O.sparse_attention(q, K, V, S, pos, lam)
+    toks = list(range(64, 128)) + list(range(128, pos + 1))
+    for g in range(2):
+        ls = [sum(q[g, d] * K[i, d] for d in range(D)) / math.sqrt(D) + lam[i] for i in toks]
+        m = max(ls)
+        ws = [math.exp(l - m) for l in ls]
+        z = sum(ws)
+        for d in range(D):
+            ref = sum(w * V[i, d] for w, i in zip(ws, toks)) / z
+            assert abs(got[g, d] - ref) <= 1e-12
+
+
+def test_evict_bias_can_pick_one_token():
+    rng = np.random.default_rng(25)
+    T, D, pos = 64 * 3 + 1, 8, 64 * 3
+    K, V = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    q = rng.standard_normal((1, D))
+    lam = np.full(T, -1e4)
+    lam[70] = 0.0
+    np.testing.assert_allclose(O.sparse_attention(q, K, V, [1], pos, lam)[0], V[70], rtol=0, atol=1e-12)
