@@ -179,6 +179,28 @@ int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query,
                        size_t ws_bytes, void* stream);
 
 /*
+ * nosa_select_blocks_fill -- nosa_select_blocks under the other reading of
+ * Eq. 7, a variant kept for comparison (the path itself uses the union of
+ * two independent top-k sets).
+ *
+ * The montaan summary's Eq. 7 ("Key Design Components" item 4) fills "the
+ * remainder" with query-agnostic blocks; read as the remainder of the
+ * candidates, the query-agnostic part is the top-ke of e_blk over the
+ * candidates outside Gamma_q:
+ *   Gamma_q  as in nosa_select_blocks;
+ *   F        = the min(ke, c - |Gamma_q|) blocks j < c, j not in Gamma_q, with
+ *              the best (e_blk desc, j asc);
+ *   sel      = Gamma_q U F ascending, exactly min(kq + ke, c) blocks.
+ * A block can leave F when it enters Gamma_q and come back when it leaves
+ * Gamma_q, which the eviction rule of the same summary (item 1) forbids.
+ * Arguments, layouts, workspace and errors as nosa_select_blocks.
+ */
+int nosa_select_blocks_fill(const nosa_dims* dims, const void* q, int32_t n_query,
+                            const int32_t* pos, const void* k_comp, const float* e_blk,
+                            int32_t kq, int32_t ke, int32_t* sel, int32_t* n_sel, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
  * nosa_select_blocks_shared -- one selection for all n_query rows of a
  * prefill chunk.
  *
@@ -307,6 +329,34 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
                             int64_t window_head_stride, int64_t window_block_stride,
                             const int32_t* pos, float scale, void* out, void* ws,
                             size_t ws_bytes, void* stream);
+
+/*
+ * nosa_sparse_decode_attn_bias -- nosa_sparse_decode_attn over the resident
+ * cache with each token's eviction logit added to its attention logit, a
+ * variant kept for comparison (the path itself adds no bias, so that top-k
+ * over every block is dense causal attention).
+ *
+ * The gist.science summary ("1. Algorithme : NOSA", ED-DMA) defers the
+ * eviction head's exponential to the attention step; read as an additive
+ * logit:
+ *   out[b][h*G+g] = sum_{i in T} softmax_i(scale * q . K_i + L[b][h][i]) V_i
+ * with T as in nosa_sparse_decode_attn and L = evict_logits (natural-log
+ * units, the same for every query head of the KV head).
+ *
+ *   q, pos, scale, out, ws   as nosa_sparse_decode_attn
+ *   kv            device cache [B][Hkv][NB][block]; the window is block
+ *                 pos/64 of the cache
+ *   sel, n_sel    device int32 [B][Hkv][k_cap], [B][Hkv] (k_cap <= 512), as
+ *                 nosa_select_blocks writes them; entries outside [0, NB)
+ *                 are skipped
+ *   evict_logits  device fp32 [B][Hkv][NB*64], the logits nosa_pool_keys
+ *                 pools
+ * Errors as nosa_sparse_decode_attn.
+ */
+int nosa_sparse_decode_attn_bias(const nosa_dims* dims, const void* q, const void* kv, const int32_t* sel,
+                                 const int32_t* n_sel, int32_t k_cap, const int32_t* pos, float scale,
+                                 const float* evict_logits, void* out, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /*
  * nosa_sparse_decode_attn_pool -- nosa_sparse_decode_attn over the HBM pool

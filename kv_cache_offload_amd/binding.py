@@ -25,7 +25,8 @@ EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_sparse_decode_attn", "nosa_decode_step", "nosa_workspace_size",
            "nosa_status_str", "nosa_last_error", "nosa_update_pool", "nosa_gather_blocks",
            "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn", "nosa_split_qkv",
-           "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static")
+           "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static",
+           "nosa_select_blocks_fill", "nosa_sparse_decode_attn_bias")
 
 
 class NosaError(RuntimeError):
@@ -56,6 +57,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_pool_keys.argtypes = [D, P, I64, I64, P, I32, I32, P, P, P, P]
     lib.nosa_select_blocks.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
     lib.nosa_select_blocks_shared.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
+    lib.nosa_select_blocks_fill.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
+    lib.nosa_sparse_decode_attn_bias.argtypes = [D, P, P, P, P, I32, P, F, P, P, P, SZ, P]
     lib.nosa_fetch_blocks.argtypes = [D, P, P, I32, P, P, P, I32, P, P, I32, P, P, P, P, P, P]
     lib.nosa_sparse_decode_attn.argtypes = [D, P, P, I32, P, P, I32, P, I64, I64, P, F, P, P, SZ, P]
     lib.nosa_decode_step.argtypes = [D, P, P, P, P, I32, I32, P, F, P, P, P, P, SZ, P]
@@ -74,7 +77,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_last_error.restype = ctypes.c_char_p
     for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
                  "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool",
-                 "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static"):
+                 "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static",
+                 "nosa_select_blocks_fill", "nosa_sparse_decode_attn_bias"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -135,6 +139,28 @@ def select_blocks(d: Dims, q, n_query: int, pos, k_comp, e_blk, kq: int, ke: int
                                    _ptr(e_blk), kq, ke, _ptr(sel), _ptr(n_sel), _ptr(ws), ws_bytes,
                                    _stream(stream))
     _check("nosa_select_blocks", rc)
+
+
+def select_blocks_fill(d: Dims, q, n_query: int, pos, k_comp, e_blk, kq: int, ke: int, sel, n_sel,
+                       ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = load().nosa_select_blocks_fill(ctypes.byref(d), _ptr(q), n_query, _ptr(pos), _ptr(k_comp),
+                                        _ptr(e_blk), kq, ke, _ptr(sel), _ptr(n_sel), _ptr(ws), ws_bytes,
+                                        _stream(stream))
+    _check("nosa_select_blocks_fill", rc)
+
+
+def sparse_decode_attn_bias(d: Dims, q, kv, sel, n_sel, k_cap: int, pos, scale: Optional[float], evict_logits,
+                            out, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if scale is None:
+        scale = 1.0 / math.sqrt(d.head_dim)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = load().nosa_sparse_decode_attn_bias(ctypes.byref(d), _ptr(q), _ptr(kv), _ptr(sel), _ptr(n_sel), k_cap,
+                                             _ptr(pos), float(scale), _ptr(evict_logits), _ptr(out), _ptr(ws),
+                                             ws_bytes, _stream(stream))
+    _check("nosa_sparse_decode_attn_bias", rc)
 
 
 def select_blocks_shared(d: Dims, q, n_query: int, pos, k_comp, e_blk, kq: int, ke: int, sel, n_sel,

@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     int64_t win_block_stride, const int32_t* __restrict__ pos, float scale_log2, int n_q_heads,
     int n_kv_heads, int nb, typename T::storage* __restrict__ out, int32_t* __restrict__ ticket,
     float* __restrict__ part_ml, float* __restrict__ part_o, const int32_t* __restrict__ miss_list,
-    const int32_t* __restrict__ n_miss_p, int n_split_main, int n_query) {
+    const int32_t* __restrict__ n_miss_p, int n_split_main, int n_query, const float* __restrict__ bias) {
   constexpr int ND = D / 16;
   const int G = n_q_heads / n_kv_heads;
   // grid (units, splits): workgroups are dispatched x-fastest, so every
@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     // only those (and no window)
     const int e = (int)blockIdx.y * WAVES + wave;
     const typename T::storage* blk = nullptr;
-    int len = 0;
+    int len = 0, lblk = -1;      // lblk: the block's logical id (its position / 64)
     if (e < ns) {
       const int pb = phys[(size_t)unit * k_cap + e];
       bool take = pb >= 0 && pb < blocks_per_head;
@@ -147,12 +147,17 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
       if (take) {
         blk = blocks + ((size_t)cunit * blocks_per_head + pb) * blk_elems;
         len = kBlock;
+        lblk = pb;
       }
     } else if (e < n_ent && PART != 1) {
       blk = window_kv + (int64_t)cunit * win_head_stride + (int64_t)c * win_block_stride;
       len = p - c * kBlock + 1;
+      lblk = c;
     }
-    if (blk != nullptr) attend_block<T, D>(q_group, G, blk, len, scale_log2, lane, m_run, l_run, o);
+    // the eviction-bias variant (resident cache: phys are block ids < nb)
+    const float* bias_blk = (bias != nullptr && blk != nullptr && lblk < nb)
+                                ? bias + ((size_t)cunit * nb + lblk) * kBlock : nullptr;
+    if (blk != nullptr) attend_block<T, D>(q_group, G, blk, len, scale_log2, lane, m_run, l_run, o, bias_blk);
   }
 
   __shared__ AttnLds<D, WAVES, GMAX> L;
@@ -395,7 +400,7 @@ static void launch_w(const LaunchAttn& a) {
   a.stream, (const typename T::storage*)a.q, (const typename T::storage*)a.blocks, a.blocks_per_head, a.phys, \
       a.n_sel, a.k_cap, (const typename T::storage*)a.window_kv, a.window_head_stride, a.window_block_stride,  \
       a.pos, scale_log2, a.n_q_heads, a.n_kv_heads, a.nb, (typename T::storage*)a.out, ticket, part_ml,        \
-      part_o, a.miss_list, a.n_miss, splits, a.n_query
+      part_o, a.miss_list, a.n_miss, splits, a.n_query, a.bias
   if (a.part < 0)
     hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, -1>), dim3(units, splits), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
   else if (a.part == 0)

@@ -148,11 +148,20 @@ __device__ __forceinline__ void block_pv(const Frags<T, D>& f, const float (&p)[
 // One wavefront: the unnormalised attention partial of tiles t0 .. t0+NTL-1
 // of one block whose operands are in f (load_tiles + load_q), the first
 // `len` tokens valid.  m, l are per head (lane column), o holds
-// O^T[d = 16*dt + 4*(lane/16) + i][head = lane%16].
+// O^T[d = 16*dt + 4*(lane/16) + i][head = lane%16].  bias_blk, when given,
+// points at the block's 64 per-token additive logits (natural-log units),
+// added to every head's logit of that token (the eviction-bias variant).
 template <class T, int D, int NTL>
 __device__ __forceinline__ void attend_frags(const Frags<T, D>& f, int t0, int len, float scale_log2, int lane,
-                                             float& m_out, float& l_out, f32x4 (&o)[D / 16]) {
+                                             float& m_out, float& l_out, f32x4 (&o)[D / 16],
+                                             const float* bias_blk = nullptr) {
   const int grp = lane >> 4;
+  // the 4 rows of a tile that a lane holds are 4 consecutive tokens
+  float4 bias[4];
+  if (bias_blk != nullptr) {
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) bias[t] = *reinterpret_cast<const float4*>(bias_blk + tile_token<T>(t0 + t, 4 * grp));
+  }
   f32x4 acc[4];
   block_scores<T, D, NTL>(f, acc);
   float x[4][4];
@@ -162,7 +171,12 @@ __device__ __forceinline__ void attend_frags(const Frags<T, D>& f, int t0, int l
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = tile_token<T>(t0 + t, 4 * grp + i);
-      x[t][i] = (tok < len) ? acc[t][i] * scale_log2 : -INFINITY;
+      float v = acc[t][i] * scale_log2;
+      if (bias_blk != nullptr) {
+        const float bv = i == 0 ? bias[t].x : (i == 1 ? bias[t].y : (i == 2 ? bias[t].z : bias[t].w));
+        v = fmaf(bv, 1.4426950408889634f, v);      // natural-log units to log2 units
+      }
+      x[t][i] = (tok < len) ? v : -INFINITY;
       mb = fmaxf(mb, x[t][i]);
     }
   mb = fmaxf(mb, __shfl_xor(mb, 16));
@@ -190,11 +204,11 @@ template <class T, int D, int NTL>
 __device__ __forceinline__ void attend_tiles(const typename T::storage* q_group, int G,
                                              const typename T::storage* blk, int t0, int len,
                                              float scale_log2, int lane, float& m_out,
-                                             float& l_out, f32x4 (&o)[D / 16]) {
+                                             float& l_out, f32x4 (&o)[D / 16], const float* bias_blk = nullptr) {
   Frags<T, D> f;
   load_tiles<T, D, NTL>(f, blk, t0, lane);
   load_q<T, D>(f, q_group, G, lane);
-  attend_frags<T, D, NTL>(f, t0, len, scale_log2, lane, m_out, l_out, o);
+  attend_frags<T, D, NTL>(f, t0, len, scale_log2, lane, m_out, l_out, o, bias_blk);
 }
 
 // A whole block (tiles 0..3).
@@ -202,8 +216,8 @@ template <class T, int D>
 __device__ __forceinline__ void attend_block(const typename T::storage* q_group, int G,
                                              const typename T::storage* blk, int len,
                                              float scale_log2, int lane, float& m_out,
-                                             float& l_out, f32x4 (&o)[D / 16]) {
-  attend_tiles<T, D, 4>(q_group, G, blk, 0, len, scale_log2, lane, m_out, l_out, o);
+                                             float& l_out, f32x4 (&o)[D / 16], const float* bias_blk = nullptr) {
+  attend_tiles<T, D, 4>(q_group, G, blk, 0, len, scale_log2, lane, m_out, l_out, o, bias_blk);
 }
 
 template <int D, int WAVES, int GMAX>

@@ -90,10 +90,10 @@ int nosa_pool_keys(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride
   return check_launch(fn);
 }
 
-int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query, const int32_t* pos,
-                       const void* k_comp, const float* e_blk, int32_t kq, int32_t ke,
+// nosa_select_blocks and its variant nosa_select_blocks_fill
+static int select_call(const char* fn, bool fill, const nosa_dims* dims, const void* q, int32_t n_query,
+                       const int32_t* pos, const void* k_comp, const float* e_blk, int32_t kq, int32_t ke,
                        int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
-  static const char* fn = "nosa_select_blocks";
   if (int rc = check_dims(dims, fn)) return rc;
   if (n_query < 1) return fail(NOSA_ERR_ARG, fn, "n_query must be >= 1");
   if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
@@ -116,6 +116,7 @@ int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query, co
   a.nb = dims->max_blocks;
   a.kq = kq;
   a.ke = ke;
+  a.fill = fill;
   a.q = q;
   a.pos = pos;
   a.k_comp = k_comp;
@@ -126,6 +127,20 @@ int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query, co
   a.stream = (hipStream_t)stream;
   nosa::launch_select(a);
   return check_launch(fn);
+}
+
+int nosa_select_blocks(const nosa_dims* dims, const void* q, int32_t n_query, const int32_t* pos,
+                       const void* k_comp, const float* e_blk, int32_t kq, int32_t ke,
+                       int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  return select_call("nosa_select_blocks", false, dims, q, n_query, pos, k_comp, e_blk, kq, ke, sel, n_sel, ws,
+                     ws_bytes, stream);
+}
+
+int nosa_select_blocks_fill(const nosa_dims* dims, const void* q, int32_t n_query, const int32_t* pos,
+                            const void* k_comp, const float* e_blk, int32_t kq, int32_t ke,
+                            int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  return select_call("nosa_select_blocks_fill", true, dims, q, n_query, pos, k_comp, e_blk, kq, ke, sel, n_sel, ws,
+                     ws_bytes, stream);
 }
 
 int nosa_select_blocks_shared(const nosa_dims* dims, const void* q, int32_t n_query, const int32_t* pos,
@@ -245,7 +260,7 @@ static int sparse_attn(const char* fn, int part, int n_query, const nosa_dims* d
                        int32_t blocks_per_head, const int32_t* phys, const int32_t* n_sel, int32_t k_cap,
                        const int32_t* miss_list, const int32_t* n_miss, const void* window_kv,
                        int64_t window_head_stride, int64_t window_block_stride, const int32_t* pos, float scale,
-                       void* out, void* ws, size_t ws_bytes, void* stream) {
+                       void* out, void* ws, size_t ws_bytes, void* stream, const float* bias = nullptr) {
   if (int rc = check_dims(dims, fn)) return rc;
   if (k_cap < 0 || k_cap > 512) return fail(NOSA_ERR_UNSUPPORTED, fn, "k_cap must be in [0, 512]");
   if (blocks_per_head < 1 && k_cap > 0) return fail(NOSA_ERR_ARG, fn, "blocks_per_head must be >= 1");
@@ -285,6 +300,7 @@ static int sparse_attn(const char* fn, int part, int n_query, const nosa_dims* d
   a.part = part;
   a.miss_list = miss_list;
   a.n_miss = n_miss;
+  a.bias = bias;
   a.stream = (hipStream_t)stream;
   nosa::launch_attn(a);
   return check_launch(fn);
@@ -298,6 +314,18 @@ int nosa_sparse_decode_attn(const nosa_dims* dims, const void* q, const void* bl
   return sparse_attn("nosa_sparse_decode_attn", -1, 1, dims, q, blocks, blocks_per_head, phys, n_sel, k_cap,
                      nullptr, nullptr, window_kv, window_head_stride, window_block_stride, pos, scale, out, ws,
                      ws_bytes, stream);
+}
+
+int nosa_sparse_decode_attn_bias(const nosa_dims* dims, const void* q, const void* kv, const int32_t* sel,
+                                 const int32_t* n_sel, int32_t k_cap, const int32_t* pos, float scale,
+                                 const float* evict_logits, void* out, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "nosa_sparse_decode_attn_bias";
+  if (int rc = check_dims(dims, fn)) return rc;
+  if (!evict_logits) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
+  // the resident cache, each window read from it
+  const int64_t blk = (int64_t)2 * 64 * dims->head_dim;
+  return sparse_attn(fn, -1, 1, dims, q, kv, dims->max_blocks, sel, n_sel, k_cap, nullptr, nullptr, kv,
+                     dims->max_blocks * blk, blk, pos, scale, out, ws, ws_bytes, stream, evict_logits);
 }
 
 int nosa_sparse_decode_attn_pool(const nosa_dims* dims, const void* q, const void* pool, int32_t pool_slots,

@@ -28,6 +28,7 @@ struct LaunchSelect {
   int head_dim;
   int batch, n_query, n_q_heads, n_kv_heads, nb;
   int kq, ke;
+  bool fill;                   // Eq. 7 filled from the candidates left (a variant, off by default)
   const void* q;
   const int32_t* pos;
   const void* k_comp;
@@ -78,6 +79,7 @@ struct LaunchAttn {
   int part;                    // -1 whole step; 0 / 1 the two parts of a pool step
   const int32_t* miss_list;    // parts 0 and 1: the fetch's miss list and counts
   const int32_t* n_miss;
+  const float* bias;           // per-token eviction logits added to the attention logits, or NULL
   hipStream_t stream;
 };
 

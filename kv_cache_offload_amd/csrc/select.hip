@@ -58,7 +58,7 @@ template <class T, int D>
 __global__ void __launch_bounds__(kSelThreads) select_kernel(
     const typename T::storage* __restrict__ q, const int32_t* __restrict__ pos,
     const typename T::storage* __restrict__ k_comp, const float* __restrict__ e_blk, int n_query,
-    int n_q_heads, int n_kv_heads, int nb, int kq, int ke, int32_t* __restrict__ sel,
+    int n_q_heads, int n_kv_heads, int nb, int kq, int ke, int fill, int32_t* __restrict__ sel,
     int32_t* __restrict__ n_sel, int32_t* __restrict__ ticket, float* __restrict__ score) {
   const int G = n_q_heads / n_kv_heads;
   const int row = blockIdx.y;             // (b * n_query + r) * Hkv + h
@@ -134,8 +134,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   }
   __syncthreads();
   const int half = tid / kHalf;
-  select_top<kHalf>(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, s_hist[half],
+  // the fill variant takes the eviction scores' top ke + nq, trimmed below
+  const int ke_top = fill ? min(c, ke + min(kq, c)) : ke;
+  select_top<kHalf>(half ? key_e : key_q, c, half ? ke_top : kq, half ? flag_e : flag_q, s_hist[half],
                     s_small[half], half ? blist_e : blist_q, tid % kHalf);
+  if (fill) keep_fill<kSelThreads>(key_e, flag_q, flag_e, c, ke, reinterpret_cast<int32_t*>(key_q), s_wsum, tid);
 
   // ---- union in ascending order
   const int total = write_union<kSelThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
@@ -234,7 +237,7 @@ __global__ void __launch_bounds__(kMThreads) mscan_kernel(const uint16_t* __rest
 template <class T>
 __global__ void __launch_bounds__(kTopkThreads) mtopk_kernel(const int32_t* __restrict__ pos, const float* __restrict__ e_blk,
                                                           const float* __restrict__ score, int n_query, int n_kv_heads,
-                                                          int nb, int kq, int ke, int32_t* __restrict__ sel,
+                                                          int nb, int kq, int ke, int fill, int32_t* __restrict__ sel,
                                                           int32_t* __restrict__ n_sel) {
   constexpr int kH = kTopkThreads / 2;
   const int row = blockIdx.x;               // (b * n_query + r) * Hkv + h
@@ -267,8 +270,10 @@ __global__ void __launch_bounds__(kTopkThreads) mtopk_kernel(const int32_t* __re
   }
   __syncthreads();
   const int half = tid / kH;
-  select_top<kH>(half ? key_e : key_q, c, half ? ke : kq, half ? flag_e : flag_q, s_hist[half], s_small[half],
+  const int ke_top = fill ? min(c, ke + min(kq, c)) : ke;
+  select_top<kH>(half ? key_e : key_q, c, half ? ke_top : kq, half ? flag_e : flag_q, s_hist[half], s_small[half],
                  half ? blist_e : blist_q, tid % kH);
+  if (fill) keep_fill<kTopkThreads>(key_e, flag_q, flag_e, c, ke, reinterpret_cast<int32_t*>(key_q), s_wsum, tid);
   const int total = write_union<kTopkThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
   if (tid == 0) n_sel[row] = total;
 }
@@ -295,7 +300,7 @@ static bool launch_multi(const LaunchSelect& a) {
     default: return false;
   }
   hipLaunchKernelGGL((mtopk_kernel<Bf16>), dim3(rows), dim3(kTopkThreads), select_lds_bytes(a.nb), a.stream, a.pos,
-                     a.e_blk, score, a.n_query, a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel);
+                     a.e_blk, score, a.n_query, a.n_kv_heads, a.nb, a.kq, a.ke, a.fill ? 1 : 0, a.sel, a.n_sel);
   return true;
 }
 
@@ -493,7 +498,7 @@ static void launch(const LaunchSelect& a) {
   hipLaunchKernelGGL((select_kernel<T, D>), dim3(splits, rows), dim3(kSelThreads),
                      select_lds_bytes(a.nb), a.stream, (const typename T::storage*)a.q, a.pos,
                      (const typename T::storage*)a.k_comp, a.e_blk, a.n_query, a.n_q_heads,
-                     a.n_kv_heads, a.nb, a.kq, a.ke, a.sel, a.n_sel, ticket, score);
+                     a.n_kv_heads, a.nb, a.kq, a.ke, a.fill ? 1 : 0, a.sel, a.n_sel, ticket, score);
 }
 
 void launch_select(const LaunchSelect& a) {

@@ -314,6 +314,31 @@ __device__ int write_ids(Pick pick, int c, int32_t* out, int k_cap, int* wsum, i
   return total;
 }
 
+// Eq. 7 read as "fill the remainder from the candidates left" (a variant,
+// off by default): given flag_q = Gamma_q and flag_e = the top ke + nq of the
+// eviction scores (nq = |Gamma_q|), keep in flag_e only the ke best (key
+// desc, id asc) of its members outside Gamma_q.  That is the top-ke of the
+// eviction scores over the candidates outside Gamma_q, since at most nq of
+// the top ke + nq lie in Gamma_q.  list: scratch of at least ke + nq ints.
+template <int NT>
+__device__ void keep_fill(const uint32_t* key_e, const uint8_t* flag_q, uint8_t* flag_e, int c, int ke,
+                          int32_t* list, int* wsum, int tid) {
+  const int n = write_ids<NT>([&](int j) { return flag_e[j] != 0 && flag_q[j] == 0; }, c, list, 0, wsum, tid);
+  __syncthreads();
+  for (int a = tid; a < n; a += NT) {
+    const int ia = list[a];
+    const uint32_t ua = key_e[ia];
+    int rank = 0;
+    for (int b2 = 0; b2 < n; ++b2) {
+      const int ib = list[b2];
+      const uint32_t ub = key_e[ib];
+      rank += (ub > ua) || (ub == ua && ib < ia);
+    }
+    if (rank >= ke) flag_e[ia] = 0;
+  }
+  __syncthreads();
+}
+
 // The union of two flag arrays, ascending (see write_ids).
 template <int NT>
 __device__ int write_union(const uint8_t* flag_q, const uint8_t* flag_e, int c, int32_t* out,

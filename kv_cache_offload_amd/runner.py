@@ -149,9 +149,17 @@ class DecodeLayer:
                      self.e_sub, self.e_blk, stream=stream)
 
     # -- one decode step -------------------------------------------------
-    def select(self, q: torch.Tensor, pos: torch.Tensor, stream=None) -> None:
-        nb.select_blocks(self.dims, q, 1, pos, self.k_comp, self.e_blk, self.kq, self.ke, self.sel,
-                         self.n_sel, self.ws_sel, stream=stream)
+    def select(self, q: torch.Tensor, pos: torch.Tensor, stream=None, fill: bool = False) -> None:
+        """nosa_select_blocks, or with fill=True its variant nosa_select_blocks_fill."""
+        call = nb.select_blocks_fill if fill else nb.select_blocks
+        call(self.dims, q, 1, pos, self.k_comp, self.e_blk, self.kq, self.ke, self.sel, self.n_sel, self.ws_sel,
+             stream=stream)
+
+    def attend_resident_bias(self, q: torch.Tensor, kv: torch.Tensor, pos: torch.Tensor, logits: torch.Tensor,
+                             stream=None) -> None:
+        """nosa_sparse_decode_attn_bias: the eviction logits added to the attention logits."""
+        nb.sparse_decode_attn_bias(self.dims, q, kv, self.sel, self.n_sel, self.k, pos, self.scale, logits,
+                                   self.out, self.ws_attn, stream=stream)
 
     def attend_resident(self, q: torch.Tensor, kv: torch.Tensor, pos: torch.Tensor, stream=None) -> None:
         nb.sparse_decode_attn(self.dims, q, kv, self.NB, self.sel, self.n_sel, self.k, kv,

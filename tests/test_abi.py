@@ -279,3 +279,23 @@ def test_static_step_rejects_a_workspace_above_its_size(lib):
         nb.decode_step_static(d, FAKE, FAKE, FAKE, FAKE, 16, 48, FAKE, None, FAKE, FAKE, FAKE, stream=0)
     assert e.value.code == nb.ERR_WORKSPACE
     assert "16 MiB" in lib.nosa_last_error().decode()
+
+
+def test_variant_calls_check_like_their_bases(lib):
+    d = _d()
+    need = nb.workspace_size(d, nb.OP_SELECT, 1, 16, 48)
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks_fill(d, FAKE, 1, FAKE, FAKE, FAKE, 16, 48, FAKE, FAKE, FAKE, ws_bytes=need - 1, stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
+    with pytest.raises(nb.NosaError) as e:
+        nb.select_blocks_fill(d, FAKE, 0, FAKE, FAKE, FAKE, 16, 48, FAKE, FAKE, FAKE, ws_bytes=need, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    need_a = nb.workspace_size(d, nb.OP_ATTN, 1, 64, 0)
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_decode_attn_bias(d, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None, FAKE, FAKE, ws_bytes=need_a,
+                                   stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.sparse_decode_attn_bias(d, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, FAKE, FAKE, ws_bytes=need_a - 1,
+                                   stream=0)
+    assert e.value.code == nb.ERR_WORKSPACE
