@@ -143,6 +143,33 @@ int nosa_pool_keys(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride
                    int32_t blk_end, void* k_comp, float* e_sub, float* e_blk, void* stream);
 
 /*
+ * nosa_pool_keys_entries -- nosa_pool_keys for one block per batch entry,
+ * the block named on the device.
+ *
+ * The sequences of a batch sit at their own positions, so their windows
+ * complete blocks on different steps; NOSI's memory manager handles each
+ * sequence's blocks as units of its own (montaan summary, "System
+ * Optimization (NOSI)" item 2).  For every b with 0 <= entry_block[b] < NB
+ * and every KV head h, block j = entry_block[b] of (b, h) is pooled exactly
+ * as nosa_pool_keys pools it (same formulas, same bit-exact results); entries
+ * with any other value are skipped and nothing of theirs is written.
+ *
+ *   entry_block   device int32 [B]    (read; the caller's, not kept)
+ *   kv, strides   as for nosa_pool_keys: block j of (b, h) starts at element
+ *                 (b*Hkv + h) * kv_unit_stride + j * kv_block_stride; a
+ *                 window buffer [B][Hkv][block] holding each entry's just
+ *                 completed block has strides block and 0
+ *   evict_logits, k_comp, e_sub, e_blk    as for nosa_pool_keys
+ * Errors: -1 for a NULL entry_block or buffer, or negative strides.  The
+ * block indices are read on the device, so one launch serves any mix of
+ * entries (a graph can hold it).
+ */
+int nosa_pool_keys_entries(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride,
+                           int64_t kv_block_stride, const float* evict_logits,
+                           const int32_t* entry_block, void* k_comp, float* e_sub, float* e_blk,
+                           void* stream);
+
+/*
  * nosa_select_blocks -- the blocks each query row attends (Eq. 7).
  *
  * Defined by the montaan summary ("How it works": one Top-k over the query

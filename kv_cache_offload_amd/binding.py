@@ -26,7 +26,7 @@ EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_status_str", "nosa_last_error", "nosa_update_pool", "nosa_gather_blocks",
            "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn", "nosa_split_qkv",
            "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static",
-           "nosa_select_blocks_fill", "nosa_sparse_decode_attn_bias")
+           "nosa_select_blocks_fill", "nosa_sparse_decode_attn_bias", "nosa_pool_keys_entries")
 
 
 class NosaError(RuntimeError):
@@ -55,6 +55,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     D = ctypes.POINTER(Dims)
     lib.nosa_pool_keys.argtypes = [D, P, I64, I64, P, I32, I32, P, P, P, P]
+    lib.nosa_pool_keys_entries.argtypes = [D, P, I64, I64, P, P, P, P, P, P]
     lib.nosa_select_blocks.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
     lib.nosa_select_blocks_shared.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
     lib.nosa_select_blocks_fill.argtypes = [D, P, I32, P, P, P, I32, I32, P, P, P, SZ, P]
@@ -78,7 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks", "nosa_sparse_decode_attn",
                  "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool",
                  "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static",
-                 "nosa_select_blocks_fill", "nosa_sparse_decode_attn_bias"):
+                 "nosa_select_blocks_fill", "nosa_sparse_decode_attn_bias", "nosa_pool_keys_entries"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -129,6 +130,14 @@ def pool_keys(d: Dims, kv, kv_unit_stride: int, kv_block_stride: int, evict_logi
                                _ptr(evict_logits), blk_begin, blk_end, _ptr(k_comp), _ptr(e_sub),
                                _ptr(e_blk), _stream(stream))
     _check("nosa_pool_keys", rc)
+
+
+def pool_keys_entries(d: Dims, kv, kv_unit_stride: int, kv_block_stride: int, evict_logits, entry_block,
+                      k_comp, e_sub, e_blk, stream=None) -> None:
+    rc = load().nosa_pool_keys_entries(ctypes.byref(d), _ptr(kv), kv_unit_stride, kv_block_stride,
+                                       _ptr(evict_logits), _ptr(entry_block), _ptr(k_comp), _ptr(e_sub),
+                                       _ptr(e_blk), _stream(stream))
+    _check("nosa_pool_keys_entries", rc)
 
 
 def select_blocks(d: Dims, q, n_query: int, pos, k_comp, e_blk, kq: int, ke: int, sel, n_sel,

@@ -60,10 +60,11 @@ constexpr int kMaxStepK = 256;          // the fused step keeps its lists in LDS
 
 extern "C" {
 
-int nosa_pool_keys(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride,
-                   int64_t kv_block_stride, const float* evict_logits, int32_t blk_begin,
-                   int32_t blk_end, void* k_comp, float* e_sub, float* e_blk, void* stream) {
-  static const char* fn = "nosa_pool_keys";
+// nosa_pool_keys (a block range shared by the batch) and nosa_pool_keys_entries
+// (one block per batch entry, named on the device)
+static int pool_call(const char* fn, const nosa_dims* dims, const void* kv, int64_t kv_unit_stride,
+                     int64_t kv_block_stride, const float* evict_logits, int32_t blk_begin, int32_t blk_end,
+                     const int32_t* entry_block, void* k_comp, float* e_sub, float* e_blk, void* stream) {
   if (int rc = check_dims(dims, fn)) return rc;
   if (!kv || !evict_logits || !k_comp || !e_sub || !e_blk)
     return fail(NOSA_ERR_ARG, fn, "NULL buffer");
@@ -78,6 +79,8 @@ int nosa_pool_keys(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride
   a.nb = dims->max_blocks;
   a.blk_begin = blk_begin;
   a.n_blk = blk_end - blk_begin;
+  a.entry_block = entry_block;
+  a.n_kv_heads = dims->n_kv_heads;
   a.kv = kv;
   a.kv_unit_stride = kv_unit_stride;
   a.kv_block_stride = kv_block_stride;
@@ -88,6 +91,22 @@ int nosa_pool_keys(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride
   a.stream = (hipStream_t)stream;
   nosa::launch_pool_keys(a);
   return check_launch(fn);
+}
+
+int nosa_pool_keys(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride,
+                   int64_t kv_block_stride, const float* evict_logits, int32_t blk_begin,
+                   int32_t blk_end, void* k_comp, float* e_sub, float* e_blk, void* stream) {
+  return pool_call("nosa_pool_keys", dims, kv, kv_unit_stride, kv_block_stride, evict_logits, blk_begin,
+                   blk_end, nullptr, k_comp, e_sub, e_blk, stream);
+}
+
+int nosa_pool_keys_entries(const nosa_dims* dims, const void* kv, int64_t kv_unit_stride,
+                           int64_t kv_block_stride, const float* evict_logits, const int32_t* entry_block,
+                           void* k_comp, float* e_sub, float* e_blk, void* stream) {
+  static const char* fn = "nosa_pool_keys_entries";
+  if (!entry_block) return fail(NOSA_ERR_ARG, fn, "NULL entry_block");
+  return pool_call(fn, dims, kv, kv_unit_stride, kv_block_stride, evict_logits, 0, 1, entry_block, k_comp,
+                   e_sub, e_blk, stream);
 }
 
 // nosa_select_blocks and its variant nosa_select_blocks_fill

@@ -14,6 +14,8 @@ struct LaunchPool {
   int64_t n_units;  // B * Hkv
   int nb;           // blocks per unit in the cache
   int blk_begin, n_blk;
+  const int32_t* entry_block;  // device [B] block per batch entry (n_blk = 1), or null
+  int n_kv_heads;
   const void* kv;
   int64_t kv_unit_stride, kv_block_stride;  // elements
   const float* logits;

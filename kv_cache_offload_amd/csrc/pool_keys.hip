@@ -25,7 +25,7 @@ template <class T, int D>
 __global__ void __launch_bounds__((64 * pool_waves<T, D>())) pool_keys_kernel(
     const typename T::storage* __restrict__ kv, int64_t kv_unit_stride, int64_t kv_block_stride,
     const float* __restrict__ logits, int64_t n_units, int nb, int blk_begin, int n_blk,
-    typename T::storage* __restrict__ k_comp,
+    const int32_t* __restrict__ entry_block, int hkv, typename T::storage* __restrict__ k_comp,
     float* __restrict__ e_sub, float* __restrict__ e_blk) {
   constexpr int EPC = T::kPer16B;              // elements per 16-byte chunk
   constexpr int LPR = D / EPC;                 // chunks per key row
@@ -37,8 +37,14 @@ __global__ void __launch_bounds__((64 * pool_waves<T, D>())) pool_keys_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t item = (int64_t)blockIdx.x * kPoolWaves + wave;   // (unit, block)
   if (item >= n_units * n_blk) return;
-  const int jb = blk_begin + (int)(item % n_blk);
   const int64_t unit = item / n_blk;
+  // a block range shared by the batch, or (n_blk = 1) the one block the
+  // unit's batch entry names; a whole wavefront leaves together
+  int jb = blk_begin + (int)(item % n_blk);
+  if (entry_block != nullptr) {
+    jb = entry_block[unit / hkv];
+    if (jb < 0 || jb >= nb) return;
+  }
   const typename T::storage* keys = kv + unit * kv_unit_stride + (int64_t)jb * kv_block_stride;
 
   // stage the keys: fragment f, lane l -> chunk 64 f + l (contiguous loads)
@@ -100,8 +106,8 @@ static void launch(const LaunchPool& a) {
   const int64_t grid = (items + kPoolWaves - 1) / kPoolWaves;
   hipLaunchKernelGGL((pool_keys_kernel<T, D>), dim3((unsigned)grid), dim3(64 * kPoolWaves), 0, a.stream,
                      (const typename T::storage*)a.kv, a.kv_unit_stride, a.kv_block_stride,
-                     a.logits, a.n_units, a.nb, a.blk_begin,
-                     a.n_blk, (typename T::storage*)a.k_comp, a.e_sub, a.e_blk);
+                     a.logits, a.n_units, a.nb, a.blk_begin, a.n_blk, a.entry_block, a.n_kv_heads,
+                     (typename T::storage*)a.k_comp, a.e_sub, a.e_blk);
 }
 
 void launch_pool_keys(const LaunchPool& a) {

@@ -148,6 +148,17 @@ class DecodeLayer:
         nb.pool_keys(self.dims, window, self.blk_elems, 0, logits, block, block + 1, self.k_comp,
                      self.e_sub, self.e_blk, stream=stream)
 
+    def pool_entries(self, kv: torch.Tensor, logits: torch.Tensor, entry_block: torch.Tensor,
+                     unit_stride: Optional[int] = None, block_stride: Optional[int] = None, stream=None) -> None:
+        """Compressed keys of one block per batch entry (entry_block: device
+        int32 [B], -1 for none), read from the HBM cache, or with
+        unit_stride = block and block_stride = 0 from a window buffer
+        [B, Hkv, block] holding each entry's block."""
+        us = self.NB * self.blk_elems if unit_stride is None else unit_stride
+        bs = self.blk_elems if block_stride is None else block_stride
+        nb.pool_keys_entries(self.dims, kv, us, bs, logits, entry_block, self.k_comp, self.e_sub, self.e_blk,
+                             stream=stream)
+
     # -- one decode step -------------------------------------------------
     def select(self, q: torch.Tensor, pos: torch.Tensor, stream=None, fill: bool = False) -> None:
         """nosa_select_blocks, or with fill=True its variant nosa_select_blocks_fill."""

@@ -377,7 +377,8 @@ def decode_unit(K: np.ndarray, V: np.ndarray, lam: np.ndarray, q_rows: np.ndarra
                 positions: Sequence[int], kq: int, ke: int, bf16: bool,
                 pool_slots: Optional[int] = None, attend: bool = True,
                 forced_sel: Optional[Dict[int, List[int]]] = None,
-                fill_remaining: bool = False, evict_bias: bool = False) -> UnitTrace:
+                fill_remaining: bool = False, evict_bias: bool = False,
+                pool_reset_at: Optional[int] = None) -> UnitTrace:
     """Run the path for one (batch, KV head) over consecutive decode positions.
 
     K, V: [T, D]; lam: [T]; q_rows: [n, G, D]; positions: the n positions.
@@ -385,6 +386,8 @@ def decode_unit(K: np.ndarray, V: np.ndarray, lam: np.ndarray, q_rows: np.ndarra
     own (used to keep lock-step when a score tie is accepted).
     `fill_remaining` selects with reading U21 (gamma_e then holds the
     query-agnostic part), `evict_bias` attends with reading U22.
+    `pool_reset_at`: at that step the pool starts again empty (a restart that
+    forgets every resident block; the selection is not affected).
     """
     kbar = subblock_key_means(K, bf16)
     E = block_eviction_scores(subblock_logit_means(lam))
@@ -404,6 +407,8 @@ def decode_unit(K: np.ndarray, V: np.ndarray, lam: np.ndarray, q_rows: np.ndarra
         tr.gamma_e.append(g_e)
         tr.sel.append(S)
         if pool is not None:
+            if t == pool_reset_at:
+                pool = BlockPool(pool_slots)
             insert = prev_c if (prev_c is not None and c > prev_c) else None
             misses, ins_slot, phys = pool.step(t, S, insert)
             tr.misses.append(misses)

@@ -79,21 +79,25 @@ def unit_selections(S_rows, N_rows, b, h) -> List[List[int]]:
     return [list(S[b, h, :N[b, h]]) for S, N in zip(S_rows, N_rows)]
 
 
-def oracle_scores(w: NI.Workload, K, V, lam, q, b, h):
+def oracle_scores(w: NI.Workload, K, V, lam, q, b, h, positions=None):
     """Oracle per-step selection data for unit (b, h): s_q, E, own selections."""
     G = w.group
     qrows = q[:, b, h * G:(h + 1) * G]
-    tr = O.decode_unit(K[b, h], V[b, h], lam[b, h], qrows, w.positions()[: q.shape[0]], w.kq, w.ke,
+    positions = w.positions() if positions is None else positions
+    tr = O.decode_unit(K[b, h], V[b, h], lam[b, h], qrows, positions[: q.shape[0]], w.kq, w.ke,
                        bf16=(w.dtype == "bf16"), attend=False)
     E = O.block_eviction_scores(O.subblock_logit_means(lam[b, h]))
     return tr, E
 
 
-def compare_unit(w: NI.Workload, K, V, lam, q, b, h, gpu_sel, gpu_out=None, gpu_pool=None):
-    """Check one (b, h) unit of a GPU run against the oracle; returns stats."""
+def compare_unit(w: NI.Workload, K, V, lam, q, b, h, gpu_sel, gpu_out=None, gpu_pool=None, positions=None,
+                 pool_reset_at=None):
+    """Check one (b, h) unit of a GPU run against the oracle; returns stats.
+    positions: the unit's own positions (default: the workload's);
+    pool_reset_at: step at which the oracle's pool starts again empty."""
     G = w.group
-    positions = w.positions()
-    tr, E = oracle_scores(w, K, V, lam, q, b, h)
+    positions = w.positions() if positions is None else positions
+    tr, E = oracle_scores(w, K, V, lam, q, b, h, positions)
     forced: Dict[int, List[int]] = {}
     ties = 0
     for t, S in enumerate(gpu_sel):
@@ -109,7 +113,7 @@ def compare_unit(w: NI.Workload, K, V, lam, q, b, h, gpu_sel, gpu_out=None, gpu_
     qrows = q[:, b, h * G:(h + 1) * G]
     tr2 = O.decode_unit(K[b, h], V[b, h], lam[b, h], qrows, positions[: len(gpu_sel)], w.kq, w.ke,
                         bf16=(w.dtype == "bf16"), pool_slots=w.pool_slots if gpu_pool else None,
-                        attend=gpu_out is not None, forced_sel=forced)
+                        attend=gpu_out is not None, forced_sel=forced, pool_reset_at=pool_reset_at)
     err = 0.0
     if gpu_out is not None:
         for t in range(len(gpu_sel)):
@@ -122,28 +126,48 @@ def compare_unit(w: NI.Workload, K, V, lam, q, b, h, gpu_sel, gpu_out=None, gpu_
 
 
 def run_offload(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None, side_stream: bool = True,
-                record_tables: bool = True):
-    """GPU decode in offload mode (KV in pinned host memory, HBM block pool)."""
+                record_tables: bool = True, offsets=None, reset_at: Optional[int] = None):
+    """GPU decode in offload mode (KV in pinned host memory, HBM block pool).
+
+    offsets: per batch entry, how many positions it lags the workload's
+    (entry b decodes position p_t - offsets[b] at step t), so the entries'
+    windows complete blocks on different steps: each step pools and inserts
+    the blocks that just completed, per entry.  reset_at: before that step
+    the pool tables are cleared (a cold restart: every resident block is
+    forgotten, the compressed keys are kept)."""
     n = w.n_steps if steps is None else steps
-    kv_dev, logits, qd, pos = device_inputs(w, K, V, lam, q)
+    kv_dev, logits, qd, _ = device_inputs(w, K, V, lam, q)
+    offs = np.zeros(w.batch, np.int64) if offsets is None else np.asarray(offsets, np.int64)
+    P = w.positions()[:n, None].astype(np.int64) - offs[None, :]          # [n, B]
+    assert P.min() >= 0
+    pos = torch.from_numpy(P.astype(np.int32)).cuda()
     host = kv_dev.cpu().pin_memory()
     layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq,
                           w.ke, pool_slots=w.pool_slots)
-    positions = w.positions()
-    c_prev = int(positions[0]) // 64
-    layer.pool_blocks(kv_dev, logits, 0, c_prev)          # prefill: the prompt's complete blocks
-    windows = {c: kv_dev[:, :, c].clone() for c in sorted({int(p) // 64 for p in positions[:n]})}
-    del kv_dev
+    C = P // 64                                                             # window block per step, entry
+    c_prev = C[0].copy()
+    lo = int(c_prev.min())
+    layer.pool_blocks(kv_dev, logits, 0, lo)          # prefill: blocks complete for every entry
+    for j in range(lo, int(c_prev.max())):            # and the ones complete for some entries only
+        eb = torch.from_numpy(np.where(j < c_prev, j, -1).astype(np.int32)).cuda()
+        layer.pool_entries(kv_dev, logits, eb)
+    bidx = torch.arange(w.batch, device="cuda")
+    blocks_of = lambda c: kv_dev[bidx, :, torch.from_numpy(c).cuda()]      # [B, Hkv, block]
     side = torch.cuda.Stream() if side_stream else None
     rec = {k: [] for k in ("sel", "n_sel", "out", "phys", "miss_list", "n_miss", "block_table", "slot_block")}
     for t in range(n):
-        c = int(positions[t]) // 64
+        c = C[t]
         ins_blk = ins_src = None
-        if c > c_prev:
-            layer.pool_window(windows[c_prev], logits, c_prev)
-            ins_blk = torch.full((w.batch,), c_prev, dtype=torch.int32, device="cuda")
-            ins_src = windows[c_prev]
-        layer.step_offload(qd[t], host, windows[c], pos[t], t, ins_blk, ins_src, side)
+        done = c > c_prev
+        if done.any():
+            ins_src = blocks_of(c_prev).contiguous()
+            ins_blk = torch.from_numpy(np.where(done, c_prev, -1).astype(np.int32)).cuda()
+            layer.pool_entries(ins_src, logits, ins_blk, layer.blk_elems, 0)
+        if reset_at is not None and t == reset_at:
+            for k in ("block_table", "slot_block", "slot_last_use"):
+                getattr(layer, k).fill_(-1)
+        window = blocks_of(c).contiguous()
+        layer.step_offload(qd[t], host, window, pos[t], t, ins_blk, ins_src, side)
         for k in ("sel", "n_sel", "phys", "miss_list", "n_miss"):
             rec[k].append(getattr(layer, k).clone())
         rec["out"].append(layer.out.float().clone())
@@ -152,14 +176,18 @@ def run_offload(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None, side_
             rec["slot_block"].append(layer.slot_block.clone())
         c_prev = c
     torch.cuda.synchronize()
+    del kv_dev
     out = {k: [x.cpu().numpy() for x in v] for k, v in rec.items()}
+    out["positions"] = P
     return out, layer, host
 
 
-def check_offload_unit(w: NI.Workload, K, V, lam, q, rec, b, h):
+def check_offload_unit(w: NI.Workload, K, V, lam, q, rec, b, h, pool_reset_at=None):
     """Oracle comparison of one unit of an offload run: selections, outputs, pool."""
+    positions = rec["positions"][:, b] if "positions" in rec else w.positions()[: len(rec["sel"])]
     sels = unit_selections(rec["sel"], rec["n_sel"], b, h)
-    st = compare_unit(w, K, V, lam, q, b, h, sels, gpu_out=rec["out"], gpu_pool=True)
+    st = compare_unit(w, K, V, lam, q, b, h, sels, gpu_out=rec["out"], gpu_pool=True, positions=positions,
+                      pool_reset_at=pool_reset_at)
     tr = st["trace"]
     for t in range(len(sels)):
         nm = int(rec["n_miss"][t][b, h])
@@ -167,7 +195,7 @@ def check_offload_unit(w: NI.Workload, K, V, lam, q, rec, b, h):
         got = [tuple(int(x) for x in ml[i]) for i in range(nm)]
         assert got == [tuple(m) for m in tr.misses[t]], (b, h, t, got, tr.misses[t])
         ins = tuple(int(x) for x in ml[w.kq + w.ke])
-        exp_ins = (-1, -1) if tr.insert_slot[t] < 0 else (int(w.positions()[t]) // 64 - 1, tr.insert_slot[t])
+        exp_ins = (-1, -1) if tr.insert_slot[t] < 0 else (int(positions[t]) // 64 - 1, tr.insert_slot[t])
         assert ins == exp_ins, (b, h, t, ins, exp_ins)
         assert list(rec["phys"][t][b, h, : len(sels[t])]) == tr.phys[t]
     st["misses"] = sum(len(m) for m in tr.misses)

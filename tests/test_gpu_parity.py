@@ -217,7 +217,7 @@ def test_attention_dense_equivalence():
     assert float((out[0] - ref.float()).abs().max()) <= 2e-2
 
 
-def test_attention_split_counts_and_repeats_agree():
+def test_attention_repeats_are_bit_identical():
     _banner("attention determinism across repeats")
     w = _w("layer32k", batch=4, prompt_len=64 * 100 + 20, n_steps=3)
     K, V, lam, q = NI.layer_inputs(w)
@@ -227,6 +227,87 @@ def test_attention_split_counts_and_repeats_agree():
         assert np.array_equal(a, b)
     for a, b in zip(o1, o2):
         assert np.array_equal(a, b)
+
+
+def test_determinism_across_split_counts_and_launch_orders():
+    """The same step computed with other work decompositions and launch
+    orders: the selected sets must be identical and the outputs agree within
+    the output tolerance (bit for bit where the decomposition is the same).
+
+      * attention split count: the same sets in rows of 64, 96 and 200
+        entries (9, 13 and 26 splits of 8 blocks per unit);
+      * one-launch step worker count: batch 16 (32 units, 8 workers per unit)
+        against each entry run alone (2 units, 16 workers per unit); the
+        separate calls keep their decomposition per unit, so there the outputs
+        are bit-identical;
+      * launch order: two layers' steps interleaved on two streams against
+        the same steps run one layer after the other;
+      * the offload step with and without the side stream: identical pool
+        tables, miss lists and slots."""
+    _banner("determinism: split counts, worker counts, launch orders")
+    w = _w("layer32k", batch=16, prompt_len=64 * 100 + 20, n_steps=3)
+    K, V, lam, q = NI.layer_inputs(w)
+    atol = H.ATOL[w.dtype]
+    s_ref, n_ref, o_ref, L = H.run_resident(w, K, V, lam, q)
+    s_f, n_f, o_f, _ = H.run_resident(w, K, V, lam, q, fused=True)
+    kv, logits, qd, pos = H.device_inputs(w, K, V, lam, q)
+    k = w.kq + w.ke
+    for t in range(w.n_steps):
+        assert np.array_equal(s_f[t], s_ref[t]) and np.array_equal(n_f[t], n_ref[t])
+        assert float(np.abs(o_f[t] - o_ref[t]).max()) <= atol
+    # attention split counts
+    for k_cap in (96, 200):
+        ws = torch.zeros(nb.workspace_size(L.dims, nb.OP_ATTN, 1, k_cap, 0), dtype=torch.uint8, device="cuda")
+        out = torch.zeros_like(L.out)
+        for t in range(w.n_steps):
+            sel = torch.full((w.batch, w.n_kv_heads, k_cap), -1, dtype=torch.int32, device="cuda")
+            sel[..., :k] = torch.from_numpy(s_ref[t]).cuda()
+            n_sel = torch.from_numpy(n_ref[t]).cuda()
+            nb.sparse_decode_attn(L.dims, qd[t], kv, L.NB, sel, n_sel, k_cap, kv, L.NB * L.blk_elems, L.blk_elems,
+                                  pos[t], None, out, ws)
+            torch.cuda.synchronize()
+            e = float(np.abs(out.float().cpu().numpy() - o_ref[t]).max())
+            assert e <= atol, (k_cap, t, e)
+    # worker counts (one-launch step) and grid size (separate calls)
+    w1 = NI.scaled(w, batch=1)
+    for b in (0, 5, 15):
+        sl = slice(b, b + 1)
+        s1, n1, o1, _ = H.run_resident(w1, K[sl], V[sl], lam[sl], q[:, sl])
+        s1f, n1f, o1f, _ = H.run_resident(w1, K[sl], V[sl], lam[sl], q[:, sl], fused=True)
+        for t in range(w.n_steps):
+            assert np.array_equal(s1[t][0], s_ref[t][b]) and np.array_equal(s1f[t][0], s_ref[t][b])
+            assert np.array_equal(o1[t][0], o_ref[t][b])
+            assert float(np.abs(o1f[t][0] - o_ref[t][b]).max()) <= atol
+    # launch order: two layers on two streams, steps interleaved
+    layers = [R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
+              for _ in range(2)]
+    c0 = int(w.positions()[0]) // 64
+    for Lx in layers:
+        Lx.pool_blocks(kv, logits, 0, c0)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [[], []]
+    for t in range(w.n_steps):
+        for i in (1, 0):
+            with torch.cuda.stream(streams[i]):
+                (layers[i].step_fused if i else layers[i].step_resident)(qd[t], kv, pos[t], streams[i])
+                got[i].append((layers[i].sel.clone(), layers[i].out.float().clone()))
+    torch.cuda.synchronize()
+    for t in range(w.n_steps):
+        assert np.array_equal(got[0][t][0].cpu().numpy(), s_ref[t])
+        assert np.array_equal(got[1][t][0].cpu().numpy(), s_ref[t])
+        assert np.array_equal(got[0][t][1].cpu().numpy(), o_ref[t])
+        assert np.array_equal(got[1][t][1].cpu().numpy(), o_f[t])
+    # offload with and without the side stream
+    wo = _w("offload", batch=3, prompt_len=64 * 40 + 30, n_steps=60, kq=4, ke=6, pool_slots=14)
+    Ko, Vo, lamo, qo = NI.layer_inputs(wo)
+    ra, _, _ = H.run_offload(wo, Ko, Vo, lamo, qo, side_stream=True)
+    rb, _, _ = H.run_offload(wo, Ko, Vo, lamo, qo, side_stream=False)
+    for key in ("sel", "n_sel", "phys", "miss_list", "n_miss", "block_table", "slot_block"):
+        for t in range(wo.n_steps):
+            assert np.array_equal(ra[key][t], rb[key][t]), (key, t)
+    for t in range(wo.n_steps):
+        assert float(np.abs(ra["out"][t] - rb["out"][t]).max()) <= atol
 
 
 # ------------------------------------------------------- end-to-end decode
@@ -278,6 +359,81 @@ def test_offload_small_pool_matches_oracle(side):
             total += st["misses"]
             _pool_consistent(layer, host, b, h)
     assert total > w.batch * w.n_kv_heads * 10
+
+
+@pytest.mark.parametrize("side", [True, False])
+def test_offload_ragged_positions(side):
+    """Batch entries at their own positions (lagging the first by 0, 17, 40
+    and 63 tokens), so their windows complete blocks on different steps: each
+    completed block is pooled for its entry alone (nosa_pool_keys_entries)
+    and inserted for that entry alone (a per-entry insert_block).  Every unit
+    against the oracle at its own positions; the compressed keys and eviction
+    scores of each entry's complete blocks bit-exact, and nothing written for
+    blocks an entry has not completed."""
+    _banner(f"offload ragged positions: B=4, lags 0/17/40/63, 100 steps, pool 14, side stream={side}")
+    w = _w("offload", batch=4, prompt_len=64 * 40 + 30, n_steps=100, kq=4, ke=6, pool_slots=14)
+    K, V, lam, q = NI.layer_inputs(w)
+    offs = [0, 17, 40, 63]
+    rec, layer, host = H.run_offload(w, K, V, lam, q, side_stream=side, offsets=offs)
+    P = rec["positions"]
+    done_steps = [set(np.nonzero(P[1:, b] // 64 > P[:-1, b] // 64)[0] + 1) for b in range(w.batch)]
+    assert all(done_steps) and len(set().union(*done_steps)) == sum(map(len, done_steps))   # no two together
+    bf16 = w.dtype == "bf16"
+    kc = layer.k_comp.float().cpu().numpy()
+    es, eb = layer.e_sub.cpu().numpy(), layer.e_blk.cpu().numpy()
+    for b in range(w.batch):
+        c_end = int(P[-1, b]) // 64
+        for h in range(w.n_kv_heads):
+            st = H.check_offload_unit(w, K, V, lam, q, rec, b, h)
+            assert st["misses"] > 0
+            _pool_consistent(layer, host, b, h)
+            kbar = O.subblock_key_means(K[b, h], bf16)
+            e_sub = O.subblock_logit_means(lam[b, h])
+            assert np.array_equal(kc[b, h, : 4 * c_end], kbar[: 4 * c_end])
+            assert np.array_equal(es[b, h, : 4 * c_end], e_sub[: 4 * c_end])
+            assert np.array_equal(eb[b, h, :c_end], O.block_eviction_scores(e_sub)[:c_end])
+            assert not kc[b, h, 4 * c_end:].any() and not eb[b, h, c_end:].any()
+
+
+@pytest.mark.parametrize("reset_at", [30, 34], ids=["mid-block", "on-a-completion"])
+def test_offload_cold_restart_mid_run(reset_at):
+    """The pool tables cleared before step `reset_at` (every resident block
+    forgotten): the same sets, the same outputs within tolerance, more
+    misses, and from the restart on the misses, slots and insertions of a
+    pool that starts empty there (the oracle's)."""
+    _banner(f"offload cold restart at step {reset_at}")
+    w = _w("offload", batch=3, prompt_len=64 * 40 + 30, n_steps=60, kq=4, ke=6, pool_slots=14)
+    K, V, lam, q = NI.layer_inputs(w)
+    base, _, _ = H.run_offload(w, K, V, lam, q)
+    rec, layer, host = H.run_offload(w, K, V, lam, q, reset_at=reset_at)
+    assert (int(w.positions()[reset_at]) // 64 > int(w.positions()[reset_at - 1]) // 64) == (reset_at == 34)
+    for t in range(w.n_steps):
+        assert np.array_equal(rec["sel"][t], base["sel"][t]) and np.array_equal(rec["n_sel"][t], base["n_sel"][t])
+        assert float(np.abs(rec["out"][t] - base["out"][t]).max()) <= H.ATOL[w.dtype]
+    # every selected block misses at the restart, except a completed block inserted there
+    done = int(w.positions()[reset_at]) // 64 - 1 if reset_at == 34 else -1
+    S, N = rec["sel"][reset_at], rec["n_sel"][reset_at]
+    inserted = np.array([[done in S[b, h, : N[b, h]] for h in range(w.n_kv_heads)] for b in range(w.batch)])
+    assert np.array_equal(rec["n_miss"][reset_at], N - inserted)
+    assert sum(int(m.sum()) for m in rec["n_miss"]) > sum(int(m.sum()) for m in base["n_miss"])
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            H.check_offload_unit(w, K, V, lam, q, rec, b, h, pool_reset_at=reset_at)
+            _pool_consistent(layer, host, b, h)
+
+
+@pytest.mark.parametrize("kq,ke", [(8, 56), (32, 32), (64, 0)], ids=["kq8", "kq32", "kq64"])
+def test_offload_sweep_points(kq, ke):
+    """The kq/k sweep points of the offload workload (k = 64, 16K context,
+    pool of 80) at batch 2, every unit, 96 steps (one block completes)."""
+    _banner(f"offload sweep point kq={kq} ke={ke}: B=2, 16K context, pool 80, 96 steps")
+    w = _w("offload", batch=2, n_steps=96, kq=kq, ke=ke)
+    K, V, lam, q = NI.layer_inputs(w)
+    rec, layer, host = H.run_offload(w, K, V, lam, q)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            H.check_offload_unit(w, K, V, lam, q, rec, b, h)
+            _pool_consistent(layer, host, b, h)
 
 
 def test_offload_workload_sampled_units():

@@ -389,6 +389,37 @@ def test_pool_replay_invariants():
     assert total_misses > 0 and inserts > 0
 
 
+def test_pool_restart_mid_run():
+    """A restart at step r forgets every resident block: step r misses every
+    selected block (ascending, into the lowest slots, after the completed block
+    when one is inserted first), the selections and outputs are unchanged, the
+    steps before r are unchanged, and from r on the trace equals a pool replay
+    that starts empty at r."""
+    w = NI.scaled(NI.WORKLOADS["tiny"], prompt_len=64 * 24 + 60, n_steps=40, kq=5, ke=6, head_dim=16)
+    K, V, lam = NI.unit_kv(w, 0, 0)
+    q = NI.queries(w)[:, 0]
+    pos = w.positions()
+    P, r = 14, 7                                   # a block completes at step 4
+    a = O.decode_unit(K, V, lam, q, pos, 5, 6, bf16=False, pool_slots=P)
+    b = O.decode_unit(K, V, lam, q, pos, 5, 6, bf16=False, pool_slots=P, pool_reset_at=r)
+    assert a.sel == b.sel and all(np.array_equal(x, y) for x, y in zip(a.out, b.out))
+    assert a.misses[:r] == b.misses[:r] and a.phys[:r] == b.phys[:r]
+    assert [m for m, _ in b.misses[r]] == b.sel[r] and [s for _, s in b.misses[r]] == list(range(len(b.sel[r])))
+    assert sum(map(len, b.misses)) > sum(map(len, a.misses))
+    pool = O.BlockPool(P)
+    for t in range(r, len(pos)):
+        c, c0 = int(pos[t]) // 64, int(pos[t - 1]) // 64
+        m, ins, ph = pool.step(t, b.sel[t], c0 if c > c0 else None)
+        assert (m, ins, ph) == (b.misses[t], b.insert_slot[t], b.phys[t])
+    # a restart on the step a block completes: the inserted block takes slot 0
+    c = pos // 64
+    r2 = int(np.nonzero(c[1:] > c[:-1])[0][0]) + 1
+    d = O.decode_unit(K, V, lam, q, pos, 5, 6, bf16=False, pool_slots=P, attend=False, pool_reset_at=r2)
+    assert d.insert_slot[r2] == 0
+    assert [s for _, s in d.misses[r2]] == list(range(1, 1 + len(d.misses[r2])))
+    assert [m for m, _ in d.misses[r2]] == [j for j in d.sel[r2] if j != c[r2] - 1]
+
+
 # ---------------------------------------------------------------- eviction head
 def test_softplus_closed_forms():
     # log 2 at 0; x + log1p(e^-x) and log1p(e^x) written out with the math module
