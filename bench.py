@@ -21,11 +21,14 @@ Infinity Cache (R = 16: 624 MB in between).  The same steps on one replica
 are reported too, labelled warm; `value` and the roofline are the cold ones.
 
 Prints ONE JSON line.  Extra objects: roofline of the dominant kernel
-(step_kernel, the one launch of a step), per-kernel times, the offload leg
-(KV in pinned host memory, HBM pool of 80 blocks per KV head, the offload
-workload, the kq/k sweep and the transfer operator's blocks-per-call sweep),
-the 28-layer stack, the prefill leg, the QKV split and the oracle's CPU
-baseline on a bounded sample.
+(step_kernel, the one launch of a step), per-kernel times, the two variant
+readings beside the path's own (fill-the-remainder selection: Jaccard, set
+sizes, re-admissions, output deltas; eviction-logit bias: output deltas) on
+layer32k and on the offload workload, the offload leg (KV in pinned host
+memory, HBM pool of 80 blocks per KV head, the offload workload, the kq/k
+sweep and the transfer operator's blocks-per-call sweep), the 28-layer
+stack, the prefill leg, the QKV split and the oracle's CPU baseline on a
+bounded sample.
 """
 from __future__ import annotations
 
@@ -250,6 +253,12 @@ def main():
     attn_ms = time_graph(g_attn)[0] / K_steps
     g_sep = capture(lambda t: step_separate(t, stream), K_steps)
     sep_ms = time_graph(g_sep)[0] / K_steps
+    # the two variant calls, same rotation
+    g_self = capture(lambda t: layers[t % n_rep].select(qd[t % n_pos], pos[t % n_pos], stream, fill=True), K_steps)
+    sel_fill_ms = time_graph(g_self)[0] / K_steps
+    g_attb = capture(lambda t: layers[t % n_rep].attend_resident_bias(qd[t % n_pos], kvs[t % n_rep], pos[t % n_pos],
+                                                                        logits, stream), K_steps)
+    attn_bias_ms = time_graph(g_attb)[0] / K_steps
     # bounded hand-off waits of the one-launch step that hit their bound in any
     # of the timed launches (each spoils that launch's outputs)
     timeouts = sum(L.step_timeouts() for L in layers)
@@ -303,10 +312,15 @@ def main():
                      "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": int(step_b)},
     }
+    result["kernels"].update({"select_fill_us": round(sel_fill_ms * 1e3, 3),
+                              "attn_bias_us": round(attn_bias_ms * 1e3, 3)})
+    t0 = time.perf_counter()
+    result["variants"] = _variants(torch, nb, layers[0], kvs[0], logits, qd, pos, range(n_pos))
+    log(f"variants layer32k ({time.perf_counter() - t0:.1f}s): {json.dumps(result['variants'])}")
     del layers, kvs
 
     if not args.no_offload:
-        result["offload"] = _offload_leg(torch, NI, R)
+        result["offload"] = _offload_leg(torch, NI, R, nb)
         torch._C._host_emptyCache()          # hand the offload leg's pinned cache back
     if not args.no_prefill:
         result["prefill"] = _prefill_leg(torch, NI, R, nb)
@@ -338,10 +352,11 @@ def _device_inputs(w, K, V, lam, q, R):
 KQ_SWEEP = (8, 16, 32, 64)        # kq at k = kq + ke = 64: kq/k = 0.125, 0.25, 0.5, 1.0
 
 
-def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos):
+def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos, fill=False):
     """One offload decode run from a cold pool; per-step events, no host sync
-    inside the loop.  Returns step and fetch times (ms), misses, set sizes and
-    selections per step."""
+    inside the loop (fill: the selection under the other reading of Eq. 7).
+    Returns step and fetch times (ms), misses, set sizes and selections per
+    step."""
     positions = w.positions()
     layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, kq, ke,
                           pool_slots=w.pool_slots)
@@ -359,7 +374,7 @@ def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos):
             layer.pool_window(windows[c_prev], logits, c_prev, main)
             ins_blk = torch.full((w.batch,), c_prev, dtype=torch.int32, device="cuda")
             ins_src = windows[c_prev]
-        layer.select(qd[t], pos[t], main)
+        layer.select(qd[t], pos[t], main, fill=fill)
         # pool update, then the gather on the side stream while the attention
         # over the blocks already resident runs (the runner's offload step)
         f0.record(main)
@@ -383,7 +398,7 @@ def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos):
     return step_ms, fetch_ms, misses, nsel, sels
 
 
-def _offload_leg(torch, NI, R):
+def _offload_leg(torch, NI, R, nb):
     """The offload workload: KV in pinned host memory, HBM pool of 80 blocks
     per KV head, kq = 16 + ke = 48; then the kq/k sweep at k = 64 on the same
     inputs (each point from a cold pool)."""
@@ -422,6 +437,17 @@ def _offload_leg(torch, NI, R):
             "fetch_share_of_step": round(float(fetch_ms[warm].sum() / step_ms[warm].sum()), 4),
         }
 
+    # the GPU's mapping of the pinned cache touched once before anything is timed
+    L = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke,
+                      pool_slots=w.pool_slots)
+    t0 = time.perf_counter()
+    warm_rates = _warm_host_mapping(torch, nb, L, host, w.n_blocks)
+    sweep = _transfer_sweep(torch, nb, L, host, blocks[0])
+    log(f"host cache warm-up passes (GB/s): {', '.join(f'{r:.1f}' for r in warm_rates)}")
+    log(f"transfer sweep ({time.perf_counter() - t0:.1f}s, memcpy {link_ref:.1f} GB/s): " +
+        ", ".join(f"{n}: {g:.1f}" for n, _, g in sweep))
+    del L
+
     points = []
     for kq in KQ_SWEEP:
         ke = 64 - kq
@@ -434,6 +460,23 @@ def _offload_leg(torch, NI, R):
            "steps": w.n_steps, "graph": False, "memcpy_h2d_gbps": round(link_ref, 2)}
     out.update(main_pt)
     out["kq_sweep"] = [{k: v for k, v in p.items() if k not in ("ms_per_step_p10_p90",)} for p in points]
+    out["host_warmup_pass_gbps"] = [round(r, 2) for r in warm_rates]
+    out["transfer_sweep"] = {
+        "call": "nosa_gather_blocks alone, n blocks of 32 KiB per call spread over the 128 units, each block "
+                "read once per call size; median of 20 calls",
+        "points": [{"blocks": n, "us": round(us, 2), "gbps": round(g, 2), "frac_of_memcpy": round(g / link_ref, 4)}
+                   for n, us, g in sweep]}
+    # the other reading of Eq. 7 through the same offload step, and both variants step by step
+    fp = summary(w.kq, w.ke, *_offload_run(torch, R, w, w.kq, w.ke, kv_dev, host, windows, logits, qd, pos,
+                                           fill=True))
+    L = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
+    L.pool_blocks(kv_dev, logits, 0, blocks[-1])
+    var = _variants(torch, nb, L, kv_dev, logits, qd, pos, range(w.n_steps))
+    var["fill_offload"] = {k: fp[k] for k in ("ms_per_step", "misses_per_unit_step", "miss_fraction",
+                                              "locality_gamma", "host_link_gbps")}
+    out["variants"] = var
+    log(f"variants offload: {json.dumps(var)}")
+    del L
     del windows, kv_dev
     return out
 
@@ -467,6 +510,167 @@ def _locality(sels, nsels, blocks):
             b = set(prev[idx][: int(nsels[t - 1][idx])].tolist()) | {blocks[t - 1]}
             vals.append(len(a & b) / n)
     return float(np.mean(vals)) if vals else float("nan")
+
+
+def _readmissions(parts):
+    """Blocks that come back into a unit's query-agnostic part after having
+    left it, summed over the steps; `parts` is that part's block set per step.
+    The eviction rule (a block pushed out of that part never returns) makes
+    this 0 under the path's reading of Eq. 7."""
+    dropped, count = set(), 0
+    for t, cur in enumerate(parts):
+        count += len(cur & dropped)
+        if t:
+            dropped |= parts[t - 1] - cur
+        dropped -= cur
+    return count
+
+
+def _variants(torch, nb, L, kv, logits, qd, pos, steps):
+    """The two alternative readings beside the path's own, step by step on one
+    layer whose compressed keys cover every candidate of the given steps
+    (nothing timed here):
+
+      * Eq. 7 as "fill the remainder from the candidates left"
+        (nosa_select_blocks_fill) against the union Gamma_q | Gamma_e: Jaccard
+        of the two sets, their sizes, the re-admissions of each reading's
+        query-agnostic part (Gamma_e for the union, S \\ Gamma_q for the fill;
+        Gamma_q and Gamma_e come from the same selection kernel run with one
+        budget at 0), and the attention output over the fill set against the
+        one over the union set;
+      * ED-DMA's logits as an attention bias (nosa_sparse_decode_attn_bias)
+        against the plain attention, both over the union set.
+
+    Output deltas are max |delta| and ||delta||_2 / ||out||_2 per step."""
+    kq, ke = L.kq, L.ke
+    z = dict(device="cuda")
+
+    def one_budget(a, b):
+        ws = torch.zeros(max(nb.workspace_size(L.dims, nb.OP_SELECT, 1, a, b), 1), dtype=torch.uint8, **z)
+        s = torch.full((L.B, L.Hkv, max(a + b, 1)), -1, dtype=torch.int32, **z)
+        n = torch.zeros((L.B, L.Hkv), dtype=torch.int32, **z)
+        return lambda t: (nb.select_blocks(L.dims, qd[t], 1, pos[t], L.k_comp, L.e_blk, a, b, s, n, ws), s, n)
+
+    sel_q, sel_e = one_budget(kq, 0), one_budget(0, ke)
+
+    def sets(s, n):
+        s, n = s.cpu().numpy(), n.cpu().numpy()
+        return {u: set(s[u][: n[u]].tolist()) for u in np.ndindex(n.shape)}
+
+    def delta(a, b):
+        d = (a - b).abs()
+        return float(d.max()), float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b).clamp_min(1e-30))
+
+    jac, n_u, n_f, bias_d, fill_d, broken = [], [], [], [], [], 0
+    part_u, part_f = {}, {}
+    for t in steps:
+        L.select(qd[t], pos[t])
+        S_u = sets(L.sel, L.n_sel)
+        L.attend_resident(qd[t], kv, pos[t])
+        out_u = L.out.float().clone()
+        L.attend_resident_bias(qd[t], kv, pos[t], logits)
+        bias_d.append(delta(L.out.float(), out_u))
+        L.select(qd[t], pos[t], fill=True)
+        S_f = sets(L.sel, L.n_sel)
+        L.attend_resident(qd[t], kv, pos[t])
+        fill_d.append(delta(L.out.float(), out_u))
+        G_q = sets(*sel_q(t)[1:])
+        G_e = sets(*sel_e(t)[1:])
+        for u in S_u:
+            if S_u[u] != G_q[u] | G_e[u]:
+                broken += 1
+            jac.append(len(S_u[u] & S_f[u]) / max(len(S_u[u] | S_f[u]), 1))
+            n_u.append(len(S_u[u]))
+            n_f.append(len(S_f[u]))
+            part_u.setdefault(u, []).append(G_e[u])
+            part_f.setdefault(u, []).append(S_f[u] - G_q[u])
+    torch.cuda.synchronize()
+    if broken:
+        raise RuntimeError(f"{broken} union sets differ from Gamma_q | Gamma_e of the one-budget selections")
+    units = len(part_u)
+    re_u = sum(_readmissions(p) for p in part_u.values())
+    re_f = sum(_readmissions(p) for p in part_f.values())
+    bd, fd = np.array(bias_d), np.array(fill_d)
+    return {
+        "steps": len(steps), "units": units,
+        "fill_vs_union": {
+            "jaccard_mean": round(float(np.mean(jac)), 4), "jaccard_min": round(float(np.min(jac)), 4),
+            "set_size_union_mean": round(float(np.mean(n_u)), 3), "set_size_fill_mean": round(float(np.mean(n_f)), 3),
+            "readmissions_union": int(re_u), "readmissions_fill": int(re_f),
+            "readmissions_fill_per_unit_step": round(re_f / (units * len(steps)), 4),
+            "output_max_abs_delta": round(float(fd[:, 0].max()), 5),
+            "output_rel_l2_delta_mean": round(float(fd[:, 1].mean()), 5)},
+        "bias_vs_plain": {
+            "output_max_abs_delta": round(float(bd[:, 0].max()), 5),
+            "output_rel_l2_delta_mean": round(float(bd[:, 1].mean()), 5)},
+    }
+
+
+def _transfer_sweep(torch, nb, L, host, n_blocks, reps=20):
+    """The gather alone (nosa_gather_blocks) at 1 ... 1024 blocks per call:
+    per call, `n` misses spread over the units (unit u takes n // units, plus
+    one if u < n % units), each from a block no earlier call of the same size
+    read, into pool slots 0, 1, ...  Median over `reps` calls (events around
+    each).  Returns [(n, us, GB/s)]."""
+    units = L.B * L.Hkv
+    k1 = L.k + 1
+    blk_bytes = L.blk_elems * host.element_size()
+    ml = torch.full((units, k1, 2), -1, dtype=torch.int32)
+    out = []
+    for n in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
+        per = np.array([n // units + (u < n % units) for u in range(units)], np.int32)
+        assert per.max() <= L.k and per.max() <= L.pool_slots
+        calls = []
+        for r in range(reps + 2):                 # two untimed calls first
+            m = ml.clone()
+            for u in np.nonzero(per)[0]:
+                e = np.arange(per[u])
+                m[u, e, 0] = torch.from_numpy(((r * per[u] + e) % n_blocks).astype(np.int32))
+                m[u, e, 1] = torch.from_numpy(e.astype(np.int32))
+            calls.append(m.cuda())
+        n_miss = torch.from_numpy(per).cuda()
+        times = []
+        for r, m in enumerate(calls):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            nb.gather_blocks(L.dims, host, L.pool, L.pool_slots, L.k, None, m, n_miss)
+            b.record()
+            b.synchronize()
+            if r >= 2:
+                times.append(a.elapsed_time(b))
+        us = float(np.median(times)) * 1e3
+        out.append((n, us, n * blk_bytes / (us * 1e-6) / 1e9))
+    return out
+
+
+def _warm_host_mapping(torch, nb, L, host, n_blocks, max_passes=8):
+    """Untimed-in-the-results gathers of every block of the host cache (64
+    blocks of each unit per call), pass after pass until two passes in a row
+    agree within 5%: the first GPU reads of a pinned page run at about half
+    the link rate, which would otherwise show up in whichever cold step
+    comes first.  Returns each pass's GB/s."""
+    units = L.B * L.Hkv
+    k = min(L.k, L.pool_slots)
+    calls = []
+    for b0 in range(0, n_blocks, k):
+        n = min(k, n_blocks - b0)
+        m = torch.full((units, L.k + 1, 2), -1, dtype=torch.int32)
+        m[:, :n, 0] = torch.arange(b0, b0 + n, dtype=torch.int32)
+        m[:, :n, 1] = torch.arange(n, dtype=torch.int32)
+        calls.append((m.cuda(), torch.full((units,), n, dtype=torch.int32, device="cuda")))
+    nbytes = units * n_blocks * L.blk_elems * host.element_size()
+    rates = []
+    for _ in range(max_passes):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for m, n_miss in calls:
+            nb.gather_blocks(L.dims, host, L.pool, L.pool_slots, L.k, None, m, n_miss)
+        b.record()
+        b.synchronize()
+        rates.append(nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+        if len(rates) >= 2 and abs(rates[-1] - rates[-2]) <= 0.05 * rates[-1]:
+            break
+    return rates
 
 
 def _stack_leg(torch, NI, R):

@@ -41,3 +41,23 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     assert res.returncode == 2
     line = json.loads(res.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "single GPU" in line["error"]
+
+
+def test_readmissions_match_oracle_definition():
+    """The re-admission count bench.py reports from GPU selections agrees with
+    the oracle's on random part sequences, and on the oracle's fill trace of a
+    small decode run, where it is known to be positive."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        steps = int(rng.integers(1, 9))
+        parts = [sorted(rng.choice(12, size=int(rng.integers(0, 6)), replace=False).tolist()) for _ in range(steps)]
+        assert bench._readmissions([set(p) for p in parts]) == O.readmissions(parts)
+    E = np.float32([10, 9, 8, 7])
+    picks = [0, 3, 0]          # the query-aware pick per step, kq = 1, ke = 2
+    parts = []
+    for p in picks:
+        s_q = np.full(4, -1.0, np.float32)
+        s_q[p] = 1.0
+        g_q, g_f, _ = O.select_blocks_fill(s_q, E, 4, 1, 2)
+        parts.append(g_f)
+    assert O.readmissions(parts) == bench._readmissions([set(p) for p in parts]) == 1
