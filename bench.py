@@ -352,11 +352,12 @@ def _device_inputs(w, K, V, lam, q, R):
 KQ_SWEEP = (8, 16, 32, 64)        # kq at k = kq + ke = 64: kq/k = 0.125, 0.25, 0.5, 1.0
 
 
-def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos, fill=False):
+def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos, fill=False, fused_fetch=False):
     """One offload decode run from a cold pool; per-step events, no host sync
-    inside the loop (fill: the selection under the other reading of Eq. 7).
-    Returns step and fetch times (ms), misses, set sizes and selections per
-    step."""
+    inside the loop (fill: the selection under the other reading of Eq. 7;
+    fused_fetch: the gather folded into the attention, one stream).  Returns
+    step and gather times (ms; with fused_fetch, the attention's, which holds
+    the gather), misses, set sizes and selections per step."""
     positions = w.positions()
     layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, kq, ke,
                           pool_slots=w.pool_slots)
@@ -374,17 +375,26 @@ def _offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos, fi
             layer.pool_window(windows[c_prev], logits, c_prev, main)
             ins_blk = torch.full((w.batch,), c_prev, dtype=torch.int32, device="cuda")
             ins_src = windows[c_prev]
-        layer.select(qd[t], pos[t], main, fill=fill)
-        # pool update, then the gather on the side stream while the attention
-        # over the blocks already resident runs (the runner's offload step)
-        f0.record(main)
-        layer.update_pool(t, ins_blk, main)
-        side.wait_stream(main)
-        layer.gather(host, ins_src, side)
-        f1.record(side)
-        layer.attend_pool_part(qd[t], windows[c], pos[t], 0, main)
-        main.wait_stream(side)
-        layer.attend_pool_part(qd[t], windows[c], pos[t], 1, main)
+        # selection and pool update (one launch; two for the fill variant),
+        # then the gather on the side stream while the attention over the
+        # blocks already resident runs (the runner's offload step)
+        if fill:
+            layer.select(qd[t], pos[t], main, fill=True)
+            layer.update_pool(t, ins_blk, main)
+        else:
+            layer.select_update(qd[t], pos[t], t, ins_blk, main)
+        if fused_fetch:
+            f0.record(main)
+            layer.attend_fetch(qd[t], host, windows[c], pos[t], ins_src, main)
+            f1.record(main)
+        else:
+            side.wait_stream(main)
+            f0.record(side)
+            layer.gather(host, ins_src, side)
+            f1.record(side)
+            layer.attend_pool_part(qd[t], windows[c], pos[t], 0, main)
+            main.wait_stream(side)
+            layer.attend_pool_part(qd[t], windows[c], pos[t], 1, main)
         e1.record(main)
         ev.append((e0, e1, f0, f1))
         rec.append((layer.n_miss.clone(), layer.n_sel.clone(), layer.sel.clone()))
@@ -434,7 +444,7 @@ def _offload_leg(torch, NI, R, nb):
             "locality_gamma": round(_locality(sels, nsel, blocks), 4),
             "host_link_gbps": round(link, 2), "host_link_frac_of_memcpy": round(link / link_ref, 4),
             "cold_step_host_link_gbps": round(float(miss_bytes[0] / (fetch_ms[0] * 1e-3) / 1e9), 2),
-            "fetch_share_of_step": round(float(fetch_ms[warm].sum() / step_ms[warm].sum()), 4),
+            "gather_share_of_step": round(float(fetch_ms[warm].sum() / step_ms[warm].sum()), 4),
         }
 
     # the GPU's mapping of the pinned cache touched once before anything is timed
@@ -451,13 +461,16 @@ def _offload_leg(torch, NI, R, nb):
     points = []
     for kq in KQ_SWEEP:
         ke = 64 - kq
-        pt = summary(kq, ke, *_offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos))
+        pt = summary(kq, ke, *_offload_run(torch, R, w, kq, ke, kv_dev, host, windows, logits, qd, pos,
+                                           fused_fetch=True))
         log(f"offload kq={kq:2d} ke={ke:2d}: step {pt['ms_per_step']:.3f} ms, misses/unit/step "
             f"{pt['misses_per_unit_step']:.2f}, gamma {pt['locality_gamma']:.3f}, link {pt['host_link_gbps']:.1f} GB/s")
         points.append(pt)
     main_pt = next(p for p in points if p["kq"] == w.kq and p["ke"] == w.ke)
     out = {"workload": "offload", "batch": w.batch, "context": w.prompt_len, "pool_slots": w.pool_slots,
-           "steps": w.n_steps, "graph": False, "memcpy_h2d_gbps": round(link_ref, 2)}
+           "steps": w.n_steps, "graph": False, "memcpy_h2d_gbps": round(link_ref, 2),
+           "step": "selection + pool update (one launch), then the attention with the gather folded in; "
+                   "host_link_gbps: miss bytes / that attention's time"}
     out.update(main_pt)
     out["kq_sweep"] = [{k: v for k, v in p.items() if k not in ("ms_per_step_p10_p90",)} for p in points]
     out["host_warmup_pass_gbps"] = [round(r, 2) for r in warm_rates]
@@ -466,9 +479,17 @@ def _offload_leg(torch, NI, R, nb):
                 "read once per call size; median of 20 calls",
         "points": [{"blocks": n, "us": round(us, 2), "gbps": round(g, 2), "frac_of_memcpy": round(g / link_ref, 4)}
                    for n, us, g in sweep]}
+    # the same step with the gather on a side stream beside the attention over
+    # the resident blocks, then the attention over the fetched ones
+    ss = summary(w.kq, w.ke, *_offload_run(torch, R, w, w.kq, w.ke, kv_dev, host, windows, logits, qd, pos))
+    out["gather_on_side_stream"] = {k: ss[k] for k in ("tokens_per_s", "ms_per_step", "ms_per_step_p10_p90",
+                                                       "cold_step_ms", "misses_per_unit_step", "host_link_gbps",
+                                                       "gather_share_of_step")}
+    log(f"offload, gather on a side stream, kq={w.kq}: step {ss['ms_per_step']:.3f} ms, "
+        f"link {ss['host_link_gbps']:.1f} GB/s")
     # the other reading of Eq. 7 through the same offload step, and both variants step by step
     fp = summary(w.kq, w.ke, *_offload_run(torch, R, w, w.kq, w.ke, kv_dev, host, windows, logits, qd, pos,
-                                           fill=True))
+                                           fill=True, fused_fetch=True))
     L = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
     L.pool_blocks(kv_dev, logits, 0, blocks[-1])
     var = _variants(torch, nb, L, kv_dev, logits, qd, pos, range(w.n_steps))
@@ -701,22 +722,41 @@ def _stack_leg(torch, NI, R):
 
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
-    fetch_ev = [[] for _ in range(w.n_layers)]
-    step_ev = []
-    rec_sel, rec_n, rec_miss = [], [], []
 
-    def on_layer(l, L):
-        rec_sel.append(L.sel.clone())
-        rec_n.append(L.n_sel.clone())
-        rec_miss.append(L.n_miss.clone())
+    def run(fused_update, fused_fetch=False):
+        """The decode steps from empty pools (tables cleared, window back at
+        the prompt's end; the compressed keys of blocks completed on the way
+        are pooled again, to the same values)."""
+        for L in stack.layers:
+            for k in ("block_table", "slot_block", "slot_last_use"):
+                getattr(L, k).fill_(-1)
+        stack.block = blocks[0]
+        torch.cuda.synchronize()
+        fetch_ev = [[] for _ in range(w.n_layers)]
+        step_ev = []
+        rec = ([], [], [])
 
-    for t in range(w.n_steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(main)
-        stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer, fetch_ev)
-        e1.record(main)
-        step_ev.append((e0, e1))
-    torch.cuda.synchronize()
+        def on_layer(l, L):
+            rec[0].append(L.sel.clone())
+            rec[1].append(L.n_sel.clone())
+            rec[2].append(L.n_miss.clone())
+
+        for t in range(w.n_steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main)
+            stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer, fetch_ev, fused_update,
+                       fused_fetch)
+            e1.record(main)
+            step_ev.append((e0, e1))
+        torch.cuda.synchronize()
+        return fetch_ev, step_ev, rec
+
+    # the selection and the pool update as two launches, then as one; then
+    # also the gather folded into the attention (reported)
+    med = lambda ev: float(np.median(np.array([a.elapsed_time(b) for a, b in ev])[1:]))
+    ms_two = med(run(False)[1])
+    ms_side = med(run(True)[1])
+    fetch_ev, step_ev, (rec_sel, rec_n, rec_miss) = run(True, True)
     nL = w.n_layers
     step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
     fetch_ms = np.array([[a.elapsed_time(b) for a, b in fetch_ev[l]] for l in range(nL)]).T   # [t, l]
@@ -738,7 +778,8 @@ def _stack_leg(torch, NI, R):
     link = float(miss_bytes[warm].sum() / (fetch_ms[warm].sum() * 1e-3) / 1e9)
     cold_link = float(miss_bytes[0].sum() / (fetch_ms[0].sum() * 1e-3) / 1e9)
     fetch_share = float(fetch_ms[warm].sum() / step_ms[warm].sum())
-    log(f"stack: step {ms:.3f} ms ({ms / nL * 1e3:.1f} us per layer), cold step {step_ms[0]:.2f} ms, "
+    log(f"stack: step {ms:.3f} ms ({ms / nL * 1e3:.1f} us per layer; gather on a side stream: {ms_side:.3f} ms, "
+        f"and with the selection and the pool update as two launches {ms_two:.3f} ms), cold step {step_ms[0]:.2f} ms, "
         f"misses/unit/layer-step {n_miss[warm].mean():.2f}, gamma {gamma:.3f}, link {link:.1f} GB/s "
         f"(cold {cold_link:.1f}; memcpy {link_ref:.1f}), HBM {hbm_gbps:.0f} GB/s")
     return {
@@ -750,6 +791,9 @@ def _stack_leg(torch, NI, R):
         "ms_per_step_p10_p90": [round(float(np.percentile(step_ms[warm], 10)), 4),
                                 round(float(np.percentile(step_ms[warm], 90)), 4)],
         "us_per_layer_step": round(ms / nL * 1e3, 2),
+        "step": "per layer: selection + pool update (one launch), then the attention with the gather folded in",
+        "ms_per_step_gather_on_side_stream": round(ms_side, 4),
+        "ms_per_step_gather_on_side_stream_select_and_update_as_two_launches": round(ms_two, 4),
         "cold_step_ms": round(float(step_ms[0]), 3),
         "hbm_gbps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "misses_per_unit_layer_step": round(float(n_miss[warm].mean()), 3),
@@ -758,7 +802,7 @@ def _stack_leg(torch, NI, R):
         "host_link_gbps": round(link, 2), "cold_step_host_link_gbps": round(cold_link, 2),
         "memcpy_h2d_gbps": round(link_ref, 2), "host_link_frac_of_memcpy": round(link / link_ref, 4),
         "cold_frac_of_memcpy": round(cold_link / link_ref, 4),
-        "fetch_share_of_step": round(fetch_share, 4),
+        "gather_share_of_step": round(fetch_share, 4),
         "setup_seconds": round(setup_s, 1),
     }
 

@@ -320,6 +320,31 @@ int nosa_gather_blocks(const nosa_dims* dims, const void* host_kv, void* pool, i
                        const int32_t* n_miss, void* stream);
 
 /*
+ * nosa_select_update_pool -- nosa_select_blocks (one query row per batch
+ * entry) and nosa_update_pool in one launch.
+ *
+ * The selection (montaan summary, "Key Design Components" item 4, Eq. 7) and
+ * the set difference against the pool (montaan, "System Optimization (NOSI)"
+ * item 2; gist.science, "2. Système : NOSI") run back to back on the critical
+ * path of an offloaded step: the workgroup that completes a (b, h)
+ * selection updates that unit's pool from the set it has just written, so
+ * the gather (nosa_gather_blocks, normally on a side stream) can follow
+ * directly.  The effect is exactly that of
+ *   nosa_select_blocks(dims, q, 1, pos, k_comp, e_blk, kq, ke, sel, n_sel, ws, ws_bytes, stream);
+ *   nosa_update_pool(dims, pool_slots, block_table, slot_block, slot_last_use, step,
+ *                    sel, n_sel, kq + ke, insert_block, phys, miss_list, n_miss, stream);
+ * with every argument as documented there (sel and n_sel written, then
+ * read).  kq + ke <= 64 (the pool's limit).  Errors: those of both calls,
+ * checked before anything is launched.
+ */
+int nosa_select_update_pool(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
+                            const float* e_blk, int32_t kq, int32_t ke, int32_t* sel, int32_t* n_sel,
+                            void* ws, size_t ws_bytes, int32_t pool_slots, int32_t* block_table,
+                            int32_t* slot_block, int32_t* slot_last_use, int32_t step,
+                            const int32_t* insert_block, int32_t* phys, int32_t* miss_list,
+                            int32_t* n_miss, void* stream);
+
+/*
  * nosa_sparse_decode_attn -- exact attention over the selected blocks.
  *
  * Defined by the wmrh.cn NOSA-1B post ("工程实现亮点": two-stage attention,
@@ -410,6 +435,33 @@ int nosa_sparse_decode_attn_pool(const nosa_dims* dims, const void* q, const voi
                                  const void* window_kv, int64_t window_head_stride,
                                  int64_t window_block_stride, const int32_t* pos, float scale,
                                  int32_t part, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nosa_sparse_decode_attn_fetch -- the gather and the attention of an
+ * offload step in one launch.
+ *
+ * NOSI moves the missing blocks with a zero-copy read of host memory
+ * through unified virtual addressing (montaan summary, "System Optimization
+ * (NOSI)" item 3).  Here the read feeds the attention directly: a fetched
+ * block comes from the host cache into the registers of the wavefront that
+ * attends it, which also writes it to its pool slot, while the other
+ * wavefronts attend the blocks already resident.  The effect is exactly
+ * that of
+ *   nosa_gather_blocks(dims, host_kv, pool, pool_slots, k_cap, insert_src, miss_list, n_miss, stream);
+ *   nosa_sparse_decode_attn(dims, q, pool, pool_slots, phys, n_sel, k_cap, window_kv,
+ *                           window_head_stride, window_block_stride, pos, scale, out, ws, ws_bytes, stream);
+ * on one stream, after nosa_update_pool (or nosa_select_update_pool) of the
+ * step, with every argument as documented there; k_cap <= 64.  The pool
+ * slots this step fills are written, the others only read.
+ * Errors as those two calls (host_kv must not be NULL).
+ */
+int nosa_sparse_decode_attn_fetch(const nosa_dims* dims, const void* q, const void* host_kv, void* pool,
+                                  int32_t pool_slots, const int32_t* phys, const int32_t* n_sel,
+                                  int32_t k_cap, const int32_t* miss_list, const int32_t* n_miss,
+                                  const void* insert_src, const void* window_kv,
+                                  int64_t window_head_stride, int64_t window_block_stride,
+                                  const int32_t* pos, float scale, void* out, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /*
  * nosa_sparse_chunk_attn -- exact attention for n_query rows of one batch

@@ -83,11 +83,29 @@ __device__ __forceinline__ bool slot_fetched(int slot, const int32_t* ml, int n_
   return false;
 }
 
+// Where the block in a pool slot being filled this step comes from: the host
+// cache block of its miss (>= 0), the block the window just completed (-2),
+// or nowhere: the slot is resident (-1).
+__device__ __forceinline__ int fetch_source(int slot, const int32_t* ml, int n_miss, int k_cap, int nb) {
+  if (slot == ml[2 * k_cap + 1] && ml[2 * k_cap] >= 0) return -2;
+  for (int i = 0; i < n_miss; ++i)
+    if (ml[2 * i + 1] == slot) {
+      const int blk = ml[2 * i];
+      return (blk >= 0 && blk < nb) ? blk : -1;
+    }
+  return -1;
+}
+
 // PART -1: the whole attention (splits merged by the last workgroup).
 // PART 0: a pool step's entries already resident plus the window, while the
 //         fetch's gather runs; partials only (slots 0 .. S-1).
 // PART 1: the same split of the entries, the fetched ones only (slots S ..
 //         2S-1); the last workgroup of the unit merges all 2S partials.
+// PART 2: a pool step with the gather folded in: a fetched entry's block is
+//         read from the host cache (or the completed window block), written
+//         to its pool slot from the registers and attended; entry n_sel + 1
+//         copies the completed block when the set does not hold it.  Splits
+//         merged by the last workgroup, as in PART -1.
 template <class T, int D, int WAVES, int GMAX, int PART>
 __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ blocks,
@@ -96,13 +114,15 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     int64_t win_block_stride, const int32_t* __restrict__ pos, float scale_log2, int n_q_heads,
     int n_kv_heads, int nb, typename T::storage* __restrict__ out, int32_t* __restrict__ ticket,
     float* __restrict__ part_ml, float* __restrict__ part_o, const int32_t* __restrict__ miss_list,
-    const int32_t* __restrict__ n_miss_p, int n_split_main, int n_query, const float* __restrict__ bias) {
+    const int32_t* __restrict__ n_miss_p, int n_split_main, int n_query, const float* __restrict__ bias,
+    const typename T::storage* __restrict__ host_kv, const typename T::storage* __restrict__ insert_src,
+    typename T::storage* __restrict__ pool_w) {
   constexpr int ND = D / 16;
   const int G = n_q_heads / n_kv_heads;
   // grid (units, splits): workgroups are dispatched x-fastest, so every
   // unit's first split starts before any unit's second and the light last
   // splits (often just the window) go last
-  const int n_split = PART < 0 ? (int)gridDim.y : 2 * n_split_main;   // partial slots per unit
+  const int n_split = (PART < 0 || PART == 2) ? (int)gridDim.y : 2 * n_split_main;   // partial slots per unit
   const int split = PART == 1 ? n_split_main + (int)blockIdx.y : (int)blockIdx.y;
   // a unit is one query row of one KV head: unit = (b * n_query + r) * Hkv + h
   // (q, pos, phys / n_sel, out, the ticket and the partials are per unit);
@@ -139,25 +159,53 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
     // only those (and no window)
     const int e = (int)blockIdx.y * WAVES + wave;
     const typename T::storage* blk = nullptr;
+    [[maybe_unused]] typename T::storage* copy_to = nullptr;   // PART 2: the slot a fetched block fills
     int len = 0, lblk = -1;      // lblk: the block's logical id (its position / 64)
     if (e < ns) {
       const int pb = phys[(size_t)unit * k_cap + e];
       bool take = pb >= 0 && pb < blocks_per_head;
-      if (PART >= 0 && take) take = slot_fetched(pb, ml, nm, k_cap) == (PART == 1);
+      if ((PART == 0 || PART == 1) && take) take = slot_fetched(pb, ml, nm, k_cap) == (PART == 1);
       if (take) {
         blk = blocks + ((size_t)cunit * blocks_per_head + pb) * blk_elems;
         len = kBlock;
         lblk = pb;
+        if constexpr (PART == 2) {
+          int src = fetch_source(pb, ml, nm, k_cap, nb);
+          if (src == -2 && insert_src == nullptr) src = -1;   // nothing to copy from: the slot as it is
+          if (src != -1) {
+            copy_to = pool_w + ((size_t)cunit * blocks_per_head + pb) * blk_elems;
+            blk = src == -2 ? insert_src + (size_t)cunit * blk_elems : host_kv + ((size_t)cunit * nb + src) * blk_elems;
+          }
+        }
       }
     } else if (e < n_ent && PART != 1) {
       blk = window_kv + (int64_t)cunit * win_head_stride + (int64_t)c * win_block_stride;
       len = p - c * kBlock + 1;
       lblk = c;
+    } else if (PART == 2 && e == n_ent) {
+      // the completed block enters its slot whether or not the set holds it
+      // (when it does, that entry writes the same bytes too)
+      const int ib = ml[2 * k_cap], is = ml[2 * k_cap + 1];
+      if (ib >= 0 && is >= 0 && is < blocks_per_head && insert_src != nullptr) {
+        blk = insert_src + (size_t)cunit * blk_elems;
+        copy_to = pool_w + ((size_t)cunit * blocks_per_head + is) * blk_elems;
+        len = 0;       // copied, not attended
+      }
     }
-    // the eviction-bias variant (resident cache: phys are block ids < nb)
-    const float* bias_blk = (bias != nullptr && blk != nullptr && lblk < nb)
-                                ? bias + ((size_t)cunit * nb + lblk) * kBlock : nullptr;
-    if (blk != nullptr) attend_block<T, D>(q_group, G, blk, len, scale_log2, lane, m_run, l_run, o, bias_blk);
+    if constexpr (PART == 2) {
+      if (blk != nullptr) {
+        Frags<T, D> f;
+        load_tiles<T, D, 4>(f, blk, 0, lane);
+        load_q<T, D>(f, q_group, G, lane);
+        if (copy_to != nullptr) store_tiles<T, D, 4>(f, copy_to, 0, lane);
+        if (len > 0) attend_frags<T, D, 4>(f, 0, len, scale_log2, lane, m_run, l_run, o);
+      }
+    } else {
+      // the eviction-bias variant (resident cache: phys are block ids < nb)
+      const float* bias_blk = (bias != nullptr && blk != nullptr && lblk < nb)
+                                  ? bias + ((size_t)cunit * nb + lblk) * kBlock : nullptr;
+      if (blk != nullptr) attend_block<T, D>(q_group, G, blk, len, scale_log2, lane, m_run, l_run, o, bias_blk);
+    }
   }
 
   __shared__ AttnLds<D, WAVES, GMAX> L;
@@ -390,6 +438,9 @@ static void launch_w(const LaunchAttn& a) {
   const int units = a.batch * a.n_query * a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int splits = attn_splits(a.k_cap, G);
+  // PART 2 has one more entry per unit (the completed block's copy); the
+  // partials' layout (2 * splits per unit) has room for it
+  const int splits_fetch = (a.k_cap + 2 + WAVES - 1) / WAVES;
   char* ws = (char*)a.ws;
   int32_t* ticket = (int32_t*)ws;
   float* part_ml = (float*)(ws + align256((size_t)units * sizeof(int32_t)));
@@ -400,9 +451,13 @@ static void launch_w(const LaunchAttn& a) {
   a.stream, (const typename T::storage*)a.q, (const typename T::storage*)a.blocks, a.blocks_per_head, a.phys, \
       a.n_sel, a.k_cap, (const typename T::storage*)a.window_kv, a.window_head_stride, a.window_block_stride,  \
       a.pos, scale_log2, a.n_q_heads, a.n_kv_heads, a.nb, (typename T::storage*)a.out, ticket, part_ml,        \
-      part_o, a.miss_list, a.n_miss, splits, a.n_query, a.bias
+      part_o, a.miss_list, a.n_miss, splits, a.n_query, a.bias, (const typename T::storage*)a.host_kv,   \
+      (const typename T::storage*)a.insert_src, (typename T::storage*)const_cast<void*>(a.blocks)
   if (a.part < 0)
     hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, -1>), dim3(units, splits), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
+  else if (a.part == 2)
+    hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, 2>), dim3(units, splits_fetch), dim3(64 * WAVES), 0,
+                       NOSA_ATTN_ARGS);
   else if (a.part == 0)
     hipLaunchKernelGGL((attn_kernel<T, D, WAVES, GMAX, 0>), dim3(units, splits), dim3(64 * WAVES), 0, NOSA_ATTN_ARGS);
   else

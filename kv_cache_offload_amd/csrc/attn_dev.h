@@ -91,6 +91,31 @@ __device__ __forceinline__ void load_tiles(Frags<T, D>& f, const typename T::sto
   }
 }
 
+// The operands load_tiles loaded, stored back in the same format to another
+// block (a copy of those tiles made on the way through the registers).
+template <class T, int D, int NTL>
+__device__ __forceinline__ void store_tiles(const Frags<T, D>& f, typename T::storage* blk, int t0, int lane) {
+  constexpr int EPC = T::kPer16B;
+  constexpr int NK = Frags<T, D>::NK, ND = Frags<T, D>::ND;
+  typename T::storage* kp = blk + lane * EPC;
+  typename T::storage* vp = blk + (size_t)kBlock * D + lane * EPC;
+#pragma unroll
+  for (int t = 0; t < NTL; ++t)
+#pragma unroll
+    for (int s = 0; s < NK; ++s) st16(kp + (size_t)((t0 + t) * NK + s) * 64 * EPC, f.k[t][s]);
+  if constexpr (sizeof(typename T::storage) == 2) {
+#pragma unroll
+    for (int h = 0; h < NTL / 2; ++h)
+#pragma unroll
+      for (int u = 0; u < ND; ++u) st16(vp + (size_t)((t0 / 2 + h) * ND + u) * 64 * EPC, f.v[h][u]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+      for (int u = 0; u < ND; ++u) st16(vp + (size_t)((t0 + t) * ND + u) * 64 * EPC, f.v[t][u]);
+  }
+}
+
 // S^T tiles: acc[t][i] = q_col . K[tile_token(t0 + t, 4*grp + i)]
 template <class T, int D, int NTL>
 __device__ __forceinline__ void block_scores(const Frags<T, D>& f, f32x4 (&acc)[4]) {

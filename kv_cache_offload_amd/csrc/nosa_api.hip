@@ -112,7 +112,8 @@ int nosa_pool_keys_entries(const nosa_dims* dims, const void* kv, int64_t kv_uni
 // nosa_select_blocks and its variant nosa_select_blocks_fill
 static int select_call(const char* fn, bool fill, const nosa_dims* dims, const void* q, int32_t n_query,
                        const int32_t* pos, const void* k_comp, const float* e_blk, int32_t kq, int32_t ke,
-                       int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream,
+                       const nosa::LaunchFetch* pool = nullptr) {
   if (int rc = check_dims(dims, fn)) return rc;
   if (n_query < 1) return fail(NOSA_ERR_ARG, fn, "n_query must be >= 1");
   if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
@@ -143,6 +144,7 @@ static int select_call(const char* fn, bool fill, const nosa_dims* dims, const v
   a.sel = sel;
   a.n_sel = n_sel;
   a.ws = ws;
+  a.pool = pool;
   a.stream = (hipStream_t)stream;
   nosa::launch_select(a);
   return check_launch(fn);
@@ -204,12 +206,13 @@ int nosa_select_blocks_shared(const nosa_dims* dims, const void* q, int32_t n_qu
   return check_launch(fn);
 }
 
-// nosa_fetch_blocks and its two phases (1: tables, 2: gather)
-static int fetch_phases(const char* fn, int phases, const nosa_dims* dims, const void* host_kv, void* pool,
-                        int32_t pool_slots, int32_t* block_table, int32_t* slot_block, int32_t* slot_last_use,
-                        int32_t step, const int32_t* sel, const int32_t* n_sel, int32_t k_cap,
-                        const int32_t* insert_block, const void* insert_src, int32_t* phys, int32_t* miss_list,
-                        int32_t* n_miss, void* stream) {
+// nosa_fetch_blocks and its two phases (1: tables, 2: gather): checks the
+// arguments and fills the launch descriptor
+static int fetch_args(const char* fn, int phases, const nosa_dims* dims, const void* host_kv, void* pool,
+                      int32_t pool_slots, int32_t* block_table, int32_t* slot_block, int32_t* slot_last_use,
+                      int32_t step, const int32_t* sel, const int32_t* n_sel, int32_t k_cap,
+                      const int32_t* insert_block, const void* insert_src, int32_t* phys, int32_t* miss_list,
+                      int32_t* n_miss, void* stream, nosa::LaunchFetch& a) {
   if (int rc = check_dims(dims, fn)) return rc;
   if (k_cap < 0 || k_cap > kMaxFetchK)
     return fail(NOSA_ERR_UNSUPPORTED, fn, "k_cap must be in [0, 64]");
@@ -222,7 +225,7 @@ static int fetch_phases(const char* fn, int phases, const nosa_dims* dims, const
   if (phases == 3 && insert_block && !insert_src) return fail(NOSA_ERR_ARG, fn, "insert_block needs insert_src");
   if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
     return fail(NOSA_ERR_UNSUPPORTED, fn, "batch * n_kv_heads above 65535");
-  nosa::LaunchFetch a{};
+  a = nosa::LaunchFetch{};
   a.bf16 = dims->dtype == NOSA_BF16;
   a.head_dim = dims->head_dim;
   a.batch = dims->batch;
@@ -245,8 +248,35 @@ static int fetch_phases(const char* fn, int phases, const nosa_dims* dims, const
   a.n_miss = n_miss;
   a.phases = phases;
   a.stream = (hipStream_t)stream;
+  return NOSA_OK;
+}
+
+static int fetch_phases(const char* fn, int phases, const nosa_dims* dims, const void* host_kv, void* pool,
+                        int32_t pool_slots, int32_t* block_table, int32_t* slot_block, int32_t* slot_last_use,
+                        int32_t step, const int32_t* sel, const int32_t* n_sel, int32_t k_cap,
+                        const int32_t* insert_block, const void* insert_src, int32_t* phys, int32_t* miss_list,
+                        int32_t* n_miss, void* stream) {
+  nosa::LaunchFetch a;
+  if (int rc = fetch_args(fn, phases, dims, host_kv, pool, pool_slots, block_table, slot_block, slot_last_use, step,
+                          sel, n_sel, k_cap, insert_block, insert_src, phys, miss_list, n_miss, stream, a))
+    return rc;
   nosa::launch_fetch(a);
   return check_launch(fn);
+}
+
+int nosa_select_update_pool(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
+                            const float* e_blk, int32_t kq, int32_t ke, int32_t* sel, int32_t* n_sel, void* ws,
+                            size_t ws_bytes, int32_t pool_slots, int32_t* block_table, int32_t* slot_block,
+                            int32_t* slot_last_use, int32_t step, const int32_t* insert_block, int32_t* phys,
+                            int32_t* miss_list, int32_t* n_miss, void* stream) {
+  static const char* fn = "nosa_select_update_pool";
+  if (kq < 0 || ke < 0) return fail(NOSA_ERR_ARG, fn, "kq and ke must be >= 0");
+  if ((int64_t)kq + ke > kMaxFetchK) return fail(NOSA_ERR_UNSUPPORTED, fn, "kq + ke must be <= 64");
+  nosa::LaunchFetch f;
+  if (int rc = fetch_args(fn, 1, dims, nullptr, nullptr, pool_slots, block_table, slot_block, slot_last_use, step,
+                          sel, n_sel, kq + ke, insert_block, nullptr, phys, miss_list, n_miss, stream, f))
+    return rc;
+  return select_call(fn, false, dims, q, 1, pos, k_comp, e_blk, kq, ke, sel, n_sel, ws, ws_bytes, stream, &f);
 }
 
 int nosa_fetch_blocks(const nosa_dims* dims, const void* host_kv, void* pool, int32_t pool_slots,
@@ -279,14 +309,16 @@ static int sparse_attn(const char* fn, int part, int n_query, const nosa_dims* d
                        int32_t blocks_per_head, const int32_t* phys, const int32_t* n_sel, int32_t k_cap,
                        const int32_t* miss_list, const int32_t* n_miss, const void* window_kv,
                        int64_t window_head_stride, int64_t window_block_stride, const int32_t* pos, float scale,
-                       void* out, void* ws, size_t ws_bytes, void* stream, const float* bias = nullptr) {
+                       void* out, void* ws, size_t ws_bytes, void* stream, const float* bias = nullptr,
+                       const void* host_kv = nullptr, const void* insert_src = nullptr) {
   if (int rc = check_dims(dims, fn)) return rc;
   if (k_cap < 0 || k_cap > 512) return fail(NOSA_ERR_UNSUPPORTED, fn, "k_cap must be in [0, 512]");
   if (blocks_per_head < 1 && k_cap > 0) return fail(NOSA_ERR_ARG, fn, "blocks_per_head must be >= 1");
   if (!q || !window_kv || !pos || !out || !n_sel || !ws || (k_cap > 0 && (!blocks || !phys)))
     return fail(NOSA_ERR_ARG, fn, "NULL buffer");
   if (part >= 0 && (!miss_list || !n_miss)) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
-  if (part > 1) return fail(NOSA_ERR_ARG, fn, "part must be 0 or 1");
+  if (part > 2) return fail(NOSA_ERR_ARG, fn, "part must be 0 or 1");
+  if (part == 2 && !host_kv) return fail(NOSA_ERR_ARG, fn, "NULL buffer");
   if (window_head_stride < 0 || window_block_stride < 0)
     return fail(NOSA_ERR_ARG, fn, "window strides must be >= 0");
   if (!(scale == scale)) return fail(NOSA_ERR_ARG, fn, "scale is NaN");
@@ -320,6 +352,8 @@ static int sparse_attn(const char* fn, int part, int n_query, const nosa_dims* d
   a.miss_list = miss_list;
   a.n_miss = n_miss;
   a.bias = bias;
+  a.host_kv = host_kv;
+  a.insert_src = insert_src;
   a.stream = (hipStream_t)stream;
   nosa::launch_attn(a);
   return check_launch(fn);
@@ -352,10 +386,24 @@ int nosa_sparse_decode_attn_pool(const nosa_dims* dims, const void* q, const voi
                                  const int32_t* miss_list, const int32_t* n_miss, const void* window_kv,
                                  int64_t window_head_stride, int64_t window_block_stride, const int32_t* pos,
                                  float scale, int32_t part, void* out, void* ws, size_t ws_bytes, void* stream) {
-  if (part < 0) return fail(NOSA_ERR_ARG, "nosa_sparse_decode_attn_pool", "part must be 0 or 1");
+  if (part != 0 && part != 1) return fail(NOSA_ERR_ARG, "nosa_sparse_decode_attn_pool", "part must be 0 or 1");
   return sparse_attn("nosa_sparse_decode_attn_pool", part, 1, dims, q, pool, pool_slots, phys, n_sel, k_cap,
                      miss_list, n_miss, window_kv, window_head_stride, window_block_stride, pos, scale, out, ws,
                      ws_bytes, stream);
+}
+
+int nosa_sparse_decode_attn_fetch(const nosa_dims* dims, const void* q, const void* host_kv, void* pool,
+                                  int32_t pool_slots, const int32_t* phys, const int32_t* n_sel, int32_t k_cap,
+                                  const int32_t* miss_list, const int32_t* n_miss, const void* insert_src,
+                                  const void* window_kv, int64_t window_head_stride, int64_t window_block_stride,
+                                  const int32_t* pos, float scale, void* out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  static const char* fn = "nosa_sparse_decode_attn_fetch";
+  if (pool_slots < 1) return fail(NOSA_ERR_ARG, fn, "pool_slots must be >= 1");
+  if (k_cap > 64) return fail(NOSA_ERR_UNSUPPORTED, fn, "k_cap must be in [0, 64]");
+  return sparse_attn(fn, 2, 1, dims, q, pool, pool_slots, phys, n_sel, k_cap, miss_list, n_miss, window_kv,
+                     window_head_stride, window_block_stride, pos, scale, out, ws, ws_bytes, stream, nullptr, host_kv,
+                     insert_src);
 }
 
 int nosa_sparse_chunk_attn(const nosa_dims* dims, const void* q, int32_t n_query, const void* kv,

@@ -25,22 +25,6 @@ struct LaunchPool {
   hipStream_t stream;
 };
 
-struct LaunchSelect {
-  bool bf16;
-  int head_dim;
-  int batch, n_query, n_q_heads, n_kv_heads, nb;
-  int kq, ke;
-  bool fill;                   // Eq. 7 filled from the candidates left (a variant, off by default)
-  const void* q;
-  const int32_t* pos;
-  const void* k_comp;
-  const float* e_blk;
-  int32_t* sel;
-  int32_t* n_sel;
-  void* ws;
-  hipStream_t stream;
-};
-
 struct LaunchFetch {
   bool bf16;
   int head_dim;
@@ -61,6 +45,23 @@ struct LaunchFetch {
   hipStream_t stream;
 };
 
+struct LaunchSelect {
+  bool bf16;
+  int head_dim;
+  int batch, n_query, n_q_heads, n_kv_heads, nb;
+  int kq, ke;
+  bool fill;                   // Eq. 7 filled from the candidates left (a variant, off by default)
+  const void* q;
+  const int32_t* pos;
+  const void* k_comp;
+  const float* e_blk;
+  int32_t* sel;
+  int32_t* n_sel;
+  void* ws;
+  const LaunchFetch* pool;     // the pool update run by the selection's last workgroup, or null
+  hipStream_t stream;
+};
+
 struct LaunchAttn {
   bool bf16;
   int head_dim;
@@ -78,10 +79,13 @@ struct LaunchAttn {
   void* out;
   void* ws;
   int n_query;                 // query rows per batch entry (q, pos, phys, out per row)
-  int part;                    // -1 whole step; 0 / 1 the two parts of a pool step
-  const int32_t* miss_list;    // parts 0 and 1: the fetch's miss list and counts
+  int part;                    // -1 whole step; 0 / 1 the two parts of a pool step; 2 a pool step
+                               // with the gather folded in
+  const int32_t* miss_list;    // parts 0, 1 and 2: the fetch's miss list and counts
   const int32_t* n_miss;
   const float* bias;           // per-token eviction logits added to the attention logits, or NULL
+  const void* host_kv;         // part 2: the host cache [B][Hkv][NB][block]
+  const void* insert_src;      // part 2: the completed window blocks [B][Hkv][block], or NULL
   hipStream_t stream;
 };
 

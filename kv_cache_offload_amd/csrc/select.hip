@@ -23,6 +23,7 @@
 #include "nosa_common.h"
 #include "nosa_launch.h"
 #include "select_dev.h"
+#include "pool_dev.h"
 
 namespace nosa {
 
@@ -54,12 +55,21 @@ static int select_splits(int rows, int nb) {
   return s;
 }
 
-template <class T, int D>
+// The pool update of a decode step (one query row per unit), run by
+// wavefront 0 of the workgroup that selects (see pool_dev.h).
+struct SelPool {
+  int P, step;
+  int32_t *block_table, *slot_block, *slot_last_use;
+  const int32_t* insert_block;
+  int32_t *phys, *miss_list, *n_miss;
+};
+
+template <class T, int D, bool POOL>
 __global__ void __launch_bounds__(kSelThreads) select_kernel(
     const typename T::storage* __restrict__ q, const int32_t* __restrict__ pos,
     const typename T::storage* __restrict__ k_comp, const float* __restrict__ e_blk, int n_query,
     int n_q_heads, int n_kv_heads, int nb, int kq, int ke, int fill, int32_t* __restrict__ sel,
-    int32_t* __restrict__ n_sel, int32_t* __restrict__ ticket, float* __restrict__ score) {
+    int32_t* __restrict__ n_sel, int32_t* __restrict__ ticket, float* __restrict__ score, SelPool pl) {
   const int G = n_q_heads / n_kv_heads;
   const int row = blockIdx.y;             // (b * n_query + r) * Hkv + h
   const int h = row % n_kv_heads;
@@ -88,6 +98,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   __shared__ int s_small[2][32];
   __shared__ int s_wsum[kSelThreads / 64];
   float* my_score = score + (size_t)row * nb;
+  [[maybe_unused]] PoolLds* pool_lds = nullptr;
 
   // block eviction scores and cleared flags first, so their loads overlap the scan
   const float* eb = e_blk + (size_t)unit * nb;
@@ -132,6 +143,18 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
       }
     }
   }
+  // pool update, phase 1 (wavefront 0): the slot tables go to LDS while the
+  // scores above are still arriving
+  [[maybe_unused]] PoolUnit pu;
+  [[maybe_unused]] int p_ins = -1;
+  if constexpr (POOL) {
+    __shared__ PoolLds s_pool;
+    pu = PoolUnit{nb, pl.P, k_cap, pl.step, pl.block_table + (size_t)unit * nb, pl.slot_block + (size_t)unit * pl.P,
+                  pl.slot_last_use + (size_t)unit * pl.P, pl.miss_list + (size_t)unit * (k_cap + 1) * 2,
+                  pl.phys + (size_t)unit * k_cap, pl.n_miss + unit};
+    if (tid < 64) p_ins = pool_load(pu, pl.insert_block, b, tid, s_pool);
+    pool_lds = &s_pool;
+  }
   __syncthreads();
   const int half = tid / kHalf;
   // the fill variant takes the eviction scores' top ke + nq, trimmed below
@@ -143,6 +166,13 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   // ---- union in ascending order
   const int total = write_union<kSelThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
   if (tid == 0) n_sel[row] = total;
+  if constexpr (POOL) {
+    // pool update, phase 2 (wavefront 0) on the union just written
+    __syncthreads();
+    if (tid >= 64) return;
+    const int sel_raw = k_cap > 0 ? sel[(size_t)row * k_cap + min(tid, k_cap - 1)] : -1;
+    pool_decide(pu, tid, *pool_lds, sel_raw, total, p_ins, WaveSync{});
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -495,14 +525,25 @@ static void launch(const LaunchSelect& a) {
   char* ws = (char*)a.ws;
   int32_t* ticket = (int32_t*)ws;
   float* score = (float*)(ws + align256((size_t)rows * sizeof(int32_t)));
-  hipLaunchKernelGGL((select_kernel<T, D>), dim3(splits, rows), dim3(kSelThreads),
-                     select_lds_bytes(a.nb), a.stream, (const typename T::storage*)a.q, a.pos,
-                     (const typename T::storage*)a.k_comp, a.e_blk, a.n_query, a.n_q_heads,
-                     a.n_kv_heads, a.nb, a.kq, a.ke, a.fill ? 1 : 0, a.sel, a.n_sel, ticket, score);
+  const dim3 grid(splits, rows);
+  if (a.pool) {
+    const LaunchFetch& f = *a.pool;
+    const SelPool pl{f.pool_slots, f.step, f.block_table, f.slot_block, f.slot_last_use, f.insert_block, f.phys,
+                     f.miss_list, f.n_miss};
+    hipLaunchKernelGGL((select_kernel<T, D, true>), grid, dim3(kSelThreads), select_lds_bytes(a.nb), a.stream,
+                       (const typename T::storage*)a.q, a.pos, (const typename T::storage*)a.k_comp, a.e_blk,
+                       a.n_query, a.n_q_heads, a.n_kv_heads, a.nb, a.kq, a.ke, a.fill ? 1 : 0, a.sel, a.n_sel,
+                       ticket, score, pl);
+  } else {
+    hipLaunchKernelGGL((select_kernel<T, D, false>), grid, dim3(kSelThreads), select_lds_bytes(a.nb), a.stream,
+                       (const typename T::storage*)a.q, a.pos, (const typename T::storage*)a.k_comp, a.e_blk,
+                       a.n_query, a.n_q_heads, a.n_kv_heads, a.nb, a.kq, a.ke, a.fill ? 1 : 0, a.sel, a.n_sel,
+                       ticket, score, SelPool{});
+  }
 }
 
 void launch_select(const LaunchSelect& a) {
-  if (a.bf16 && a.n_query >= kMRows) {
+  if (a.bf16 && a.n_query >= kMRows && !a.pool) {
     const bool done = a.head_dim == 128 ? launch_multi<128>(a) : launch_multi<64>(a);
     if (done) return;
   }

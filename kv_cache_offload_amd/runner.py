@@ -190,6 +190,14 @@ class DecodeLayer:
                               window, self.blk_elems, 0, pos, self.scale, self.out, self.ws_attn,
                               stream=stream)
 
+    def attend_fetch(self, q: torch.Tensor, host_kv: torch.Tensor, window: torch.Tensor, pos: torch.Tensor,
+                     insert_src: Optional[torch.Tensor] = None, stream=None) -> None:
+        """nosa_sparse_decode_attn_fetch: the gather folded into the attention
+        over the pool (after the step's pool update)."""
+        nb.sparse_decode_attn_fetch(self.dims, q, host_kv, self.pool, self.pool_slots, self.phys, self.n_sel, self.k,
+                                    self.miss_list, self.n_miss, insert_src, window, self.blk_elems, 0, pos,
+                                    self.scale, self.out, self.ws_attn, stream=stream)
+
     def step_resident(self, q, kv, pos, stream=None) -> None:
         self.select(q, pos, stream)
         self.attend_resident(q, kv, pos, stream)
@@ -213,24 +221,37 @@ class DecodeLayer:
         return int(out.item())
 
     def step_offload(self, q, host_kv, window, pos, step: int, insert_block=None, insert_src=None,
-                     side: Optional[torch.cuda.Stream] = None) -> None:
-        """One offload step.  Without a side stream: select -> fetch -> attention
-        on one stream.  With one: select -> pool update, then the gather on the
-        side stream while the attention over the blocks already resident (and
-        the window) runs on the compute stream; then the attention over the
-        fetched blocks merges both."""
+                     side: Optional[torch.cuda.Stream] = None, fused_fetch: bool = True) -> None:
+        """One offload step.  fused_fetch (the default): selection and pool
+        update in one launch, then the gather folded into the attention (two
+        launches, one stream).  Else, without a side stream: select -> fetch
+        -> attention on one stream; with one: selection and pool update in
+        one launch, then the gather on the side stream while the attention
+        over the blocks already resident (and the window) runs on the compute
+        stream; then the attention over the fetched blocks merges both."""
         main = torch.cuda.current_stream()
-        self.select(q, pos, main)
+        if fused_fetch:
+            self.select_update(q, pos, step, insert_block, main)
+            self.attend_fetch(q, host_kv, window, pos, insert_src, main)
+            return
         if side is None:
+            self.select(q, pos, main)
             self.fetch(host_kv, step, insert_block, insert_src, main)
             self.attend_pool(q, window, pos, main)
             return
-        self.update_pool(step, insert_block, main)
+        self.select_update(q, pos, step, insert_block, main)
         side.wait_stream(main)
         self.gather(host_kv, insert_src, side)
         self.attend_pool_part(q, window, pos, 0, main)
         main.wait_stream(side)
         self.attend_pool_part(q, window, pos, 1, main)
+
+    def select_update(self, q: torch.Tensor, pos: torch.Tensor, step: int,
+                      insert_block: Optional[torch.Tensor] = None, stream=None) -> None:
+        """nosa_select_update_pool: the selection and the pool update in one launch."""
+        nb.select_update_pool(self.dims, q, pos, self.k_comp, self.e_blk, self.kq, self.ke, self.sel, self.n_sel,
+                              self.ws_sel, self.pool_slots, self.block_table, self.slot_block, self.slot_last_use,
+                              step, insert_block, self.phys, self.miss_list, self.n_miss, stream=stream)
 
     def update_pool(self, step: int, insert_block: Optional[torch.Tensor] = None, stream=None) -> None:
         nb.update_pool(self.dims, self.pool_slots, self.block_table, self.slot_block, self.slot_last_use, step,
@@ -315,13 +336,19 @@ class OffloadStack:
         del kv
 
     def step(self, t: int, qs, pos: torch.Tensor, block: int, side: Optional[torch.cuda.Stream] = None,
-             on_layer=None, fetch_events=None) -> None:
+             on_layer=None, fetch_events=None, fused_update: bool = True, fused_fetch: bool = True) -> None:
         """Decode step t of every layer: qs[l] is layer l's query [B, Hq, D],
         pos [B] int32 the positions, all inside window block `block`.  When
         the window has moved on, the block it left is complete: its compressed
         keys are built and it enters the pool.  on_layer(l, layer) runs after
         each layer is enqueued; fetch_events[l] (a list) gets the (start, end)
-        event pair around that layer's fetch."""
+        event pair around that layer's gather (with no side stream, around
+        its pool update and gather).  fused_update: the selection and the
+        pool update as one launch (nosa_select_update_pool), else as two.
+        fused_fetch: the gather folded into the attention
+        (nosa_sparse_decode_attn_fetch) on the compute stream, after the
+        one-launch selection and update; the side stream is not used and
+        fetch_events[l] gets the pair around that attention."""
         main = torch.cuda.current_stream()
         done = self.block if block > self.block else None
         for l, L in enumerate(self.layers):
@@ -330,13 +357,21 @@ class OffloadStack:
                 L.pool_window(self.windows[l][done], self.logits[l], done, main)
                 ins_blk = torch.full((L.B,), done, dtype=torch.int32, device=L.dev)
                 ins_src = self.windows[l][done]
-            L.select(qs[l], pos, main)
             ev = None
             if fetch_events is not None:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[0].record(main)
             window = self.windows[l][block]
-            if side is None:
+            if fused_fetch:
+                L.select_update(qs[l], pos, t, ins_blk, main)
+                if ev is not None:
+                    ev[0].record(main)
+                L.attend_fetch(qs[l], self.host[l], window, pos, ins_src, main)
+                if ev is not None:
+                    ev[1].record(main)
+            elif side is None:
+                L.select(qs[l], pos, main)
+                if ev is not None:
+                    ev[0].record(main)
                 L.fetch(self.host[l], t, ins_blk, ins_src, main)
                 if ev is not None:
                     ev[1].record(main)
@@ -344,8 +379,14 @@ class OffloadStack:
             else:
                 # the gather on the side stream, the attention over the resident
                 # blocks meanwhile (see DecodeLayer.step_offload)
-                L.update_pool(t, ins_blk, main)
+                if fused_update:
+                    L.select_update(qs[l], pos, t, ins_blk, main)
+                else:
+                    L.select(qs[l], pos, main)
+                    L.update_pool(t, ins_blk, main)
                 side.wait_stream(main)
+                if ev is not None:
+                    ev[0].record(side)
                 L.gather(self.host[l], ins_src, side)
                 if ev is not None:
                     ev[1].record(side)

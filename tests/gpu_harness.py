@@ -126,7 +126,7 @@ def compare_unit(w: NI.Workload, K, V, lam, q, b, h, gpu_sel, gpu_out=None, gpu_
 
 
 def run_offload(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None, side_stream: bool = True,
-                record_tables: bool = True, offsets=None, reset_at: Optional[int] = None):
+                record_tables: bool = True, offsets=None, reset_at: Optional[int] = None, fused_fetch: bool = False):
     """GPU decode in offload mode (KV in pinned host memory, HBM block pool).
 
     offsets: per batch entry, how many positions it lags the workload's
@@ -134,7 +134,8 @@ def run_offload(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None, side_
     windows complete blocks on different steps: each step pools and inserts
     the blocks that just completed, per entry.  reset_at: before that step
     the pool tables are cleared (a cold restart: every resident block is
-    forgotten, the compressed keys are kept)."""
+    forgotten, the compressed keys are kept).  fused_fetch: the gather folded
+    into the attention (nosa_select_update_pool + nosa_sparse_decode_attn_fetch)."""
     n = w.n_steps if steps is None else steps
     kv_dev, logits, qd, _ = device_inputs(w, K, V, lam, q)
     offs = np.zeros(w.batch, np.int64) if offsets is None else np.asarray(offsets, np.int64)
@@ -167,7 +168,7 @@ def run_offload(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None, side_
             for k in ("block_table", "slot_block", "slot_last_use"):
                 getattr(layer, k).fill_(-1)
         window = blocks_of(c).contiguous()
-        layer.step_offload(qd[t], host, window, pos[t], t, ins_blk, ins_src, side)
+        layer.step_offload(qd[t], host, window, pos[t], t, ins_blk, ins_src, side, fused_fetch)
         for k in ("sel", "n_sel", "phys", "miss_list", "n_miss"):
             rec[k].append(getattr(layer, k).clone())
         rec["out"].append(layer.out.float().clone())

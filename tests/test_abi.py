@@ -299,3 +299,48 @@ def test_variant_calls_check_like_their_bases(lib):
         nb.sparse_decode_attn_bias(d, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, FAKE, FAKE, ws_bytes=need_a - 1,
                                    stream=0)
     assert e.value.code == nb.ERR_WORKSPACE
+
+
+def test_pool_keys_entries_checks(lib):
+    with pytest.raises(nb.NosaError) as e:
+        nb.pool_keys_entries(_d(), FAKE, 0, 0, FAKE, None, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_ARG and "entry_block" in str(e.value)
+    with pytest.raises(nb.NosaError) as e:
+        nb.pool_keys_entries(_d(), FAKE, -1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_ARG
+    with pytest.raises(nb.NosaError) as e:
+        nb.pool_keys_entries(_d(head_dim=96), FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == nb.ERR_UNSUPPORTED
+
+
+def test_select_update_pool_checks(lib):
+    """Both calls' checks, before anything is launched: the pool's k <= 64
+    and pool_slots > k, the tables, and the selection's workspace."""
+    d = _d()
+    need = nb.workspace_size(d, nb.OP_SELECT, 1, 16, 48)
+
+    def call(kq=16, ke=48, ws_bytes=need, P=80, bt=FAKE):
+        nb.select_update_pool(d, FAKE, FAKE, FAKE, FAKE, kq, ke, FAKE, FAKE, FAKE, P, bt, FAKE, FAKE, 0, None,
+                              FAKE, FAKE, FAKE, ws_bytes=ws_bytes, stream=0)
+
+    for kw, code in ((dict(kq=16, ke=49), nb.ERR_UNSUPPORTED), (dict(kq=-1), nb.ERR_ARG),
+                     (dict(P=64), nb.ERR_ARG), (dict(P=2000), nb.ERR_UNSUPPORTED), (dict(bt=None), nb.ERR_ARG),
+                     (dict(ws_bytes=need - 1), nb.ERR_WORKSPACE)):
+        with pytest.raises(nb.NosaError) as e:
+            call(**kw)
+        assert e.value.code == code, kw
+
+
+def test_attention_fetch_checks(lib):
+    d = _d()
+    need = nb.workspace_size(d, nb.OP_ATTN, 1, 64, 0)
+
+    def call(host=FAKE, k_cap=64, P=80, part_ws=need):
+        nb.sparse_decode_attn_fetch(d, FAKE, host, FAKE, P, FAKE, FAKE, k_cap, FAKE, FAKE, None, FAKE, 0, 0, FAKE,
+                                    None, FAKE, FAKE, ws_bytes=part_ws, stream=0)
+
+    for kw, code in ((dict(host=None), nb.ERR_ARG), (dict(k_cap=65), nb.ERR_UNSUPPORTED), (dict(P=0), nb.ERR_ARG),
+                     (dict(part_ws=need - 1), nb.ERR_WORKSPACE)):
+        with pytest.raises(nb.NosaError) as e:
+            call(**kw)
+        assert e.value.code == code, kw

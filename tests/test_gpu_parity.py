@@ -242,8 +242,9 @@ def test_determinism_across_split_counts_and_launch_orders():
         are bit-identical;
       * launch order: two layers' steps interleaved on two streams against
         the same steps run one layer after the other;
-      * the offload step with and without the side stream: identical pool
-        tables, miss lists and slots."""
+      * the offload step with the gather on a side stream, on the compute
+        stream, and folded into the attention: identical pool tables, miss
+        lists and slots."""
     _banner("determinism: split counts, worker counts, launch orders")
     w = _w("layer32k", batch=16, prompt_len=64 * 100 + 20, n_steps=3)
     K, V, lam, q = NI.layer_inputs(w)
@@ -302,12 +303,13 @@ def test_determinism_across_split_counts_and_launch_orders():
     wo = _w("offload", batch=3, prompt_len=64 * 40 + 30, n_steps=60, kq=4, ke=6, pool_slots=14)
     Ko, Vo, lamo, qo = NI.layer_inputs(wo)
     ra, _, _ = H.run_offload(wo, Ko, Vo, lamo, qo, side_stream=True)
-    rb, _, _ = H.run_offload(wo, Ko, Vo, lamo, qo, side_stream=False)
-    for key in ("sel", "n_sel", "phys", "miss_list", "n_miss", "block_table", "slot_block"):
+    for other in (dict(side_stream=False), dict(fused_fetch=True)):
+        rb, _, _ = H.run_offload(wo, Ko, Vo, lamo, qo, **other)
+        for key in ("sel", "n_sel", "phys", "miss_list", "n_miss", "block_table", "slot_block"):
+            for t in range(wo.n_steps):
+                assert np.array_equal(ra[key][t], rb[key][t]), (other, key, t)
         for t in range(wo.n_steps):
-            assert np.array_equal(ra[key][t], rb[key][t]), (key, t)
-    for t in range(wo.n_steps):
-        assert float(np.abs(ra["out"][t] - rb["out"][t]).max()) <= atol
+            assert float(np.abs(ra["out"][t] - rb["out"][t]).max()) <= atol
 
 
 # ------------------------------------------------------- end-to-end decode
@@ -346,12 +348,16 @@ def _pool_consistent(layer, host, b, h):
             assert sb[s] == blk
 
 
-@pytest.mark.parametrize("side", [True, False])
-def test_offload_small_pool_matches_oracle(side):
-    _banner(f"offload: B=3, L ragged, 100 steps, pool 14 slots, side stream={side}")
+OFFLOAD_MODES = {"side-stream": dict(side_stream=True, fused_fetch=False),
+                 "one-stream": dict(side_stream=False, fused_fetch=False), "fused-fetch": dict(fused_fetch=True)}
+
+
+@pytest.mark.parametrize("mode", list(OFFLOAD_MODES))
+def test_offload_small_pool_matches_oracle(mode):
+    _banner(f"offload: B=3, L ragged, 100 steps, pool 14 slots, {mode}")
     w = _w("offload", batch=3, prompt_len=64 * 40 + 30, n_steps=100, kq=4, ke=6, pool_slots=14)
     K, V, lam, q = NI.layer_inputs(w)
-    rec, layer, host = H.run_offload(w, K, V, lam, q, side_stream=side)
+    rec, layer, host = H.run_offload(w, K, V, lam, q, **OFFLOAD_MODES[mode])
     total = 0
     for b in range(w.batch):
         for h in range(w.n_kv_heads):
@@ -361,8 +367,8 @@ def test_offload_small_pool_matches_oracle(side):
     assert total > w.batch * w.n_kv_heads * 10
 
 
-@pytest.mark.parametrize("side", [True, False])
-def test_offload_ragged_positions(side):
+@pytest.mark.parametrize("mode", list(OFFLOAD_MODES))
+def test_offload_ragged_positions(mode):
     """Batch entries at their own positions (lagging the first by 0, 17, 40
     and 63 tokens), so their windows complete blocks on different steps: each
     completed block is pooled for its entry alone (nosa_pool_keys_entries)
@@ -370,11 +376,11 @@ def test_offload_ragged_positions(side):
     against the oracle at its own positions; the compressed keys and eviction
     scores of each entry's complete blocks bit-exact, and nothing written for
     blocks an entry has not completed."""
-    _banner(f"offload ragged positions: B=4, lags 0/17/40/63, 100 steps, pool 14, side stream={side}")
+    _banner(f"offload ragged positions: B=4, lags 0/17/40/63, 100 steps, pool 14, {mode}")
     w = _w("offload", batch=4, prompt_len=64 * 40 + 30, n_steps=100, kq=4, ke=6, pool_slots=14)
     K, V, lam, q = NI.layer_inputs(w)
     offs = [0, 17, 40, 63]
-    rec, layer, host = H.run_offload(w, K, V, lam, q, side_stream=side, offsets=offs)
+    rec, layer, host = H.run_offload(w, K, V, lam, q, offsets=offs, **OFFLOAD_MODES[mode])
     P = rec["positions"]
     done_steps = [set(np.nonzero(P[1:, b] // 64 > P[:-1, b] // 64)[0] + 1) for b in range(w.batch)]
     assert all(done_steps) and len(set().union(*done_steps)) == sum(map(len, done_steps))   # no two together
@@ -422,14 +428,15 @@ def test_offload_cold_restart_mid_run(reset_at):
             _pool_consistent(layer, host, b, h)
 
 
-@pytest.mark.parametrize("kq,ke", [(8, 56), (32, 32), (64, 0)], ids=["kq8", "kq32", "kq64"])
-def test_offload_sweep_points(kq, ke):
+@pytest.mark.parametrize("kq,ke,fused", [(8, 56, False), (32, 32, True), (64, 0, False)], ids=["kq8", "kq32", "kq64"])
+def test_offload_sweep_points(kq, ke, fused):
     """The kq/k sweep points of the offload workload (k = 64, 16K context,
-    pool of 80) at batch 2, every unit, 96 steps (one block completes)."""
-    _banner(f"offload sweep point kq={kq} ke={ke}: B=2, 16K context, pool 80, 96 steps")
+    pool of 80) at batch 2, every unit, 96 steps (one block completes); one
+    of them with the gather folded into the attention."""
+    _banner(f"offload sweep point kq={kq} ke={ke}: B=2, 16K context, pool 80, 96 steps, fused fetch {fused}")
     w = _w("offload", batch=2, n_steps=96, kq=kq, ke=ke)
     K, V, lam, q = NI.layer_inputs(w)
-    rec, layer, host = H.run_offload(w, K, V, lam, q)
+    rec, layer, host = H.run_offload(w, K, V, lam, q, fused_fetch=fused)
     for b in range(w.batch):
         for h in range(w.n_kv_heads):
             H.check_offload_unit(w, K, V, lam, q, rec, b, h)
@@ -488,11 +495,12 @@ def test_stack128k_sampled_layers():
         assert misses >= 3 * (w.kq + w.ke), (lid, misses)     # at least the cold step's
 
 
-def test_stack_small_crosses_blocks():
+@pytest.mark.parametrize("fused_fetch", [False, True], ids=["side-stream", "fused-fetch"])
+def test_stack_small_crosses_blocks(fused_fetch):
     """The stack driver across block boundaries: three layers, a ragged
     prompt and 150 steps, so the window completes blocks that enter every
     layer's pool; every unit of every layer against the oracle."""
-    _banner("stack: 3 layers, B=2, ragged prompt, 150 steps across blocks, pool 20")
+    _banner(f"stack: 3 layers, B=2, ragged prompt, 150 steps across blocks, pool 20, fused fetch {fused_fetch}")
     w = _w("stack128k", batch=2, prompt_len=64 * 30 + 41, n_steps=150, kq=6, ke=8, pool_slots=20, n_layers=3)
     positions = w.positions()
     blocks = [int(p) // 64 for p in positions]
@@ -515,7 +523,7 @@ def test_stack_small_crosses_blocks():
 
     side = torch.cuda.Stream()
     for t in range(w.n_steps):
-        stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer)
+        stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer, fused_fetch=fused_fetch)
     torch.cuda.synchronize()
     assert blocks[-1] > blocks[0] + 1
     for l in range(w.n_layers):
