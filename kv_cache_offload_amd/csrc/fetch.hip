@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(64) pool_update_kernel(
   const int n_raw = n_sel[unit];
   const int sel_raw = k_cap > 0 ? sel[(size_t)unit * k_cap + min(lane, k_cap - 1)] : -1;
   const int ins = pool_load(u, insert_block, unit / n_kv_heads, lane, L);
-  pool_decide(u, lane, L, sel_raw, n_raw, ins, BlockSync{});
+  pool_decide(u, lane, L, sel_raw, n_raw, ins, BlockSync{}, [&](int blk) { return u.bt[blk]; });
 }
 
 // One workgroup per (miss entry, unit); entry k_cap is the inserted block.

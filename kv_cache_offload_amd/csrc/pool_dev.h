@@ -79,10 +79,11 @@ __device__ __forceinline__ int pool_load(const PoolUnit& u, const int32_t* inser
   return ins;
 }
 
-// Phase 2: sel_raw is this lane's entry of S (entries past n_raw ignored).
-template <class Sync>
+// Phase 2: sel_raw is this lane's entry of S (entries past n_raw ignored);
+// slot_of(block) gives the block table's entry of a block in [0, nb).
+template <class Sync, class SlotOf>
 __device__ __forceinline__ void pool_decide(const PoolUnit& u, int lane, PoolLds& L, int sel_raw, int n_raw,
-                                            int ins, Sync sync) {
+                                            int ins, Sync sync, SlotOf slot_of) {
   const int nb = u.nb, P = u.P, k_cap = u.k_cap, step = u.step;
   int32_t* bt = u.bt;
   int32_t* ml = u.ml;
@@ -103,8 +104,8 @@ __device__ __forceinline__ void pool_decide(const PoolUnit& u, int lane, PoolLds
   if (blk <= before_max) blk = -1;  // not strictly ascending: duplicate or out of order
   if (ins >= nb) ins = -1;
   // the two block-table lookups that depend on S go out together
-  const int bt_blk = blk >= 0 ? bt[blk] : -1;
-  const int bt_ins = ins >= 0 ? bt[ins] : -1;
+  const int bt_blk = blk >= 0 ? slot_of(blk) : -1;
+  const int bt_ins = ins >= 0 ? slot_of(ins) : -1;
   sync();                           // the slot tables are in LDS
   int slot = -1;
   if (blk >= 0 && bt_blk >= 0 && bt_blk < P && L.blk[bt_blk] == blk) slot = bt_blk;

@@ -28,6 +28,8 @@
 namespace nosa {
 
 constexpr int kSelThreads = 1024;
+constexpr int kMaxSelectBlocks = 4096;  // nb limit of the selection (256K tokens)
+constexpr int kMaxPoolK = 64;           // kq + ke limit of the pool update
 constexpr int kHalf = kSelThreads / 2;
 
 size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb) {
@@ -143,17 +145,26 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
       }
     }
   }
-  // pool update, phase 1 (wavefront 0): the slot tables go to LDS while the
-  // scores above are still arriving
+  // pool update, phase 1: the slot tables go to LDS (wavefront 0) while the
+  // scores above are still arriving, and a block -> slot map of the unit's
+  // candidates is cleared (every thread), so the update needs no memory
+  // round trip once the set is known
   [[maybe_unused]] PoolUnit pu;
   [[maybe_unused]] int p_ins = -1;
+  [[maybe_unused]] int16_t* slot_map = nullptr;
+  [[maybe_unused]] int32_t* union_ids = nullptr;
   if constexpr (POOL) {
     __shared__ PoolLds s_pool;
+    __shared__ int16_t s_map[kMaxSelectBlocks];
+    __shared__ int32_t s_union[kMaxPoolK];
     pu = PoolUnit{nb, pl.P, k_cap, pl.step, pl.block_table + (size_t)unit * nb, pl.slot_block + (size_t)unit * pl.P,
                   pl.slot_last_use + (size_t)unit * pl.P, pl.miss_list + (size_t)unit * (k_cap + 1) * 2,
                   pl.phys + (size_t)unit * k_cap, pl.n_miss + unit};
     if (tid < 64) p_ins = pool_load(pu, pl.insert_block, b, tid, s_pool);
+    for (int i = tid; i < nb; i += kSelThreads) s_map[i] = -1;
     pool_lds = &s_pool;
+    slot_map = s_map;
+    union_ids = s_union;
   }
   __syncthreads();
   const int half = tid / kHalf;
@@ -164,14 +175,25 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
   if (fill) keep_fill<kSelThreads>(key_e, flag_q, flag_e, c, ke, reinterpret_cast<int32_t*>(key_q), s_wsum, tid);
 
   // ---- union in ascending order
-  const int total = write_union<kSelThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
-  if (tid == 0) n_sel[row] = total;
-  if constexpr (POOL) {
-    // pool update, phase 2 (wavefront 0) on the union just written
+  if constexpr (!POOL) {
+    const int total = write_union<kSelThreads>(flag_q, flag_e, c, sel + (size_t)row * k_cap, k_cap, s_wsum, tid);
+    if (tid == 0) n_sel[row] = total;
+  } else {
+    // the union into LDS, then out; pool update, phase 2 (wavefront 0) on it
+    const int total = write_union<kSelThreads>(flag_q, flag_e, c, union_ids, k_cap, s_wsum, tid);
     __syncthreads();
+    int32_t* sr = sel + (size_t)row * k_cap;
+    for (int i = tid; i < k_cap; i += kSelThreads) sr[i] = union_ids[i];
+    if (tid == 0) n_sel[row] = total;
     if (tid >= 64) return;
-    const int sel_raw = k_cap > 0 ? sel[(size_t)row * k_cap + min(tid, k_cap - 1)] : -1;
-    pool_decide(pu, tid, *pool_lds, sel_raw, total, p_ins, WaveSync{});
+    PoolLds& L = *pool_lds;
+    for (int s = tid; s < pu.P; s += 64) {
+      const int blk = L.blk[s];
+      if (blk >= 0 && blk < nb) slot_map[blk] = (int16_t)s;
+    }
+    WaveSync{}();
+    const int sel_raw = k_cap > 0 ? union_ids[min(tid, k_cap - 1)] : -1;
+    pool_decide(pu, tid, L, sel_raw, total, p_ins, WaveSync{}, [&](int blk) { return (int)slot_map[blk]; });
   }
 }
 
