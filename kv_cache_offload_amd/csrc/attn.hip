@@ -135,10 +135,15 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t blk_elems = (size_t)2 * kBlock * D;
 
+  // the position, the set size and this wavefront's entry go out together
+  // (one memory round trip before the block's loads, not three)
+  const int e_w = (int)blockIdx.y * WAVES + wave;
   const int p = pos[br];
+  const int ns_raw = n_sel[unit];
+  const int pb_raw = e_w < k_cap ? phys[(size_t)unit * k_cap + e_w] : -1;
   const bool valid_pos = (p >= 0 && p < nb * kBlock);
   const int c = valid_pos ? p / kBlock : 0;
-  int ns = valid_pos ? n_sel[unit] : -1;
+  int ns = valid_pos ? ns_raw : -1;
   ns = ns < 0 ? -1 : (ns > k_cap ? k_cap : ns);
   const int n_ent = ns + 1;  // selected blocks, then the window (none if pos is invalid)
 
@@ -157,12 +162,12 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   {
     // entry e of this split: part 0 skips the fetched slots, part 1 takes
     // only those (and no window)
-    const int e = (int)blockIdx.y * WAVES + wave;
+    const int e = e_w;
     const typename T::storage* blk = nullptr;
     [[maybe_unused]] typename T::storage* copy_to = nullptr;   // PART 2: the slot a fetched block fills
     int len = 0, lblk = -1;      // lblk: the block's logical id (its position / 64)
     if (e < ns) {
-      const int pb = phys[(size_t)unit * k_cap + e];
+      const int pb = pb_raw;
       bool take = pb >= 0 && pb < blocks_per_head;
       if ((PART == 0 || PART == 1) && take) take = slot_fetched(pb, ml, nm, k_cap) == (PART == 1);
       if (take) {
@@ -261,9 +266,20 @@ __global__ void __launch_bounds__(64 * kChunkWaves) chunk_attn_kernel(
     int n_kv_heads, int nb, int n_query, uint16_t* __restrict__ out, int32_t* __restrict__ ticket,
     float* __restrict__ part_ml, float* __restrict__ part_o) {
   constexpr int ND = D / 16, WAVES = kChunkWaves, G = 16 / NR, NT = 64 * WAVES;
-  const int u = blockIdx.x, split = blockIdx.y, n_split = gridDim.y;
+  // XCD-aware order: workgroups go to the 8 XCDs round-robin in linear
+  // order, and the row groups of one KV head attend mostly the same blocks,
+  // the same share of them for the same split.  So the linear index picks
+  // the (KV head, split) group first: every workgroup of a group lands on
+  // the same XCD (with 8 groups; 4 groups: two XCDs), whose L2 then serves
+  // the group's re-reads of those blocks.
+  const int n_split = gridDim.y;
+  const int n_grp = n_kv_heads * n_split;
+  const int wid = (int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x;
+  const int grp = wid % n_grp, brg = wid / n_grp;
+  const int h = grp / n_split, split = grp % n_split;
+  const int u = brg * n_kv_heads + h;
   const int n_groups = (n_query + NR - 1) / NR;
-  const int h = u % n_kv_heads, brg = u / n_kv_heads, b = brg / n_groups, r0 = (brg % n_groups) * NR;
+  const int b = brg / n_groups, r0 = (brg % n_groups) * NR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ AttnLds<D, WAVES, 16> L;
   __shared__ int s_ent[kChunkMaxShare];
@@ -272,12 +288,15 @@ __global__ void __launch_bounds__(64 * kChunkWaves) chunk_attn_kernel(
 
   // ---- the union (the block marks live in the merge buffer until the merge)
   uint32_t* s_mask = reinterpret_cast<uint32_t*>(&L.o[0][0][0]);
-  int rp[NR], rn[NR];                              // each row's position and selection count
+  int rp[NR], rn[NR], rs[NR];                      // each row's position, selection count and entry tid
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
     const int r = r0 + rr;
+    const size_t row = ((size_t)b * n_query + r) * n_kv_heads + h;
     rp[rr] = r < n_query ? pos[(size_t)b * n_query + r] : -1;
-    rn[rr] = r < n_query ? n_sel[((size_t)b * n_query + r) * n_kv_heads + h] : 0;
+    rn[rr] = r < n_query ? n_sel[row] : 0;
+    // the first NT entries go out with the counts, not behind them
+    rs[rr] = (r < n_query && tid < k_cap) ? sel[row * k_cap + tid] : -1;
   }
   for (int j = tid; j < nb; j += NT) s_mask[j] = 0u;
   __syncthreads();
@@ -288,7 +307,7 @@ __global__ void __launch_bounds__(64 * kChunkWaves) chunk_attn_kernel(
     const size_t row = ((size_t)b * n_query + r0 + rr) * n_kv_heads + h;
     const int ns = rn[rr] < 0 ? 0 : (rn[rr] > k_cap ? k_cap : rn[rr]);
     for (int e = tid; e < ns; e += NT) {
-      const int blk = sel[row * k_cap + e];
+      const int blk = e == tid ? rs[rr] : sel[row * k_cap + e];
       if (blk >= 0 && blk < nb) atomicOr(&s_mask[blk], 1u << rr);
     }
     if (tid == 0) atomicOr(&s_mask[p / kBlock], 1u << (NR + rr));
