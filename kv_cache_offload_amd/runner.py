@@ -319,28 +319,40 @@ class OffloadStack:
         self.windows = [{} for _ in range(n_layers)]
         self.block = None                    # window block of the last step
 
-    def load_layer(self, l: int, K: np.ndarray, V: np.ndarray, lam: np.ndarray, prompt_blocks: int,
+    def load_layer(self, l: int, K: np.ndarray, V: np.ndarray, lam: np.ndarray, prompt_blocks,
                    window_blocks) -> None:
         """Layer l's cache from K, V [B, Hkv, T, D] and logits [B, Hkv, T]
         (float32 arrays holding cache-dtype values): the compressed keys of
         blocks [0, prompt_blocks) are pooled on the GPU, the listed window
-        blocks stay in HBM, and the packed cache moves to pinned host memory."""
+        blocks stay in HBM, and the packed cache moves to pinned host memory.
+        prompt_blocks is one count for the batch, or one per batch entry
+        (entries at their own positions)."""
         L = self.layers[l]
         kv = to_device_blocks(K, V, L.NB, L.dtype, device=L.dev)
         logits = pad_logits(torch.from_numpy(lam).to(L.dev), L.NB)
-        L.pool_blocks(kv, logits, 0, prompt_blocks)
+        pb = np.broadcast_to(np.asarray(prompt_blocks, dtype=np.int64), (L.B,))
+        lo, hi = int(pb.min()), int(pb.max())
+        L.pool_blocks(kv, logits, 0, lo)
+        for j in range(lo, hi):            # blocks complete for some entries only
+            L.pool_entries(kv, logits, torch.from_numpy(np.where(j < pb, j, -1).astype(np.int32)).to(L.dev))
         self.windows[l] = {int(c): kv[:, :, int(c)].clone() for c in window_blocks}
         self.host[l].copy_(kv)
         self.logits[l] = logits
-        self.block = prompt_blocks if self.block is None else self.block
+        self.block = (prompt_blocks if lo == hi and np.ndim(prompt_blocks) == 0 else pb.copy()) \
+            if self.block is None else self.block
         del kv
+
+    def _per_entry(self, l: int, blocks: np.ndarray) -> torch.Tensor:
+        """[B, Hkv, block]: entry b's block blocks[b] of layer l's window buffers."""
+        return torch.stack([self.windows[l][int(c)][b] for b, c in enumerate(blocks)])
 
     def step(self, t: int, qs, pos: torch.Tensor, block: int, side: Optional[torch.cuda.Stream] = None,
              on_layer=None, fetch_events=None, fused_update: bool = True, fused_fetch: bool = True) -> None:
         """Decode step t of every layer: qs[l] is layer l's query [B, Hq, D],
-        pos [B] int32 the positions, all inside window block `block`.  When
-        the window has moved on, the block it left is complete: its compressed
-        keys are built and it enters the pool.  on_layer(l, layer) runs after
+        pos [B] int32 the positions, inside window block `block` (one for the
+        batch, or one per batch entry).  When an entry's window has moved on,
+        the block it left is complete: its compressed keys are built and it
+        enters that entry's pool.  on_layer(l, layer) runs after
         each layer is enqueued; fetch_events[l] (a list) gets the (start, end)
         event pair around that layer's gather (with no side stream, around
         its pool update and gather).  fused_update: the selection and the
@@ -350,17 +362,32 @@ class OffloadStack:
         one-launch selection and update; the side stream is not used and
         fetch_events[l] gets the pair around that attention."""
         main = torch.cuda.current_stream()
-        done = self.block if block > self.block else None
+        ragged = np.ndim(block) > 0 or np.ndim(self.block) > 0
+        if ragged:
+            B = self.layers[0].B
+            cur = np.broadcast_to(np.asarray(block, dtype=np.int64), (B,)).copy()
+            prev = np.broadcast_to(np.asarray(self.block, dtype=np.int64), (B,))
+            moved = cur > prev
+            entry_done = torch.from_numpy(np.where(moved, prev, -1).astype(np.int32)).to(self.layers[0].dev)
+        else:
+            done = self.block if block > self.block else None
         for l, L in enumerate(self.layers):
             ins_blk = ins_src = None
-            if done is not None:
-                L.pool_window(self.windows[l][done], self.logits[l], done, main)
-                ins_blk = torch.full((L.B,), done, dtype=torch.int32, device=L.dev)
-                ins_src = self.windows[l][done]
+            if ragged:
+                window = self._per_entry(l, cur)
+                if moved.any():
+                    ins_src = self._per_entry(l, np.where(moved, prev, cur))
+                    L.pool_entries(ins_src, self.logits[l], entry_done, L.blk_elems, 0, main)
+                    ins_blk = entry_done
+            else:
+                window = self.windows[l][block]
+                if done is not None:
+                    L.pool_window(self.windows[l][done], self.logits[l], done, main)
+                    ins_blk = torch.full((L.B,), done, dtype=torch.int32, device=L.dev)
+                    ins_src = self.windows[l][done]
             ev = None
             if fetch_events is not None:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            window = self.windows[l][block]
             if fused_fetch:
                 L.select_update(qs[l], pos, t, ins_blk, main)
                 if ev is not None:
@@ -397,7 +424,7 @@ class OffloadStack:
                 fetch_events[l].append(ev)
             if on_layer is not None:
                 on_layer(l, L)
-        self.block = block
+        self.block = cur if ragged else block
 
 
 def to_device_blocks(K: np.ndarray, V: np.ndarray, n_blocks: int, dtype: str, device="cuda") -> torch.Tensor:

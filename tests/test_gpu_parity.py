@@ -535,6 +535,50 @@ def test_stack_small_crosses_blocks(fused_fetch):
                 _pool_consistent(stack.layers[l], stack.host[l], b, h)
 
 
+@pytest.mark.parametrize("fused_fetch", [True, False], ids=["fused-fetch", "side-stream"])
+def test_stack_ragged_positions(fused_fetch):
+    """The stack driver with batch entries at their own positions (lags 0, 20
+    and 45 tokens): per-entry window blocks, each entry's completed blocks
+    pooled and inserted for that entry alone, in every layer; every unit of
+    every layer against the oracle at its own positions."""
+    _banner(f"stack: 3 layers, B=3, lags 0/20/45, 150 steps, pool 20, fused fetch {fused_fetch}")
+    w = _w("stack128k", batch=3, prompt_len=64 * 30 + 41, n_steps=150, kq=6, ke=8, pool_slots=20, n_layers=3)
+    lags = np.array([0, 20, 45])
+    P = w.positions()[:, None] - lags[None, :]                       # [steps, B]
+    C = P // 64
+    stack = R.OffloadStack(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype,
+                           w.kq, w.ke, w.pool_slots)
+    inputs, qs = [], []
+    for l in range(w.n_layers):
+        K, V, lam, q = NI.layer_inputs(w, l)
+        stack.load_layer(l, K, V, lam, C[0], sorted(set(C.ravel().tolist())))
+        inputs.append((K, V, lam, q))
+        qs.append(torch.from_numpy(q).cuda().to(torch.bfloat16))
+    pos = torch.from_numpy(P.astype(np.int32)).cuda()
+    keys = ("sel", "n_sel", "phys", "miss_list", "n_miss")
+    rec = [{k: [] for k in keys + ("out",)} for _ in range(w.n_layers)]
+
+    def on_layer(i, L):
+        for k in keys:
+            rec[i][k].append(getattr(L, k).clone())
+        rec[i]["out"].append(L.out.float().clone())
+
+    side = torch.cuda.Stream()
+    for t in range(w.n_steps):
+        stack.step(t, [qd[t] for qd in qs], pos[t], C[t], side, on_layer, fused_fetch=fused_fetch)
+    torch.cuda.synchronize()
+    steps_done = [set(np.nonzero(C[1:, b] > C[:-1, b])[0] + 1) for b in range(w.batch)]
+    assert all(steps_done) and len(set().union(*steps_done)) == sum(map(len, steps_done))
+    for l in range(w.n_layers):
+        r = {k: [x.cpu().numpy() for x in v] for k, v in rec[l].items()}
+        r["positions"] = P
+        K, V, lam, q = inputs[l]
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                H.check_offload_unit(w, K, V, lam, q, r, b, h)
+                _pool_consistent(stack.layers[l], stack.host[l], b, h)
+
+
 def test_prefill128k_chunk_selection():
     _banner("prefill128k: pool 131072 tokens, select for 64 query rows")
     w = NI.WORKLOADS["prefill128k"]
