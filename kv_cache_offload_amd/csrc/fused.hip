@@ -16,9 +16,12 @@
 //   Q workers (nE <= j < W)  attend the window while the scores arrive, then
 //                            each takes top-kq itself (the first one also
 //                            writes the union out) and attends its share of
-//                            X = Gamma_q \ Gamma_e;
-//   merge workgroups (j >= W) each combine all W partials for one slice of
-//                            the unit's outputs and store it.
+//                            X = Gamma_q \ Gamma_e; then Q worker q combines
+//                            all W partials for slice q of the unit's
+//                            outputs and stores it;
+//   merge workgroups (j >= W) do that final merge instead when the Q workers
+//                            are too few for one output per thread (nM = 0
+//                            otherwise).
 // Work is dealt in 32-token halves of blocks, one per wavefront at a time.
 // Every E and Q worker publishes one partial (its wavefronts merged in LDS).
 //
@@ -31,14 +34,18 @@
 // starts after a merge gave up waiting for it tags its words with its own
 // launch's flag.  The workspace never needs resetting between launches.
 //
-// Workgroup j of unit u has index j * U + u, and every wait is on a
-// workgroup of lower index (Q workers wait on E workers, merge workgroups on
-// all the others), which the dispatcher has started earlier, so each wait
-// ends; the waits are bounded as well.  A wait that hits its bound is
-// counted in the workspace (nosa_step_timeouts reads the count) and the
-// outputs it feeds are written as NaN, never a hang.  The merge workgroups
-// come last in the grid, so they occupy CUs only once E workers have
-// finished.
+// Workgroup j of unit u has index j * U + u.  Q workers wait on E workers'
+// scores and merge workgroups on all the others, workgroups of lower index,
+// which the dispatcher has started earlier.  A Q worker's final merge also
+// waits on the unit's other Q workers, some of higher index when there are
+// two or more, so W >= 3: then the grid stays below 256 + units <= 384
+// workgroups (W = ceil(256 / units)), which the MI355X holds all at once (two
+// or more of these workgroups fit a CU), and E workers wait on nobody, so
+// every wait ends.  The waits are bounded as well: a wait that hits its bound
+// is counted in the workspace (nosa_step_timeouts reads the count) and the
+// outputs it feeds are written as NaN, never a hang.  Merge workgroups, when
+// there are any, come last in the grid, so they occupy CUs only once E
+// workers have finished.
 #include "nosa_common.h"
 #include "nosa_launch.h"
 #include "attn_dev.h"
@@ -75,9 +82,14 @@ static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int 
   nQ = nQ > W - 1 ? W - 1 : nQ;
   g.nQ = nQ;
   g.nE = W - nQ;
-  // merge workgroups: about 256 outputs each, at most 4
+  // the final merge: by the Q workers, one slice of the outputs each, when
+  // a slice fits one output per thread; else by merge workgroups of about
+  // 256 outputs each, at most 4
   const int GD = (n_q_heads / n_kv_heads) * head_dim;
-  g.nM = GD >= 1024 ? 4 : (GD >= 512 ? 2 : 1);
+  if (nQ > 0 && (GD + nQ - 1) / nQ <= kStepThreads)
+    g.nM = 0;
+  else
+    g.nM = GD >= 1024 ? 4 : (GD >= 512 ? 2 : 1);
   const size_t U = g.units;
   const size_t rec = (size_t)kStepGMax * head_dim + 2 * kStepGMax;
   size_t o = 0;
@@ -530,6 +542,17 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   const bool poison = __syncthreads_or(timed_out ? 1 : 0) != 0;
   merge_waves_keep<D, kStepWaves, kStepGMax>(L, m_run, l_run, o, G, tid, own);
   publish_part_ll<D, kStepWaves, kStepGMax>(L, G, tid, own, recs + (size_t)j * REC, flag, poison);
+  if (nM == 0 && is_q) {
+    // ---------------- the final merge: Q worker qj stores slice qj of the
+    // unit's outputs from all W records (its own among them)
+    const int qj = j - nE;
+    const int GD = G * D, per = (GD + nQ - 1) / nQ;
+    const int lo = min(GD, qj * per), n_out = min(per, GD - lo);
+    lds_barrier();                                    // L's record reads are done
+    typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
+    merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs, [&]() { return flag; },
+                                                    kSpinLimit, err, out_g);
+  }
 }
 
 template <class T, int D>
