@@ -433,6 +433,10 @@ def _offload_leg(torch, NI, R, nb):
         ms = float(np.median(step_ms[warm]))
         miss_bytes = misses.astype(np.float64) * blk_bytes
         link = float(miss_bytes[warm].sum() / (fetch_ms[warm].sum() * 1e-3) / 1e9)
+        # algorithmic HBM bytes of a step (the resident path's, with the misses
+        # also written into the pool), from the logged set sizes and misses
+        sb, ab = step_bytes(w, nsel, list(positions[: len(nsel)]))
+        hbm = float(np.mean((sb + ab + miss_bytes)[warm])) / (ms * 1e-3) / 1e9
         return {
             "kq": kq, "ke": ke, "kq_over_k": round(kq / (kq + ke), 4),
             "tokens_per_s": round(w.batch / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
@@ -443,6 +447,7 @@ def _offload_leg(torch, NI, R, nb):
             "miss_fraction": round(float(misses[warm].sum() / sum(n.sum() for n in nsel[1:])), 4),
             "locality_gamma": round(_locality(sels, nsel, blocks), 4),
             "host_link_gbps": round(link, 2), "host_link_frac_of_memcpy": round(link / link_ref, 4),
+            "hbm_gbps": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBPS, 4),
             "cold_step_host_link_gbps": round(float(miss_bytes[0] / (fetch_ms[0] * 1e-3) / 1e9), 2),
             "gather_share_of_step": round(float(fetch_ms[warm].sum() / step_ms[warm].sum()), 4),
         }

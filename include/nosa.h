@@ -9,6 +9,15 @@
  *                              host -> HBM gather of the missing blocks
  *   4. nosa_sparse_decode_attn exact attention over the selected blocks plus
  *                              the current (window) block
+ * and the same steps in fewer launches: nosa_decode_step (2 + 4 for a cache
+ * resident in HBM, one launch; nosa_decode_step_static without a
+ * workspace), nosa_select_update_pool (2 + the table part of 3) and
+ * nosa_sparse_decode_attn_fetch (the gather of 3 + 4) for an offloaded cache,
+ * or 3 split around a side stream (nosa_update_pool, nosa_gather_blocks,
+ * nosa_sparse_decode_attn_pool); per-entry pooling (nosa_pool_keys_entries);
+ * prefill chunks (nosa_sparse_chunk_attn, nosa_select_blocks_shared); the
+ * step before 1 (nosa_split_qkv); and two alternative readings kept for
+ * comparison (nosa_select_blocks_fill, nosa_sparse_decode_attn_bias).
  *
  * Conventions shared by every call
  * --------------------------------

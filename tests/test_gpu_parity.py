@@ -443,11 +443,12 @@ def test_offload_sweep_points(kq, ke, fused):
             _pool_consistent(layer, host, b, h)
 
 
-def test_offload_workload_sampled_units():
-    _banner("offload workload: B=64, 16K context, pool 80, 128 steps (sampled units)")
+@pytest.mark.parametrize("fused_fetch", [True, False], ids=["fused-fetch", "side-stream"])
+def test_offload_workload_sampled_units(fused_fetch):
+    _banner(f"offload workload: B=64, 16K context, pool 80, 128 steps (sampled units), fused fetch {fused_fetch}")
     w = NI.WORKLOADS["offload"]
     K, V, lam, q = NI.layer_inputs(w)
-    rec, layer, host = H.run_offload(w, K, V, lam, q, record_tables=False)
+    rec, layer, host = H.run_offload(w, K, V, lam, q, record_tables=False, fused_fetch=fused_fetch)
     for b, h in ((0, 0), (17, 1), (40, 0), (63, 1)):
         H.check_offload_unit(w, K, V, lam, q, rec, b, h)
         _pool_consistent(layer, host, b, h)
