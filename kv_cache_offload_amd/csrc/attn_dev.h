@@ -414,8 +414,9 @@ __device__ void publish_part_ll(const MergeLds<D, WAVES, GMAX>& L, int G, int ti
   }
 }
 
-// A merge workgroup of a unit: outputs [out_lo, out_lo + n_out) (n_out <=
-// 64*WAVES, one per thread) from the unit's n_part flagged records, polled
+// The final merge of a slice of a unit's outputs, by whichever workgroup
+// does it (a Q worker, or a merge workgroup): outputs [out_lo, out_lo +
+// n_out) (n_out <= 64*WAVES, one per thread) from the unit's n_part flagged records, polled
 // until they carry the launch's flag; per-head weights from one 16-lane
 // group per head (lane = record); normalised and stored.  Splitting a unit's
 // outputs over several such workgroups divides the record bytes each one
