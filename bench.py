@@ -728,10 +728,12 @@ def _stack_leg(torch, NI, R):
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
 
-    def run(fused_update, fused_fetch=False):
+    def run(fused_update, fused_fetch=False, record=False):
         """The decode steps from empty pools (tables cleared, window back at
         the prompt's end; the compressed keys of blocks completed on the way
-        are pooled again, to the same values)."""
+        are pooled again, to the same values).  record: also copy every
+        layer's sets and misses and time its gather (copies that would
+        otherwise sit inside the timed steps)."""
         for L in stack.layers:
             for k in ("block_table", "slot_block", "slot_last_use"):
                 getattr(L, k).fill_(-1)
@@ -749,8 +751,8 @@ def _stack_leg(torch, NI, R):
         for t in range(w.n_steps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(main)
-            stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer, fetch_ev, fused_update,
-                       fused_fetch)
+            stack.step(t, [qd[t] for qd in qs], pos[t], blocks[t], side, on_layer if record else None,
+                       fetch_ev if record else None, fused_update, fused_fetch)
             e1.record(main)
             step_ev.append((e0, e1))
         torch.cuda.synchronize()
@@ -761,7 +763,10 @@ def _stack_leg(torch, NI, R):
     med = lambda ev: float(np.median(np.array([a.elapsed_time(b) for a, b in ev])[1:]))
     ms_two = med(run(False)[1])
     ms_side = med(run(True)[1])
-    fetch_ev, step_ev, (rec_sel, rec_n, rec_miss) = run(True, True)
+    _, step_ev, _ = run(True, True)
+    # the same steps once more, recording each layer's sets, misses and
+    # attention time (not timed as steps)
+    fetch_ev, _, (rec_sel, rec_n, rec_miss) = run(True, True, record=True)
     nL = w.n_layers
     step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
     fetch_ms = np.array([[a.elapsed_time(b) for a, b in fetch_ev[l]] for l in range(nL)]).T   # [t, l]
