@@ -68,6 +68,10 @@ struct StepGeometry {
 // Gamma_e cache words per unit: the count, the e_blk address (two words),
 // then up to kStepMaxK ids
 constexpr int kGeHead = 3;
+// Bytes between two units' arrival tickets: one ticket per 256-byte line, so
+// the units' atomics do not queue on one line (every workgroup of the launch
+// draws one)
+constexpr size_t kArriveStride = 256;
 
 static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int head_dim, int nb, int kq,
                                   int ke) {
@@ -93,7 +97,7 @@ static StepGeometry step_geometry(int batch, int n_q_heads, int n_kv_heads, int 
   const size_t U = g.units;
   const size_t rec = (size_t)kStepGMax * head_dim + 2 * kStepGMax;
   size_t o = 0;
-  g.off_arrive = o; o += align256(U * 8);
+  g.off_arrive = o; o += align256(U * kArriveStride);
   g.off_err = o; o += 256;
   g.off_ge = o; o += align256(U * (kStepMaxK + kGeHead) * 8);
   g.off_score = o; o += align256(U * (size_t)nb * 8);
@@ -174,7 +178,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   const int unit = blockIdx.x % U, j = blockIdx.x / U;
   const bool is_q = j >= nE;
   const int b = unit / n_kv_heads, h = unit % n_kv_heads;
-  uint64_t* arrive = reinterpret_cast<uint64_t*>(ws) + unit;
+  uint64_t* arrive = reinterpret_cast<uint64_t*>(ws + (size_t)unit * kArriveStride);
   int* err = reinterpret_cast<int*>(ws + off_err);
   __shared__ uint32_t s_flag;
   const uint64_t* recs_all = reinterpret_cast<const uint64_t*>(ws + off_part);
