@@ -52,7 +52,7 @@ static ChunkGeometry chunk_geometry(int batch, int n_kv_heads, int head_dim, int
   // splits per unit: about one workgroup per CU in all, at least 2, at most 8
   const size_t s = (256 + g.units - 1) / g.units;
   g.splits = s < 2 ? 2 : (s > 8 ? 8 : s);
-  size_t o = align256(g.units * sizeof(int32_t));           // tickets
+  size_t o = g.units * kTicketBytes;                        // tickets
   g.off_ml = o; o += align256(g.units * g.splits * 16 * 2 * sizeof(float));
   g.off_o = o; o += align256(g.units * g.splits * 16 * (size_t)head_dim * sizeof(float));
   g.total = o;
@@ -63,7 +63,7 @@ size_t attn_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int
   const size_t units = (size_t)batch * n_query * n_kv_heads;
   const size_t G = n_q_heads / n_kv_heads;
   const size_t splits = 2 * attn_splits(k_cap, (int)G);   // both parts of a pool step
-  size_t need = align256(units * sizeof(int32_t)) + align256(units * splits * G * 2 * sizeof(float)) +
+  size_t need = units * kTicketBytes + align256(units * splits * G * 2 * sizeof(float)) +
                 align256(units * splits * G * head_dim * sizeof(float));
   const int NR = chunk_rows((int)G);
   if (n_query > 1 && NR > 0) {
@@ -225,9 +225,9 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(
   wait_stores_done();
   __syncthreads();
   if (tid == 0) {
-    const int t = ticket_take(&ticket[unit]);
+    const int t = ticket_take(&ticket[(size_t)unit * kTicketInts]);
     s_last = (t == (int)gridDim.y - 1);
-    if (s_last) ticket_reset(&ticket[unit]);
+    if (s_last) ticket_reset(&ticket[(size_t)unit * kTicketInts]);
   }
   __syncthreads();
   if (!s_last) return;
@@ -379,9 +379,9 @@ __global__ void __launch_bounds__(64 * kChunkWaves) chunk_attn_kernel(
   wait_stores_done();
   __syncthreads();
   if (tid == 0) {
-    const int t = ticket_take(&ticket[u]);
+    const int t = ticket_take(&ticket[(size_t)u * kTicketInts]);
     s_last = (t == n_split - 1);
-    if (s_last) ticket_reset(&ticket[u]);
+    if (s_last) ticket_reset(&ticket[(size_t)u * kTicketInts]);
   }
   __syncthreads();
   if (!s_last) return;
@@ -462,7 +462,7 @@ static void launch_w(const LaunchAttn& a) {
   const int splits_fetch = (a.k_cap + 2 + WAVES - 1) / WAVES;
   char* ws = (char*)a.ws;
   int32_t* ticket = (int32_t*)ws;
-  float* part_ml = (float*)(ws + align256((size_t)units * sizeof(int32_t)));
+  float* part_ml = (float*)(ws + (size_t)units * kTicketBytes);
   const float scale_log2 = a.scale * 1.4426950408889634f;
   // partial slots are laid out for 2 * splits per unit in every mode
   float* part_o = (float*)((char*)part_ml + align256((size_t)units * 2 * splits * G * 2 * sizeof(float)));

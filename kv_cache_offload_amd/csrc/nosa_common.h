@@ -89,6 +89,11 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void wait_stores_done() { __builtin_amdgcn_s_waitcnt(0); }
+// Workspace tickets (one per unit or row) sit one per 256-byte line, so the
+// atomics of different units do not queue on one line.
+constexpr size_t kTicketBytes = 256;
+constexpr int kTicketInts = (int)(kTicketBytes / sizeof(int));
+
 __device__ __forceinline__ int ticket_take(int* t) {
   return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

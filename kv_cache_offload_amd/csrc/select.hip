@@ -36,7 +36,7 @@ size_t select_ws_bytes(int batch, int n_query, int n_kv_heads, int nb) {
   const size_t rows = (size_t)batch * n_query * n_kv_heads;
   // tickets, scores per row and block, and (chunk-shared selection) 16
   // partial sums of the query heads, up to 128 fp32 dimensions, per unit
-  return align256(rows * sizeof(int32_t)) + align256(rows * (size_t)nb * sizeof(float)) +
+  return rows * kTicketBytes + align256(rows * (size_t)nb * sizeof(float)) +
          align256((size_t)16 * batch * n_kv_heads * 128 * sizeof(float));
 }
 
@@ -130,9 +130,9 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(
     wait_stores_done();
     __syncthreads();
     if (tid == 0) {
-      const int t = ticket_take(&ticket[row]);
+      const int t = ticket_take(&ticket[(size_t)row * kTicketInts]);
       s_last = (t == n_split - 1);
-      if (s_last) ticket_reset(&ticket[row]);
+      if (s_last) ticket_reset(&ticket[(size_t)row * kTicketInts]);
     }
     __syncthreads();
     if (!s_last) return;
@@ -340,7 +340,7 @@ static bool launch_multi(const LaunchSelect& a) {
   int splits = (a.nb + 127) / 128;
   splits = splits < 1 ? 1 : (splits > 32 ? 32 : splits);
   char* ws = (char*)a.ws;
-  float* score = (float*)(ws + align256((size_t)rows * sizeof(int32_t)));
+  float* score = (float*)(ws + (size_t)rows * kTicketBytes);
   const dim3 grid(splits, units, chunks);
   const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* kc = (const uint16_t*)a.k_comp;
@@ -518,8 +518,8 @@ static void launch_shared(const LaunchSelect& a) {
   const int units = a.batch * a.n_kv_heads;
   const size_t rows = (size_t)a.batch * a.n_query * a.n_kv_heads;
   char* ws = (char*)a.ws;
-  float* score = (float*)(ws + align256(rows * sizeof(int32_t)));
-  float* qs = (float*)(ws + align256(rows * sizeof(int32_t)) + align256(rows * (size_t)a.nb * sizeof(float)));
+  float* score = (float*)(ws + (size_t)rows * kTicketBytes);
+  float* qs = (float*)(ws + (size_t)rows * kTicketBytes + align256(rows * (size_t)a.nb * sizeof(float)));
   const uint16_t* q = (const uint16_t*)a.q;
   hipLaunchKernelGGL((qsum_kernel<D>), dim3(kQsumParts, units), dim3(kQsumThreads), 0, a.stream, q, a.n_query,
                      a.n_q_heads, a.n_kv_heads, qs);
@@ -546,7 +546,7 @@ static void launch(const LaunchSelect& a) {
   const int splits = select_splits(rows, a.nb);
   char* ws = (char*)a.ws;
   int32_t* ticket = (int32_t*)ws;
-  float* score = (float*)(ws + align256((size_t)rows * sizeof(int32_t)));
+  float* score = (float*)(ws + (size_t)rows * kTicketBytes);
   const dim3 grid(splits, rows);
   if (a.pool) {
     const LaunchFetch& f = *a.pool;
