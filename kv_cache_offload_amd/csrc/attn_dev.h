@@ -421,10 +421,11 @@ __device__ void publish_part_ll(const MergeLds<D, WAVES, GMAX>& L, int G, int ti
 // group per head (lane = record); normalised and stored.  Splitting a unit's
 // outputs over several such workgroups divides the record bytes each one
 // reads.  The first loads of every word go out before get_flag() (which may
-// itself wait on memory) is called, so its wait overlaps theirs.
+// itself wait on memory) is called, so its wait overlaps theirs.  late_flag
+// is an LDS word the caller cleared before a barrier that precedes the call.
 template <class T, int D, int WAVES, int GMAX, int MAXP, class GetFlag>
 __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int n_part, int out_lo, int n_out,
-                               const uint64_t* recs, GetFlag get_flag, int spin_limit, int* err,
+                               const uint64_t* recs, GetFlag get_flag, int spin_limit, int* err, int* late_flag,
                                typename T::storage* out_g) {
   constexpr int REC = part_record_words<D, GMAX>();
   static_assert(MAXP <= 16, "one 16-lane group per head");
@@ -475,7 +476,9 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
     // a NaN sum (a poisoned record) keeps the weights NaN
     L.a[g_ml][sp_ml] = (den > 0.f || den != den) ? a / den : 0.f;
   }
-  const bool any_late = __syncthreads_or(late ? 1 : 0) != 0;
+  if (late) *late_flag = 1;
+  lds_barrier();   // the weights and the flag
+  const bool any_late = *late_flag != 0;
   if (has) {
     const int g = idx / D;
     float n = 0.f;

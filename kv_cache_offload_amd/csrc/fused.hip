@@ -114,6 +114,18 @@ size_t step_err_offset(int batch, int n_q_heads, int n_kv_heads, int head_dim, i
   return step_geometry(batch, n_q_heads, n_kv_heads, head_dim, nb, kq, ke).off_err;
 }
 
+// Zero, from a vector register the compiler cannot see into.  An atomic on
+// an address it can prove uniform is rewritten into one atomic for the
+// wavefront plus per-lane offsets, which reads the returned value at once:
+// that wait (s_waitcnt vmcnt(0)) also waits for every load the wavefront
+// issued before the atomic.  With this offset added to the address the atomic
+// keeps its plain form and its result is waited for where it is used.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
 // This launch's flag from one arrival ticket of the unit (thread 0 draws it;
 // the caller broadcasts it): launch index + 1, never 0, which is what a word
 // nobody has written holds.
@@ -127,15 +139,6 @@ static size_t step_lds_bytes(int nb) {
   const size_t a = sizeof(MergeLds<D, kStepWaves, kStepGMax>);
   const size_t s = select_lds_bytes(nb);
   return a > s ? a : s;
-}
-
-// A workgroup barrier that orders LDS only.  __syncthreads() also releases
-// global memory, so every wavefront would first wait for its outstanding
-// global stores (the published scores); nothing after the publish needs that.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Attend half blocks first, first + stride, ... < n_half of the list
@@ -191,14 +194,18 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     extern __shared__ __align__(16) unsigned char lds_m[];
     auto& L = *reinterpret_cast<MergeLds<D, kStepWaves, kStepGMax>*>(lds_m);
     const int m = j - W;
-    if (tid == 0) s_flag = draw_flag(arrive, W + nM);
+    __shared__ int s_mlate;
+    if (tid == 0) {
+      s_flag = draw_flag(arrive, W + nM);
+      s_mlate = 0;
+    }
     __syncthreads();
     const uint32_t flag = s_flag;
     const int GD = G * D, per = (GD + nM - 1) / nM;
     const int lo = min(GD, m * per), n_out = min(per, GD - lo);
     typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
     merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs_all + (size_t)unit * W * REC_,
-                                                    [&]() { return flag; }, kSpinLimit, err, out_g);
+                                                    [&]() { return flag; }, kSpinLimit, err, &s_mlate, out_g);
     return;
   }
 
@@ -234,7 +241,9 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   uint64_t w_sc[kScoreRegs];
   auto prologue = [&]() {
     p_raw = pos[b];
-    if (tid == 0) ticket = __hip_atomic_fetch_add(arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (the ticket's result is first needed after the scan)
+    if (tid == 0)
+      ticket = __hip_atomic_fetch_add(arrive + opaque_zero(), (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int r = 0; r < GER; ++r) {
       const int i = tid + r * kStepThreads;
@@ -274,9 +283,13 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     prologue();
   }
   __shared__ int s_stale;                             // a thread found the Gamma_e cache stale
+  __shared__ int s_poison;                            // a score wait of this workgroup expired
+  __shared__ int s_late;                              // a record wait of the final merge expired
   if (tid == 0) {
     s_flag = (uint32_t)((ticket / (uint64_t)(W + nM)) % 0xFFFFFFFFull) + 1u;
     s_stale = 0;
+    s_poison = 0;
+    s_late = 0;
   }
 
   // ---- now the prologue values
@@ -311,7 +324,6 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   const bool cache_ok = s_stale == 0;
   // this launch's flag (drawn by thread 0 in the prologue)
   const uint32_t flag = s_flag;
-  bool timed_out = false;
 
   if (!is_q) {
     // ---------------- E worker: Gamma_e
@@ -393,7 +405,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
         if (ok || it >= kSpinLimit) {
           if (!ok) {
             atomicAdd(err, 1);
-            timed_out = true;
+            s_poison = 1;
           }
           break;
         }
@@ -540,11 +552,12 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
   auto& L = *reinterpret_cast<MergeLds<D, kStepWaves, kStepGMax>*>(lds);
   uint64_t* recs = reinterpret_cast<uint64_t*>(ws + off_part) + (size_t)unit * W * REC;
   float own[2];
-  // the selection arrays in LDS are dead past this barrier (L reuses the
-  // space); a worker whose score wait timed out poisons its partial, so the
-  // unit's outputs come out NaN
-  const bool poison = __syncthreads_or(timed_out ? 1 : 0) != 0;
+  // L reuses the selection arrays' LDS: every read of those came before the
+  // last barrier ahead of the attention.  A worker whose score wait timed
+  // out poisons its partial, so the unit's outputs come out NaN (the flag
+  // was set before several barriers, the merge's own among them).
   merge_waves_keep<D, kStepWaves, kStepGMax>(L, m_run, l_run, o, G, tid, own);
+  const bool poison = s_poison != 0;
   publish_part_ll<D, kStepWaves, kStepGMax>(L, G, tid, own, recs + (size_t)j * REC, flag, poison);
   if (nM == 0 && is_q) {
     // ---------------- the final merge: Q worker qj stores slice qj of the
@@ -555,7 +568,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     lds_barrier();                                    // L's record reads are done
     typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
     merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs, [&]() { return flag; },
-                                                    kSpinLimit, err, out_g);
+                                                    kSpinLimit, err, &s_late, out_g);
   }
 }
 

@@ -237,4 +237,13 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// A workgroup barrier that orders LDS only.  __syncthreads() also releases
+// global memory, so every wavefront would first wait for its outstanding
+// global stores; nothing that follows these barriers needs that.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace nosa
