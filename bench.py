@@ -47,7 +47,7 @@ COLD_FACTOR = 2.0           # bytes touched between two uses of a replica >= 2x 
 # Byte counters of step_kernel on this workload (rocprofv3 --pmc, KiB per dispatch),
 # valid for the kernel sources whose digest is recorded here.  FETCH_SIZE reads half
 # of a plain 256 MiB copy's bytes (factor 2.0); WRITE_SIZE reads all of them (1.0).
-STEP_PMC = {"src_sha256": "027188f493f797792ccdee90a79e8f094669e92d23801cf7acd298dec4d3b1e9", "fetch_kib": 21812.8, "write_kib": 2225.0}
+STEP_PMC = {"src_sha256": "ac7955d96835096cc8489a8d4f41c348b40ec27593dc6d87d9b60a8f6a650808", "fetch_kib": 21799.5, "write_kib": 2225.0}
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 STEP_SOURCES = ("fused.hip", "attn_dev.h", "select_dev.h", "nosa_common.h")
 
