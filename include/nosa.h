@@ -581,6 +581,18 @@ int nosa_decode_step_static(const nosa_dims* dims, const void* q, const int32_t*
 int nosa_step_timeouts(const nosa_dims* dims, int32_t kq, int32_t ke, const void* ws, int32_t* out,
                        void* stream);
 
+/*
+ * nosa_debug_expire_step_waits -- a test hook for the one-launch step's
+ * failure handling, for test suites only.  While on (on != 0), every launch
+ * of nosa_decode_step and nosa_decode_step_static that follows treats the
+ * query-aware workers' score words as not yet written and bounds that wait
+ * at 64 polls, so each of those waits expires: the launch counts them
+ * (nosa_step_timeouts) and writes NaN for every output (with kq > 0; kq = 0
+ * has no such wait), and every kernel still runs to its end.  on = 0 restores normal launches.  Process-wide,
+ * affects launches issued after the call; off by default; returns 0.
+ */
+int nosa_debug_expire_step_waits(int32_t on);
+
 /* Workspace bytes needed by op (NOSA_OP_SELECT, NOSA_OP_ATTN or NOSA_OP_STEP); 0 on bad input. */
 size_t nosa_workspace_size(const nosa_dims* dims, int32_t op, int32_t n_query, int32_t kq,
                            int32_t ke);

@@ -27,7 +27,7 @@ EXPORTS = ("nosa_pool_keys", "nosa_select_blocks", "nosa_fetch_blocks",
            "nosa_sparse_decode_attn_pool", "nosa_sparse_chunk_attn", "nosa_split_qkv",
            "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static",
            "nosa_select_blocks_fill", "nosa_sparse_decode_attn_bias", "nosa_pool_keys_entries",
-           "nosa_select_update_pool", "nosa_sparse_decode_attn_fetch")
+           "nosa_select_update_pool", "nosa_sparse_decode_attn_fetch", "nosa_debug_expire_step_waits")
 
 
 class NosaError(RuntimeError):
@@ -74,6 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nosa_split_qkv.argtypes = [D, P, I32, P, P, P, I32, P, P, P, P]
     lib.nosa_step_timeouts.argtypes = [D, I32, I32, P, P, P]
     lib.nosa_decode_step_static.argtypes = [D, P, P, P, P, I32, I32, P, F, P, P, P, P]
+    lib.nosa_debug_expire_step_waits.argtypes = [I32]
     lib.nosa_workspace_size.restype = SZ
     lib.nosa_status_str.argtypes = [I32]
     lib.nosa_status_str.restype = ctypes.c_char_p
@@ -83,7 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "nosa_decode_step", "nosa_update_pool", "nosa_gather_blocks", "nosa_sparse_decode_attn_pool",
                  "nosa_sparse_chunk_attn", "nosa_split_qkv", "nosa_select_blocks_shared", "nosa_step_timeouts", "nosa_decode_step_static",
                  "nosa_select_blocks_fill", "nosa_sparse_decode_attn_bias", "nosa_pool_keys_entries",
-           "nosa_select_update_pool", "nosa_sparse_decode_attn_fetch"):
+           "nosa_select_update_pool", "nosa_sparse_decode_attn_fetch", "nosa_debug_expire_step_waits"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -298,6 +299,11 @@ def step_timeouts(d: Dims, kq: int, ke: int, ws, out, stream=None) -> None:
     (an int32 device or pinned host tensor)."""
     rc = load().nosa_step_timeouts(ctypes.byref(d), kq, ke, _ptr(ws), _ptr(out), _stream(stream))
     _check("nosa_step_timeouts", rc)
+
+
+def debug_expire_step_waits(on: bool) -> None:
+    """Test hook: while on, the one-launch step's score waits expire (counted, NaN outputs)."""
+    _check("nosa_debug_expire_step_waits", load().nosa_debug_expire_step_waits(1 if on else 0))
 
 
 def decode_step_static(d: Dims, q, pos, k_comp, e_blk, kq: int, ke: int, kv, scale: Optional[float], sel, n_sel,

@@ -161,7 +161,12 @@ __device__ __forceinline__ void attend_halves(const typename T::storage* q_group
   }
 }
 
-template <class T, int D>
+// EXPIRE: the failure-handling test hook (nosa_debug_expire_step_waits): the
+// query-aware workers' score waits compare against a flag no launch uses and
+// give up after 64 polls, so each expires, is counted and poisons the
+// outputs.  A separate instantiation, so the normal kernel carries no trace
+// of it.
+template <class T, int D, bool EXPIRE>
 __global__ void __launch_bounds__(kStepThreads) step_kernel(
     const typename T::storage* __restrict__ q, const int32_t* __restrict__ pos,
     const typename T::storage* __restrict__ k_comp, const float* __restrict__ e_blk,
@@ -169,6 +174,8 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     int ke, float scale_log2, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
     typename T::storage* __restrict__ out, unsigned char* __restrict__ ws, int W, int nQ, int nM,
     size_t off_err, size_t off_ge, size_t off_score, size_t off_part) {
+  constexpr uint32_t poll_xor = EXPIRE ? 0x80000000u : 0u;
+  constexpr int spin_limit = EXPIRE ? 64 : kSpinLimit;
   constexpr int ND = D / 16;
   constexpr int REC = part_record_words<D, kStepGMax>();
   constexpr int GER = (kStepMaxK + kGeHead + kStepThreads - 1) / kStepThreads;   // cache words per thread
@@ -205,7 +212,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     const int lo = min(GD, m * per), n_out = min(per, GD - lo);
     typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
     merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs_all + (size_t)unit * W * REC_,
-                                                    [&]() { return flag; }, kSpinLimit, err, &s_mlate, out_g);
+                                                    [&]() { return flag; }, spin_limit, err, &s_mlate, out_g);
     return;
   }
 
@@ -401,8 +408,9 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
       while (true) {
         bool ok = true;
 #pragma unroll
-        for (int i = 0; i < kScoreRegs; ++i) ok = ok && (tid + i * kStepThreads >= c || ll_ok(w_sc[i], flag));
-        if (ok || it >= kSpinLimit) {
+        for (int i = 0; i < kScoreRegs; ++i)
+          ok = ok && (tid + i * kStepThreads >= c || ll_ok(w_sc[i], flag ^ poll_xor));
+        if (ok || it >= spin_limit) {
           if (!ok) {
             atomicAdd(err, 1);
             s_poison = 1;
@@ -413,7 +421,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
 #pragma unroll
         for (int i = 0; i < kScoreRegs; ++i) {
           const int jj = tid + i * kStepThreads;
-          if (jj < c && !ll_ok(w_sc[i], flag)) w_sc[i] = ll_load(&score_ll[jj]);
+          if (jj < c && !ll_ok(w_sc[i], flag ^ poll_xor)) w_sc[i] = ll_load(&score_ll[jj]);
         }
         ++it;
       }
@@ -568,7 +576,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(
     lds_barrier();                                    // L's record reads are done
     typename T::storage* out_g = out + ((size_t)b * n_q_heads + (size_t)h * G) * D;
     merge_slice_ll<T, D, kStepWaves, kStepGMax, 16>(L, G, tid, W, lo, n_out, recs, [&]() { return flag; },
-                                                    kSpinLimit, err, &s_late, out_g);
+                                                    spin_limit, err, &s_late, out_g);
   }
 }
 
@@ -577,7 +585,8 @@ static void launch(const LaunchStep& a) {
   const StepGeometry g = step_geometry(a.batch, a.n_q_heads, a.n_kv_heads, D, a.nb, a.kq, a.ke);
   const int wgs = g.units * (g.W + g.nM);
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((step_kernel<T, D>), dim3(wgs), dim3(kStepThreads), step_lds_bytes<D>(a.nb), a.stream,
+  auto kernel = a.expire_waits ? step_kernel<T, D, true> : step_kernel<T, D, false>;
+  hipLaunchKernelGGL(kernel, dim3(wgs), dim3(kStepThreads), step_lds_bytes<D>(a.nb), a.stream,
                      (const typename T::storage*)a.q, a.pos, (const typename T::storage*)a.k_comp,
                      a.e_blk, (const typename T::storage*)a.kv, a.n_q_heads, a.n_kv_heads, a.nb,
                      a.kq, a.ke, scale_log2, a.sel, a.n_sel, (typename T::storage*)a.out,

@@ -6,12 +6,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/nosa.h"
 #include "nosa_launch.h"
 
 namespace {
+// nosa_debug_expire_step_waits: process-wide, off unless a test turns it on
+std::atomic<int> g_expire_step_waits{0};
 
 thread_local std::string g_last_error;
 
@@ -488,6 +491,7 @@ int prepare_step(const char* fn, const nosa_dims* dims, const void* q, const int
   a->out = out;
   a->ws = nullptr;
   a->stream = (hipStream_t)stream;
+  a->expire_waits = g_expire_step_waits.load(std::memory_order_relaxed) != 0;
   return NOSA_OK;
 }
 
@@ -556,5 +560,10 @@ const char* nosa_status_str(int32_t status) {
 }
 
 const char* nosa_last_error(void) { return g_last_error.c_str(); }
+
+int nosa_debug_expire_step_waits(int32_t on) {
+  g_expire_step_waits.store(on ? 1 : 0, std::memory_order_relaxed);
+  return NOSA_OK;
+}
 
 }  // extern "C"

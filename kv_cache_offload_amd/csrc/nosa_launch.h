@@ -119,6 +119,9 @@ struct LaunchStep {
   void* out;
   void* ws;
   hipStream_t stream;
+  // failure-handling test hook (nosa_debug_expire_step_waits): the score
+  // waits of this launch expire
+  bool expire_waits;
 };
 
 // Geometry of a one-launch step, the key of the library's static workspace.

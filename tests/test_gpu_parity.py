@@ -1037,6 +1037,45 @@ def test_max_size_context_and_budget():
         H.compare_unit(w, K, V, lam, q, 0, h, H.unit_selections(s1, n1, 0, h), gpu_out=o1)
 
 
+def test_expired_score_waits_are_counted_and_poison_outputs():
+    """Failure handling of the one-launch step, forced from the host (the
+    library's test hook): every query-aware worker's score wait runs to a
+    short bound.  The launch must count the expired waits and write NaN for
+    every output, and every kernel must still finish.  With the hook off the
+    same workspace runs the next step exactly (against the separate calls)
+    and counts nothing more."""
+    _banner("expired score waits (host-forced)")
+    w = NI.scaled(NI.WORKLOADS["layer32k"], batch=2, prompt_len=64 * 40 + 10, n_steps=2)
+    K, V, lam, q = NI.layer_inputs(w)
+    kv, logits, qd, pos = H.device_inputs(w, K, V, lam, q)
+    c0 = int(w.positions()[0]) // 64
+    layers = []
+    for _ in range(2):
+        L = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
+        L.pool_blocks(kv, logits, 0, c0)
+        layers.append(L)
+    fused, ref = layers
+    nb.debug_expire_step_waits(True)
+    try:
+        fused.step_fused(qd[0], kv, pos[0])
+        torch.cuda.synchronize()
+        bad = fused.out.float().cpu().numpy()
+    finally:
+        nb.debug_expire_step_waits(False)
+    n_bad = fused.step_timeouts()
+    assert n_bad > 0
+    assert np.all(np.isnan(bad))
+    fused.step_fused(qd[1], kv, pos[1])
+    ref.step_resident(qd[1], kv, pos[1])
+    torch.cuda.synchronize()
+    assert fused.step_timeouts() == n_bad
+    assert np.array_equal(fused.n_sel.cpu().numpy(), ref.n_sel.cpu().numpy())
+    assert np.array_equal(fused.sel.cpu().numpy(), ref.sel.cpu().numpy())
+    out = fused.out.float().cpu().numpy()
+    assert np.all(np.isfinite(out))
+    assert float(np.max(np.abs(out - ref.out.float().cpu().numpy()))) < 2e-2
+
+
 @pytest.mark.parametrize("batch", [32, 64], ids=["64-units", "128-units"])
 def test_fused_step_many_units(batch):
     """Many (b, h) units: few workgroups per unit (a single E worker scanning
