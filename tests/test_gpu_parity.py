@@ -973,6 +973,45 @@ def test_fused_step_matches_oracle(wname, over):
             H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
 
 
+def _random_config(seed):
+    """A small seeded configuration: head grouping, head dim, dtype, batch,
+    ragged prompt length (never a multiple of 64), budgets, step count."""
+    rng = np.random.default_rng(1000 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4]))
+    L = int(rng.integers(65, 6000))
+    L += 1 if L % 64 == 0 else 0
+    kq, ke = int(rng.integers(0, 25)), int(rng.integers(0, 25))
+    if kq + ke == 0:
+        kq = 1
+    return dict(batch=int(rng.integers(1, 6)), n_q_heads=G * hkv, n_kv_heads=hkv,
+                head_dim=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f32"])), prompt_len=L,
+                n_steps=int(rng.integers(3, 41)), kq=kq, ke=ke)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_configs_match_oracle(seed):
+    """Seeded random shapes through both resident paths (the one-launch step
+    and the separate calls), every unit against the oracle: head groupings 1,
+    2, 4 and 8, head dims 64 and 128, both dtypes, budgets from 0 to 24,
+    prompts up to 6000 tokens and up to 40 steps (so some cross block ends)."""
+    over = _random_config(seed)
+    _banner(f"random config {seed}: {over}")
+    w = NI.scaled(NI.WORKLOADS["layer32k"], **over)
+    K, V, lam, q = NI.layer_inputs(w)
+    s1, n1, o1, layer = H.run_resident(w, K, V, lam, q, fused=True)
+    assert layer.step_timeouts() == 0
+    s2, n2, o2, _ = H.run_resident(w, K, V, lam, q, fused=False)
+    for a, b in zip(n1, n2):
+        assert np.array_equal(a, b)
+    for a, b in zip(s1, s2):
+        assert np.array_equal(a, b)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s1, n1, b, h), gpu_out=o1)
+            H.compare_unit(w, K, V, lam, q, b, h, H.unit_selections(s2, n2, b, h), gpu_out=o2)
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["one-launch", "separate-calls"])
 def test_exact_ties_break_by_block_id(fused):
     """Blocks whose keys and eviction logits repeat one of three patterns
