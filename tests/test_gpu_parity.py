@@ -401,6 +401,45 @@ def test_offload_ragged_positions(mode):
             assert not kc[b, h, 4 * c_end:].any() and not eb[b, h, c_end:].any()
 
 
+def _random_offload_config(seed):
+    """A small seeded offload configuration: heads, dtype, budgets, a pool a
+    little larger than the selection, ragged per-entry lags, a step form and
+    sometimes a cold restart."""
+    rng = np.random.default_rng(2000 + seed)
+    kq, ke = int(rng.integers(0, 13)), int(rng.integers(0, 13))
+    if kq + ke == 0:
+        ke = 1
+    G, hkv, B = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2])), int(rng.integers(1, 5))
+    n_steps = int(rng.integers(20, 121))
+    L = int(rng.integers(65 + 64, 4000))
+    L += 1 if L % 64 == 0 else 0
+    over = dict(batch=B, n_q_heads=G * hkv, n_kv_heads=hkv, head_dim=int(rng.choice([64, 128])),
+                dtype=str(rng.choice(["bf16", "f32"])), prompt_len=L, n_steps=n_steps, kq=kq, ke=ke,
+                pool_slots=kq + ke + int(rng.integers(1, 21)))
+    offsets = [int(x) for x in rng.integers(0, 64, B)]
+    mode = str(rng.choice(list(OFFLOAD_MODES)))
+    reset_at = int(rng.integers(1, n_steps)) if rng.random() < 0.3 else None
+    return over, offsets, mode, reset_at
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_offload_configs_match_oracle(seed):
+    """Seeded random offload runs (every step form, ragged lags, pools from
+    one to twenty blocks above the selection, both dtypes, head groupings
+    1-8, sometimes a cold restart): every unit's sets, misses, slots, tables
+    and outputs against the oracle's block pool, and every resident pool
+    block byte-identical to its host block."""
+    over, offsets, mode, reset_at = _random_offload_config(seed)
+    _banner(f"random offload {seed}: {over} lags {offsets} {mode} reset {reset_at}")
+    w = _w("offload", **over)
+    K, V, lam, q = NI.layer_inputs(w)
+    rec, layer, host = H.run_offload(w, K, V, lam, q, offsets=offsets, reset_at=reset_at, **OFFLOAD_MODES[mode])
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            H.check_offload_unit(w, K, V, lam, q, rec, b, h, pool_reset_at=reset_at)
+            _pool_consistent(layer, host, b, h)
+
+
 @pytest.mark.parametrize("reset_at", [30, 34], ids=["mid-block", "on-a-completion"])
 def test_offload_cold_restart_mid_run(reset_at):
     """The pool tables cleared before step `reset_at` (every resident block
