@@ -852,6 +852,79 @@ def _chunk_attention_case(w, K, V, lam, q_rows, pos_rows, kv, layer):
     return err
 
 
+def _random_prefill_config(seed):
+    """A small seeded prefill configuration: heads, dtype, a ragged prompt,
+    the number of query rows and the budgets."""
+    rng = np.random.default_rng(3000 + seed)
+    G, hkv = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2]))
+    T = int(rng.integers(200, 20000))
+    T += 1 if T % 64 == 0 else 0
+    kq, ke = int(rng.integers(0, 25)), int(rng.integers(0, 25))
+    if kq + ke == 0:
+        kq = 1
+    over = dict(batch=int(rng.integers(1, 4)), n_q_heads=G * hkv, n_kv_heads=hkv,
+                head_dim=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f32"])), prompt_len=T,
+                n_steps=1, kq=kq, ke=ke, prefill=True)
+    return over, int(rng.integers(1, 41))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_prefill_configs_match_oracle(seed):
+    """Seeded random prefill chunks: query rows at scattered positions of a
+    ragged prompt (a few out of range on either side), selected by
+    nosa_select_blocks (the row-chunk MFMA scan from 8 rows on, bf16) and
+    attended by nosa_sparse_chunk_attn (packed rows for bf16 with 4 or 8
+    heads per KV head, one row per unit otherwise); every row's set against
+    the oracle's top-k and its output against the oracle's attention over it."""
+    over, n_q = _random_prefill_config(seed)
+    _banner(f"random prefill {seed}: {over}, {n_q} rows")
+    w = _w("layer32k", **over)
+    T, bf16, G, k_cap = w.prompt_len, w.dtype == "bf16", w.group, w.kq + w.ke
+    K, V, lam, _ = NI.layer_inputs(w)
+    kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
+    layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, w.kq, w.ke)
+    layer.pool_blocks(kv, logits, 0, T // 64)
+    rng = np.random.default_rng(4000 + seed)
+    qn = rng.standard_normal((w.batch, n_q, w.n_q_heads, w.head_dim)).astype(np.float32)
+    qn = NI.round_to_bf16(qn) if bf16 else qn
+    posn = rng.integers(0, T, size=(w.batch, n_q)).astype(np.int32)
+    odd = rng.random((w.batch, n_q))
+    posn[odd < 0.08] = -1
+    posn[odd > 0.94] = 64 * w.n_blocks + 3
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    qd = torch.from_numpy(qn).cuda().to(tdt)
+    posd = torch.from_numpy(posn).cuda()
+    sel = torch.full((w.batch, n_q, w.n_kv_heads, k_cap), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((w.batch, n_q, w.n_kv_heads), -7, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(nb.workspace_size(layer.dims, nb.OP_SELECT, n_q, w.kq, w.ke), dtype=torch.uint8, device="cuda")
+    nb.select_blocks(layer.dims, qd, n_q, posd, layer.k_comp, layer.e_blk, w.kq, w.ke, sel, n_sel, ws)
+    out = torch.full((w.batch, n_q, w.n_q_heads, w.head_dim), 3.0, dtype=tdt, device="cuda")
+    wsa = torch.zeros(nb.workspace_size(layer.dims, nb.OP_ATTN, n_q, k_cap, 0), dtype=torch.uint8, device="cuda")
+    nb.sparse_chunk_attn(layer.dims, qd, n_q, kv, sel, n_sel, k_cap, posd, None, out, wsa)
+    sel, n_sel, out = sel.cpu().numpy(), n_sel.cpu().numpy(), out.float().cpu().numpy()
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            kbar = O.subblock_key_means(K[b, h], bf16=bf16)
+            E = O.block_eviction_scores(O.subblock_logit_means(lam[b, h]))
+            for r in range(n_q):
+                p = int(posn[b, r])
+                rows = out[b, r, h * G:(h + 1) * G]
+                got = [int(x) for x in sel[b, r, h, : n_sel[b, r, h]]]
+                assert np.all(sel[b, r, h, n_sel[b, r, h]:] == -1), (b, r, h)
+                if not 0 <= p < 64 * w.n_blocks:
+                    assert got == [] and np.all(rows == 0.0), (b, r, h, p)
+                    continue
+                c = p // 64
+                s_q = O.query_block_scores(qn[b, r, h * G:(h + 1) * G], kbar, c)
+                _, _, S = O.select_blocks(s_q, E, c, w.kq, w.ke)
+                if got != S:
+                    assert H.selection_ok(got, s_q, E, c, w.kq, w.ke), (b, r, h, p, got, S)
+                ref = O.round_output(O.sparse_attention(qn[b, r, h * G:(h + 1) * G], K[b, h], V[b, h], got, p),
+                                     bf16=bf16)
+                e = float(np.max(np.abs(rows - ref)))
+                assert e <= H.ATOL[w.dtype], (b, r, h, p, e)
+
+
 def test_chunk_attention_small():
     """Ragged prompt, two batch entries, 21 rows at scattered positions (five
     out of range, four of them a whole packed group), G = 4, D = 64."""
@@ -944,8 +1017,25 @@ def test_split_qkv_matches_oracle(name, dtype, D, Hq, Hkv, d_e, B, n_tok, contig
     against the oracle's Eq. 4 in float64.  Chunks of 16 or more tokens take
     the 16-tokens-per-workgroup path (ragged last group included)."""
     _banner(f"split qkv {name}")
+    _split_qkv_case(dtype, D, Hq, Hkv, d_e, B, n_tok, contig, 21)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_split_qkv_matches_oracle(seed):
+    """Seeded random QKV splits: head groupings 1-8, 1 to 4 KV heads, both
+    head dims and dtypes, eviction hidden sizes 1 to 300, 1 to 100 tokens at
+    scattered or consecutive positions."""
+    rng = np.random.default_rng(5000 + seed)
+    G, Hkv, D = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 4])), int(rng.choice([64, 128]))
+    case = (str(rng.choice(["bf16", "f32"])), D, G * Hkv, Hkv, int(rng.integers(1, 301)), int(rng.integers(1, 5)),
+            int(rng.integers(1, 101)), bool(rng.random() < 0.4))
+    _banner(f"random split qkv {seed}: {case}")
+    _split_qkv_case(*case, 6000 + seed)
+
+
+def _split_qkv_case(dtype, D, Hq, Hkv, d_e, B, n_tok, contig, seed):
     NB = 12
-    rng = np.random.default_rng(21)
+    rng = np.random.default_rng(seed)
     row = (Hq + 2 * Hkv) * D
     qkv = rng.standard_normal((B, n_tok, row)).astype(np.float32)
     if dtype == "bf16":
