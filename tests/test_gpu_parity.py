@@ -715,13 +715,40 @@ def test_select_shared_matches_oracle(name, over, n_q, kq, ke, starts):
     to every row, against the oracle; then each row's exact attention over it
     plus the row's own window."""
     _banner(f"chunk-shared selection {name}")
-    T = 64 * 640 + 11
+    _shared_case(64 * 640 + 11, over, n_q, kq, ke, starts, 23)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shared_selection_matches_oracle(seed):
+    """Seeded random chunk-shared selections: head groupings 1-8, both head
+    dims, 1 to 64 rows inside one block at a random offset of a ragged
+    prompt, random budgets; the shared set against the oracle and every row's
+    attention over it."""
+    rng = np.random.default_rng(7000 + seed)
+    G, hkv = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2]))
+    T = int(rng.integers(300, 20000))
+    T += 1 if T % 64 == 0 else 0
+    kq, ke = int(rng.integers(0, 25)), int(rng.integers(0, 25))
+    if kq + ke == 0:
+        kq = 1
+    n_q = int(rng.integers(1, 65))
+    starts = []
+    for _ in range(2):
+        blk = int(rng.integers(1, T // 64))         # a block whose rows all lie inside the prompt
+        lo = int(rng.integers(0, 64 - min(n_q, 64) + 1))
+        starts.append(64 * blk + lo)
+    over = dict(n_q_heads=G * hkv, n_kv_heads=hkv, head_dim=int(rng.choice([64, 128])))
+    _banner(f"random chunk-shared selection {seed}: T {T} {over} rows {n_q} kq {kq} ke {ke} starts {starts}")
+    _shared_case(T, over, n_q, kq, ke, tuple(starts), 8000 + seed)
+
+
+def _shared_case(T, over, n_q, kq, ke, starts, seed):
     w = _w("layer32k", batch=2, prompt_len=T, n_steps=1, kq=kq, ke=ke, prefill=True, **over)
     K, V, lam, _ = NI.layer_inputs(w)
     kv, logits, _, _ = H.device_inputs(w, K, V, lam, np.zeros((1, 1, 1, 1), np.float32))
     layer = R.DecodeLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_blocks, w.dtype, kq, ke)
     layer.pool_blocks(kv, logits, 0, T // 64)
-    rng = np.random.default_rng(23)
+    rng = np.random.default_rng(seed)
     qn = NI.round_to_bf16(rng.standard_normal((w.batch, n_q, w.n_q_heads, w.head_dim)).astype(np.float32))
     posn = np.stack([np.arange(n_q) + s for s in starts]).astype(np.int32)   # rows inside one block
     assert np.all(posn // 64 == posn[:, :1] // 64) and posn.max() < T
