@@ -361,12 +361,16 @@ class OffloadStack:
         (nosa_sparse_decode_attn_fetch) on the compute stream, after the
         one-launch selection and update; the side stream is not used and
         fetch_events[l] gets the pair around that attention."""
-        main = torch.cuda.current_stream()
         ragged = np.ndim(block) > 0 or np.ndim(self.block) > 0
+        B = self.layers[0].B
+        cur = np.broadcast_to(np.asarray(block, dtype=np.int64), (B,)).copy()
+        prev = np.broadcast_to(np.asarray(self.block, dtype=np.int64), (B,))
+        if np.any(cur < prev) or np.any(cur > prev + 1):
+            # one position per step: a window moves on by at most one block,
+            # and the block it leaves is the only one to pool and insert
+            raise ValueError(f"window blocks {cur.tolist()} after {prev.tolist()}: each must stay or move on by one")
+        main = torch.cuda.current_stream()
         if ragged:
-            B = self.layers[0].B
-            cur = np.broadcast_to(np.asarray(block, dtype=np.int64), (B,)).copy()
-            prev = np.broadcast_to(np.asarray(self.block, dtype=np.int64), (B,))
             moved = cur > prev
             entry_done = torch.from_numpy(np.where(moved, prev, -1).astype(np.int32)).to(self.layers[0].dev)
         else:
