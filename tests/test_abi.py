@@ -270,6 +270,19 @@ def test_step_timeouts_checks(lib):
     assert e.value.code == nb.ERR_ARG
 
 
+def test_expire_hook_toggles_and_step_checks_still_apply(lib):
+    # the failure-handling test hook only flips a flag; the step's argument
+    # checks run as before while it is on, and it is off again afterwards
+    assert lib.nosa_debug_expire_step_waits(1) == nb.OK
+    try:
+        with pytest.raises(nb.NosaError) as e:
+            nb.decode_step(_d(), FAKE, FAKE, FAKE, FAKE, -1, 48, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                           stream=0)
+        assert e.value.code == nb.ERR_ARG
+    finally:
+        assert lib.nosa_debug_expire_step_waits(0) == nb.OK
+
+
 def test_static_step_rejects_a_workspace_above_its_size(lib):
     # 2048 units x 4096 blocks of scores alone need 64 MiB: more than the
     # static workspace holds; rejected before anything touches a device
