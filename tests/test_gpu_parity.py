@@ -217,16 +217,30 @@ def test_attention_dense_equivalence():
     assert float((out[0] - ref.float()).abs().max()) <= 2e-2
 
 
-def test_attention_repeats_are_bit_identical():
-    _banner("attention determinism across repeats")
+@pytest.mark.parametrize("fused", [False, True], ids=["separate-calls", "one-launch"])
+def test_attention_repeats_are_bit_identical(fused):
+    """The same steps run twice give bit-identical sets and outputs; for the
+    one-launch step also the same step launched again and again on one
+    workspace (each launch with its own flag, the Gamma_e cache reused): the
+    final merge combines the partial records in a fixed order whatever order
+    the workgroups finish in."""
+    _banner(f"determinism across repeats, fused={fused}")
     w = _w("layer32k", batch=4, prompt_len=64 * 100 + 20, n_steps=3)
     K, V, lam, q = NI.layer_inputs(w)
-    s1, n1, o1, _ = H.run_resident(w, K, V, lam, q)
-    s2, n2, o2, _ = H.run_resident(w, K, V, lam, q)
+    s1, n1, o1, _ = H.run_resident(w, K, V, lam, q, fused=fused)
+    s2, n2, o2, layer = H.run_resident(w, K, V, lam, q, fused=fused)
     for a, b in zip(s1, s2):
         assert np.array_equal(a, b)
     for a, b in zip(o1, o2):
         assert np.array_equal(a, b)
+    if fused:
+        kv, _, qd, pos = H.device_inputs(w, K, V, lam, q)
+        for _ in range(8):
+            layer.step_fused(qd[1], kv, pos[1])
+            torch.cuda.synchronize()
+            assert np.array_equal(layer.sel.cpu().numpy(), s1[1])
+            assert np.array_equal(layer.out.float().cpu().numpy(), o1[1])
+        assert layer.step_timeouts() == 0
 
 
 def test_determinism_across_split_counts_and_launch_orders():
