@@ -47,7 +47,7 @@ COLD_FACTOR = 2.0           # bytes touched between two uses of a replica >= 2x 
 # Byte counters of step_kernel on this workload (rocprofv3 --pmc, KiB per dispatch),
 # valid for the kernel sources whose digest is recorded here.  FETCH_SIZE reads half
 # of a plain 256 MiB copy's bytes (factor 2.0); WRITE_SIZE reads all of them (1.0).
-STEP_PMC = {"src_sha256": "17a6b2d46954e89fb53fce2a59c1f6deac3713d33f0fa70e39f9d0253f4a6152", "fetch_kib": 21800.1, "write_kib": 2225.0}
+STEP_PMC = {"src_sha256": "01c1c2e8f9949ad49d0d13ee72c381ed529a441d32ec3cc326514a3c86341301", "fetch_kib": 21800.1, "write_kib": 2225.0}
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 STEP_SOURCES = ("fused.hip", "attn_dev.h", "select_dev.h", "nosa_common.h")
 

@@ -100,12 +100,6 @@ __device__ __forceinline__ int ticket_take(int* t) {
 __device__ __forceinline__ void ticket_reset(int* t) {
   __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_coherent_i(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int load_coherent_i(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Flagged words: a 32-bit payload and a 32-bit launch flag in one 8-byte
 // word, written and read with single 8-byte coherent accesses (which are
@@ -124,21 +118,6 @@ __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
 }
 __device__ __forceinline__ bool ll_ok(uint64_t w, uint32_t flag) { return (uint32_t)(w >> 32) == flag; }
 __device__ __forceinline__ float ll_float(uint64_t w) { return __uint_as_float((uint32_t)w); }
-__device__ __forceinline__ uint64_t ll_word(float v, uint32_t flag) {
-  return ((uint64_t)flag << 32) | __float_as_uint(v);
-}
-// Poll one flagged word (first load already issued) for at most `limit`
-// rounds; a timeout is counted in *err and the stale payload returned.
-__device__ __forceinline__ uint64_t ll_wait(const uint64_t* p, uint64_t w, uint32_t flag, int limit, int* err) {
-  int it = 0;
-  while (!ll_ok(w, flag) && it < limit) {
-    __builtin_amdgcn_s_sleep(1);
-    w = ll_load(p);
-    ++it;
-  }
-  if (!ll_ok(w, flag)) atomicAdd(err, 1);
-  return w;
-}
 
 // ---------------------------------------------------------------------------
 // KV block format: MFMA fragment order.
