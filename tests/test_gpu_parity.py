@@ -243,6 +243,48 @@ def test_attention_repeats_are_bit_identical(fused):
         assert layer.step_timeouts() == 0
 
 
+def test_fused_step_under_concurrent_load():
+    """The one-launch step while another stream keeps the device busy with
+    large products: the step's workgroups then start as the other kernels'
+    workgroups leave, not all at once.  Producers never wait, and every
+    waiter waits on workgroups of its launch that have started before it or
+    are running beside it, so the steps must give the results of an idle
+    device bit for bit, with no wait expired."""
+    _banner("one-launch step under concurrent load")
+    w = _w("layer32k", batch=4, prompt_len=64 * 100 + 20, n_steps=3)
+    K, V, lam, q = NI.layer_inputs(w)
+    s_ref, _, o_ref, layer = H.run_resident(w, K, V, lam, q, fused=True)
+    kv, _, qd, pos = H.device_inputs(w, K, V, lam, q)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.randn(4096, 4096, device="cuda", generator=gen)
+    b = torch.randn(4096, 4096, device="cuda", generator=gen)
+    side, main = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    sels, outs = [], []
+    overlapped = 0
+    for _ in range(4):
+        side_done = torch.cuda.Event()
+        with torch.cuda.stream(side):
+            for _ in range(6):
+                a = (a @ b) * (1.0 / 64.0)
+            side_done.record(side)
+        with torch.cuda.stream(main):
+            for t in range(w.n_steps):
+                layer.step_fused(qd[t], kv, pos[t], main)
+                sels.append(layer.sel.clone())
+                outs.append(layer.out.clone())
+        main.synchronize()
+        overlapped += not side_done.query()   # the steps ended while the products still ran
+    torch.cuda.synchronize()
+    assert overlapped > 0, "the steps never ran beside the products"
+    assert torch.isfinite(a).all()
+    for i, (s, o) in enumerate(zip(sels, outs)):
+        t = i % w.n_steps
+        assert np.array_equal(s.cpu().numpy(), s_ref[t]), f"selection differs under load, step {t}"
+        assert np.array_equal(o.float().cpu().numpy(), o_ref[t]), f"output differs under load, step {t}"
+    assert layer.step_timeouts() == 0
+
+
 def test_determinism_across_split_counts_and_launch_orders():
     """The same step computed with other work decompositions and launch
     orders: the selected sets must be identical and the outputs agree within
