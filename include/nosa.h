@@ -559,6 +559,11 @@ int nosa_decode_step(const nosa_dims* dims, const void* q, const int32_t* pos, c
  * nosa_decode_step.  A geometry whose workspace (nosa_workspace_size with
  * NOSA_OP_STEP) exceeds 16 MiB is rejected with -4.  The call allocates and
  * frees nothing; the first call on a device looks up the array's address.
+ * Under graph capture the geometry check (and the clear it may launch) runs
+ * when a call is captured, not when the graph is replayed: make one call of
+ * the geometry before capturing, so that the graph holds the step launches
+ * only, and after calls of another geometry on the device make one call of
+ * the graph's geometry outside the graph before replaying it.
  */
 int nosa_decode_step_static(const nosa_dims* dims, const void* q, const int32_t* pos, const void* k_comp,
                             const float* e_blk, int32_t kq, int32_t ke, const void* kv, float scale,

@@ -89,3 +89,39 @@ def test_static_step_matches_workspace_step():
     L = big["layer"]
     nb.step_timeouts(L.dims, L.kq, L.ke, None, out)
     assert int(out.item()) == 0
+
+
+def test_static_step_replayed_from_a_graph():
+    """Callers under graph capture: three static steps captured in one graph
+    (their geometry's first call made before the capture, so the graph holds
+    the step launches only) and replayed four times, with buffer fills and an
+    eager static step of the same geometry between the replays: every replay
+    gives the eager calls' selections and outputs bit for bit, and no wait
+    expires."""
+    case = _layer(NI.scaled(NI.WORKLOADS["layer32k"], batch=4, prompt_len=64 * 150 + 20, n_steps=3))
+    w, L = case["w"], case["layer"]
+    eager = [_both(case, t)[1] for t in range(w.n_steps)]
+    bufs = [(torch.empty_like(L.sel), torch.empty_like(L.n_sel), torch.empty_like(L.out)) for _ in range(w.n_steps)]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for t, (sel, n_sel, out) in enumerate(bufs):
+            nb.decode_step_static(L.dims, case["qd"][t], case["pos"][t], L.k_comp, L.e_blk, w.kq, w.ke, case["kv"],
+                                  L.scale, sel, n_sel, out)
+    for rep in range(4):
+        print(f"[case] static step graph replay {rep}", flush=True)
+        for sel, n_sel, out in bufs:
+            sel.fill_(-7)
+            n_sel.fill_(-7)
+            out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for t, (sel, n_sel, out) in enumerate(bufs):
+            s0, n0, o0 = eager[t]
+            assert torch.equal(n_sel, n0) and torch.equal(sel, s0), f"replay {rep}, step {t}: selection"
+            assert torch.equal(out.float(), o0), f"replay {rep}, step {t}: output"
+        _both(case, rep % w.n_steps)      # an eager static step between the replays
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nb.step_timeouts(L.dims, L.kq, L.ke, None, out)
+    assert int(out.item()) == 0
