@@ -24,6 +24,12 @@ __device__ __forceinline__ int tile_token<F32>(int t, int r) {
 template <class T, int D>
 struct Frags;
 
+template <bool STREAM>
+__device__ __forceinline__ uint4 ld16_any(const void* p) {
+  if constexpr (STREAM) return ld16_stream(p);
+  else return ld16(p);
+}
+
 // bf16: K operand 4 tiles x D/32 k-steps, V operand 2 halves x D/16 d-tiles
 template <int D>
 struct Frags<Bf16, D> {
@@ -67,7 +73,9 @@ __device__ __forceinline__ void load_q(Frags<T, D>& f, const typename T::storage
 // Operands of NTL consecutive 16-token tiles t0 .. t0+NTL-1 of one block
 // (NTL = 4: the whole block; NTL = 2: one 32-token half, t0 = 0 or 2): fully
 // contiguous 1 KiB wavefront loads (see the block format in nosa_common.h).
-template <class T, int D, int NTL>
+// STREAM: non-temporal loads, for blocks no other wavefront of the launch
+// reads.
+template <class T, int D, int NTL, bool STREAM = false>
 __device__ __forceinline__ void load_tiles(Frags<T, D>& f, const typename T::storage* blk, int t0, int lane) {
   constexpr int EPC = T::kPer16B;
   constexpr int NK = Frags<T, D>::NK, ND = Frags<T, D>::ND;
@@ -76,18 +84,18 @@ __device__ __forceinline__ void load_tiles(Frags<T, D>& f, const typename T::sto
 #pragma unroll
   for (int t = 0; t < NTL; ++t)
 #pragma unroll
-    for (int s = 0; s < NK; ++s) f.k[t][s] = ld16(kp + (size_t)((t0 + t) * NK + s) * 64 * EPC);
+    for (int s = 0; s < NK; ++s) f.k[t][s] = ld16_any<STREAM>(kp + (size_t)((t0 + t) * NK + s) * 64 * EPC);
   if constexpr (sizeof(typename T::storage) == 2) {
     // V fragments come in 32-token halves
 #pragma unroll
     for (int h = 0; h < NTL / 2; ++h)
 #pragma unroll
-      for (int u = 0; u < ND; ++u) f.v[h][u] = ld16(vp + (size_t)((t0 / 2 + h) * ND + u) * 64 * EPC);
+      for (int u = 0; u < ND; ++u) f.v[h][u] = ld16_any<STREAM>(vp + (size_t)((t0 / 2 + h) * ND + u) * 64 * EPC);
   } else {
 #pragma unroll
     for (int t = 0; t < NTL; ++t)
 #pragma unroll
-      for (int u = 0; u < ND; ++u) f.v[t][u] = ld16(vp + (size_t)((t0 + t) * ND + u) * 64 * EPC);
+      for (int u = 0; u < ND; ++u) f.v[t][u] = ld16_any<STREAM>(vp + (size_t)((t0 + t) * ND + u) * 64 * EPC);
   }
 }
 
@@ -225,13 +233,13 @@ __device__ __forceinline__ void attend_frags(const Frags<T, D>& f, int t0, int l
   block_pv<T, D, NTL>(f, pw, o);
 }
 
-template <class T, int D, int NTL>
+template <class T, int D, int NTL, bool STREAM = false>
 __device__ __forceinline__ void attend_tiles(const typename T::storage* q_group, int G,
                                              const typename T::storage* blk, int t0, int len,
                                              float scale_log2, int lane, float& m_out,
                                              float& l_out, f32x4 (&o)[D / 16], const float* bias_blk = nullptr) {
   Frags<T, D> f;
-  load_tiles<T, D, NTL>(f, blk, t0, lane);
+  load_tiles<T, D, NTL, STREAM>(f, blk, t0, lane);
   load_q<T, D>(f, q_group, G, lane);
   attend_frags<T, D, NTL>(f, t0, len, scale_log2, lane, m_out, l_out, o, bias_blk);
 }

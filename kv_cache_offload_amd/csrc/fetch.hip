@@ -43,7 +43,8 @@ __global__ void __launch_bounds__(64) pool_update_kernel(
 }
 
 // One workgroup per (miss entry, unit); entry k_cap is the inserted block.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // a native vector stays in registers
+// The copy goes through u32x4 (nosa_common.h): a native vector stays in
+// registers.
 
 __global__ void __launch_bounds__(kGatherThreads) gather_kernel(
     const uint4* __restrict__ host_kv, uint4* __restrict__ pool, const uint4* __restrict__ insert_src,

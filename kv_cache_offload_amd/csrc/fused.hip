@@ -143,7 +143,11 @@ static size_t step_lds_bytes(int nb) {
 
 // Attend half blocks first, first + stride, ... < n_half of the list
 // (entry e: half e & 1 of block blk_of(e >> 1), len_of(e >> 1) valid tokens),
-// folding them into the wavefront's running partial.
+// folding them into the wavefront's running partial.  Each half is read by
+// one wavefront once per launch, with non-temporal loads: in a decode over
+// many layers a block is read again only after the caches have turned over,
+// and on cold caches the step runs faster with the hint; a warm repeat of one
+// layer's step loses the blocks' cache hits.
 template <class T, int D, class BlkOf, class LenOf>
 __device__ __forceinline__ void attend_halves(const typename T::storage* q_group, int G,
                                               const typename T::storage* unit_kv, int nb, int first, int stride,
@@ -155,7 +159,7 @@ __device__ __forceinline__ void attend_halves(const typename T::storage* q_group
     if (blk < 0 || blk >= nb) continue;
     float mb, lb;
     f32x4 ob[D / 16];
-    attend_tiles<T, D, 2>(q_group, G, unit_kv + (size_t)blk * blk_elems, 2 * (e & 1), len_of(e >> 1),
+    attend_tiles<T, D, 2, true>(q_group, G, unit_kv + (size_t)blk * blk_elems, 2 * (e & 1), len_of(e >> 1),
                           scale_log2, lane, mb, lb, ob);
     combine_partial<D / 16>(m_run, l_run, o, mb, lb, ob);
   }

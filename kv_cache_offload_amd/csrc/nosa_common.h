@@ -158,6 +158,14 @@ __device__ __forceinline__ int key_chunk_offset(int tok, int ch, int D) {
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// The same load with the non-temporal hint, for data a launch reads once and
+// the next launch is unlikely to find cached (the KV blocks of a decode
+// step): the lines are not kept in the caches at the expense of others.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Cross-lane moves through DPP (a VALU modifier; no LDS round trip).
 // 0xB1 = swap with lane^1, 0x4E = lane^2, 0x141 = mirror inside 8 lanes,
