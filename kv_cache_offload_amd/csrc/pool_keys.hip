@@ -47,10 +47,11 @@ __global__ void __launch_bounds__((64 * pool_waves<T, D>())) pool_keys_kernel(
   }
   const typename T::storage* keys = kv + unit * kv_unit_stride + (int64_t)jb * kv_block_stride;
 
-  // stage the keys: fragment f, lane l -> chunk 64 f + l (contiguous loads)
+  // stage the keys: fragment f, lane l -> chunk 64 f + l (contiguous loads,
+  // non-temporal: every key is read once)
   uint4* sk = s_keys[wave];
 #pragma unroll
-  for (int f = 0; f < FRAGS; ++f) sk[64 * f + lane] = ld16(keys + (size_t)(64 * f + lane) * EPC);
+  for (int f = 0; f < FRAGS; ++f) sk[64 * f + lane] = ld16_stream(keys + (size_t)(64 * f + lane) * EPC);
   // logits of the block: lane i < 64 reads logit i; sub-block means by lanes
   // of chunk 0 below (read back through a wavefront shuffle of the 64 values)
   const float* lg = logits + ((size_t)unit * nb + jb) * kBlock;
