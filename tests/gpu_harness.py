@@ -79,13 +79,14 @@ def unit_selections(S_rows, N_rows, b, h) -> List[List[int]]:
     return [list(S[b, h, :N[b, h]]) for S, N in zip(S_rows, N_rows)]
 
 
-def oracle_scores(w: NI.Workload, K, V, lam, q, b, h, positions=None):
-    """Oracle per-step selection data for unit (b, h): s_q, E, own selections."""
+def oracle_scores(w: NI.Workload, K, V, lam, q, b, h, positions=None, pool_slots=None, pool_reset_at=None):
+    """Oracle per-step selection data for unit (b, h): s_q, E, own selections
+    (and, with pool_slots, the pool replay of those selections)."""
     G = w.group
     qrows = q[:, b, h * G:(h + 1) * G]
     positions = w.positions() if positions is None else positions
     tr = O.decode_unit(K[b, h], V[b, h], lam[b, h], qrows, positions[: q.shape[0]], w.kq, w.ke,
-                       bf16=(w.dtype == "bf16"), attend=False)
+                       bf16=(w.dtype == "bf16"), attend=False, pool_slots=pool_slots, pool_reset_at=pool_reset_at)
     E = O.block_eviction_scores(O.subblock_logit_means(lam[b, h]))
     return tr, E
 
@@ -97,7 +98,8 @@ def compare_unit(w: NI.Workload, K, V, lam, q, b, h, gpu_sel, gpu_out=None, gpu_
     pool_reset_at: step at which the oracle's pool starts again empty."""
     G = w.group
     positions = w.positions() if positions is None else positions
-    tr, E = oracle_scores(w, K, V, lam, q, b, h, positions)
+    pool_slots = w.pool_slots if gpu_pool else None
+    tr, E = oracle_scores(w, K, V, lam, q, b, h, positions, pool_slots, pool_reset_at)
     forced: Dict[int, List[int]] = {}
     ties = 0
     for t, S in enumerate(gpu_sel):
@@ -110,10 +112,13 @@ def compare_unit(w: NI.Workload, K, V, lam, q, b, h, gpu_sel, gpu_out=None, gpu_
         assert list(S) == sorted(S)
     if gpu_out is None and gpu_pool is None:
         return dict(ties=ties)
-    qrows = q[:, b, h * G:(h + 1) * G]
-    tr2 = O.decode_unit(K[b, h], V[b, h], lam[b, h], qrows, positions[: len(gpu_sel)], w.kq, w.ke,
-                        bf16=(w.dtype == "bf16"), pool_slots=w.pool_slots if gpu_pool else None,
-                        attend=gpu_out is not None, forced_sel=forced, pool_reset_at=pool_reset_at)
+    if not forced and gpu_out is None and len(gpu_sel) == q.shape[0]:
+        tr2 = tr          # the first run replayed the pool over the GPU's own sets
+    else:
+        qrows = q[:, b, h * G:(h + 1) * G]
+        tr2 = O.decode_unit(K[b, h], V[b, h], lam[b, h], qrows, positions[: len(gpu_sel)], w.kq, w.ke,
+                            bf16=(w.dtype == "bf16"), pool_slots=pool_slots,
+                            attend=gpu_out is not None, forced_sel=forced, pool_reset_at=pool_reset_at)
     err = 0.0
     if gpu_out is not None:
         for t in range(len(gpu_sel)):
@@ -183,12 +188,14 @@ def run_offload(w: NI.Workload, K, V, lam, q, steps: Optional[int] = None, side_
     return out, layer, host
 
 
-def check_offload_unit(w: NI.Workload, K, V, lam, q, rec, b, h, pool_reset_at=None):
-    """Oracle comparison of one unit of an offload run: selections, outputs, pool."""
+def check_offload_unit(w: NI.Workload, K, V, lam, q, rec, b, h, pool_reset_at=None, outputs: bool = True):
+    """Oracle comparison of one unit of an offload run: selections, pool
+    tables (miss list, insert entry, physical slots) and, unless outputs is
+    False, the attention outputs."""
     positions = rec["positions"][:, b] if "positions" in rec else w.positions()[: len(rec["sel"])]
     sels = unit_selections(rec["sel"], rec["n_sel"], b, h)
-    st = compare_unit(w, K, V, lam, q, b, h, sels, gpu_out=rec["out"], gpu_pool=True, positions=positions,
-                      pool_reset_at=pool_reset_at)
+    st = compare_unit(w, K, V, lam, q, b, h, sels, gpu_out=rec["out"] if outputs else None, gpu_pool=True,
+                      positions=positions, pool_reset_at=pool_reset_at)
     tr = st["trace"]
     for t in range(len(sels)):
         nm = int(rec["n_miss"][t][b, h])

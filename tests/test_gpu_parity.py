@@ -538,23 +538,38 @@ def test_offload_sweep_points(kq, ke, fused):
             _pool_consistent(layer, host, b, h)
 
 
+# units whose attention outputs the full-size offload test compares (every
+# unit's selections and pool tables are compared)
+OFFLOAD_OUT_UNITS = ((0, 0), (9, 1), (17, 1), (26, 0), (40, 0), (45, 1), (58, 0), (63, 1))
+
+
 @pytest.mark.parametrize("fused_fetch", [True, False], ids=["fused-fetch", "side-stream"])
-def test_offload_workload_sampled_units(fused_fetch):
-    _banner(f"offload workload: B=64, 16K context, pool 80, 128 steps (sampled units), fused fetch {fused_fetch}")
+def test_offload_workload_full_size(fused_fetch):
+    """The offload workload at full size (B=64, 16K context, pool of 80, 128
+    steps): the selections, miss lists, insert entries and physical slots of
+    all 128 units, the pool contents of every unit against the host cache,
+    and the outputs of eight units against the oracle."""
+    _banner(f"offload workload: B=64, 16K context, pool 80, 128 steps (every unit), fused fetch {fused_fetch}")
     w = NI.WORKLOADS["offload"]
     K, V, lam, q = NI.layer_inputs(w)
     rec, layer, host = H.run_offload(w, K, V, lam, q, record_tables=False, fused_fetch=fused_fetch)
-    for b, h in ((0, 0), (17, 1), (40, 0), (63, 1)):
-        H.check_offload_unit(w, K, V, lam, q, rec, b, h)
-        _pool_consistent(layer, host, b, h)
+    misses = 0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            st = H.check_offload_unit(w, K, V, lam, q, rec, b, h, outputs=(b, h) in OFFLOAD_OUT_UNITS)
+            misses += st["misses"]
+            _pool_consistent(layer, host, b, h)
+    assert misses == sum(int(n.sum()) for n in rec["n_miss"])
+    print(f"[offload] {misses} misses over {w.batch * w.n_kv_heads} units", flush=True)
 
 
-def test_stack128k_sampled_layers():
+def test_stack128k_full_size_layers():
     """Two layers of the 28-layer stack (the first and the last, with their
     own seeds) at full size: B=16, 131072-token context, pool of 80, 32 steps,
-    run by the stack driver the bench times; sampled units of both layers
-    against the oracle, pools against the host caches."""
-    _banner("stack128k: layers 0 and 27 at full size (B=16, 128K context, pool 80, 32 steps), sampled units")
+    run by the stack driver the bench times; every unit's selections and pool
+    tables and three units' outputs of both layers against the oracle, every
+    pool against the host caches."""
+    _banner("stack128k: layers 0 and 27 at full size (B=16, 128K context, pool 80, 32 steps), every unit")
     w = NI.WORKLOADS["stack128k"]
     layer_ids = (0, w.n_layers - 1)
     positions = w.positions()
@@ -584,11 +599,13 @@ def test_stack128k_sampled_layers():
         r = {k: [x.cpu().numpy() for x in v] for k, v in rec[i].items()}
         K, V, lam, q = inputs[i]
         misses = 0
-        for b, h in ((0, 0), (9, 1), (15, 1)):
-            st = H.check_offload_unit(w, K, V, lam, q, r, b, h)
-            misses += st["misses"]
-            _pool_consistent(stack.layers[i], stack.host[i], b, h)
-        assert misses >= 3 * (w.kq + w.ke), (lid, misses)     # at least the cold step's
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                st = H.check_offload_unit(w, K, V, lam, q, r, b, h, outputs=(b, h) in ((0, 0), (9, 1), (15, 1)))
+                misses += st["misses"]
+                _pool_consistent(stack.layers[i], stack.host[i], b, h)
+        assert misses >= w.batch * w.n_kv_heads * (w.kq + w.ke), (lid, misses)     # at least the cold step's
+        assert misses == sum(int(n.sum()) for n in r["n_miss"]), lid
 
 
 @pytest.mark.parametrize("fused_fetch", [False, True], ids=["side-stream", "fused-fetch"])
