@@ -488,11 +488,14 @@ __device__ void merge_slice_ll(MergeLds<D, WAVES, GMAX>& L, int G, int tid, int 
   lds_barrier();   // the weights and the flag
   const bool any_late = *late_flag != 0;
   if (has) {
+    // every term, with no guard on n_part: a record past n_part has weight 0
+    // (the weights above) and payload 0 (w was zeroed), so the 16 weight
+    // reads go out together instead of one per branch
+    static_assert(MAXP == 16, "the weights above cover 16 records per head");
     const int g = idx / D;
     float n = 0.f;
 #pragma unroll
-    for (int sp = 0; sp < MAXP; ++sp)
-      if (sp < n_part) n = fmaf(L.a[g][sp], ll_float(w[sp]), n);
+    for (int sp = 0; sp < MAXP; ++sp) n = fmaf(L.a[g][sp], ll_float(w[sp]), n);
     store_out(&out_g[idx], any_late ? __builtin_nanf("") : n);
   }
 }
