@@ -528,7 +528,21 @@ __device__ void merge_splits(AttnLds<D, WAVES, GMAX>& L, int G, int tid, int n_s
     }
   }
   __syncthreads();
-  if (tid < G) {
+  if (n_split <= 16) {
+    // one 16-lane group per head (lane = split): the maxima and sums by DPP,
+    // every split's LDS words read at once
+    if (tid < 16 * GMAX) {
+      const int g = tid >> 4, s = tid & 15;
+      const bool on = g < G && s < n_split;
+      const float ms = on ? fm[s * G + g] : -INFINITY;
+      const float ls = on ? fl[s * G + g] : 0.f;
+      const float M = group_max<16>(ms);
+      const float wt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      const float den = group_sum<16>(wt * ls);
+      if (on) fm[s * G + g] = wt;
+      if (g < G && s == 0) L.den[g] = den;
+    }
+  } else if (tid < G) {
     float M = -INFINITY;
     for (int s = 0; s < n_split; ++s) M = fmaxf(M, fm[s * G + tid]);
     float den = 0.f;
@@ -548,9 +562,14 @@ __device__ void merge_splits(AttnLds<D, WAVES, GMAX>& L, int G, int tid, int n_s
     const int g = idx / D, d = idx % D;
     float num = 0.f;
     if (in_regs) {
+      // every term, unguarded (reads in bounds; a term past n_split adds 0),
+      // so the weight reads go out together instead of one per branch
+      const int s_last = n_split > 0 ? n_split - 1 : 0;
 #pragma unroll
-      for (int s = 0; s < kMaxSplitRegs; ++s)
-        if (s < n_split) num += fm[s * G + g] * v[r][s];
+      for (int s = 0; s < kMaxSplitRegs; ++s) {
+        const float wt = fm[min(s, s_last) * G + g];
+        num += (s < n_split ? wt : 0.f) * v[r][s];
+      }
     } else {
       for (int s = 0; s < n_split; ++s)
         num += fm[s * G + g] * load_coherent(&po[((size_t)s * G + g) * D + d]);
