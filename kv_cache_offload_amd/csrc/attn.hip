@@ -401,25 +401,30 @@ __global__ void __launch_bounds__(64 * kChunkWaves) chunk_attn_kernel(
     fl[i] = load_coherent(&pml[2 * i + 1]);
   }
   __syncthreads();
-  if (tid < 16) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, fw[sp * 16 + tid]);
-    float den = 0.f;
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float ms = fw[sp * 16 + tid];
-      const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      fw[sp * 16 + tid] = wt;
-      den += wt * fl[sp * 16 + tid];
-    }
-    L.den[tid] = den;
+  if (tid < 16 * kRegSplits) {
+    // one 8-lane group per column (lane = split): the maxima and sums by DPP,
+    // every split's LDS words read at once
+    static_assert(kRegSplits == 8, "one 8-lane group per column");
+    const int col = tid >> 3, sp = tid & 7;
+    const bool on = sp < n_split;
+    const float ms = on ? fw[sp * 16 + col] : -INFINITY;
+    const float ls = on ? fl[sp * 16 + col] : 0.f;
+    const float M = group_max<8>(ms);
+    const float wt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    const float den = group_sum<8>(wt * ls);
+    if (on) fw[sp * 16 + col] = wt;
+    if (sp == 0) L.den[col] = den;
   }
   __syncthreads();
+  const int sp_last = n_split > 0 ? n_split - 1 : 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int idx = tid + k * NT, col = idx / D, d = idx % D, rw = r0 + col / G;
     float num = 0.f;
+    // every term, unguarded (reads in bounds; a term past n_split adds 0)
 #pragma unroll
-    for (int sp = 0; sp < kRegSplits; ++sp) num += (sp < n_split ? fw[sp * 16 + col] : 0.f) * v[k][sp];
+    for (int sp = 0; sp < kRegSplits; ++sp)
+      num += (sp < n_split ? fw[min(sp, sp_last) * 16 + col] : 0.f) * v[k][sp];
     if (rw >= n_query) continue;
     const float den = L.den[col];
     store_out(&out[(((size_t)b * n_query + rw) * n_q_heads + (size_t)h * G + col % G) * D + d],
