@@ -208,7 +208,9 @@ template <int D, int NT>
 struct MfmaScan {
   static constexpr int NK = D / 32;      // k-steps of 32 dims
   static constexpr int WAVES = NT / 64;
-  static constexpr int TPR = 2;          // tiles per wavefront per round
+  // tiles per wavefront per round: two with 8 wavefronts; one with 16, whose
+  // 128-VGPR budget two double-buffered tiles overrun (spills)
+  static constexpr int TPR = NT >= 1024 ? 1 : 2;
   const uint16_t* kc;
   int row_lo, row_hi, n_tiles, n_rounds, wave, col, grp;
   uint4 ra[TPR][NK];
