@@ -52,7 +52,7 @@ KEPT_FACTOR = 1.0           # ... and the selection's bytes (compressed keys, sc
 # Byte counters of step_kernel on this workload (rocprofv3 --pmc, KiB per dispatch),
 # valid for the kernel sources whose digest is recorded here.  FETCH_SIZE reads half
 # of a plain 256 MiB copy's bytes (factor 2.0); WRITE_SIZE reads all of them (1.0).
-STEP_PMC = {"src_sha256": "09a592ec77d7a66c8c8376ff682ab96c4681ba1c786debebca5f1b1b740f1356", "fetch_kib": 21805.6, "write_kib": 2225.0}
+STEP_PMC = {"src_sha256": "af700ed005f01f21a29223ad4f1e4c96b7123b82902ea2884a0b3f69cf63785e", "fetch_kib": 21804.4, "write_kib": 2225.0}
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 STEP_SOURCES = ("fused.hip", "attn_dev.h", "select_dev.h", "nosa_common.h")
 
